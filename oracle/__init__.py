@@ -1,0 +1,108 @@
+"""CPU oracle for the DSA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Plain fp64 C loops (dsa_oracle.c) behind ctypes.  Only the tests, the smoke
+check and the benchmark's CPU-baseline leg may import this package; the product
+library never does, and this package imports nothing from it.  See
+dsa_oracle.c for what each function computes and which page passage it
+follows.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, special cases reducing to library routines, brute force on tiny
+inputs, and the pages' printed counts).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build_oracle, ORACLE_LIB
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(ORACLE_LIB):
+            build_oracle()
+        lib = ctypes.CDLL(ORACLE_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_indexer_scores.argtypes = [i32, P, P, P, P, P, f64, P, i64]
+        lib.oracle_round_to_f32.argtypes = [i64, P, P]
+        lib.oracle_topk.argtypes = [i32, P, P, i64, i32, P]
+        lib.oracle_sparse_mla.argtypes = [i32, P, P, P, P, i32, f64, P, P]
+        lib.oracle_version.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n):
+    """Bound the OpenMP thread count of later calls (OMP_NUM_THREADS semantics)."""
+    os.environ["OMP_NUM_THREADS"] = str(int(n))
+
+
+def indexer_scores(visible_len, row_cache_base, q_idx, w, k_idx, index_scale=1.0, ld=None):
+    """fp64 scores [R, ld]; entries t >= visible_len[r] are NaN."""
+    vis = _c(visible_len, np.int32)
+    base = _c(row_cache_base, np.int64)
+    R = vis.shape[0]
+    ld = int(vis.max()) if ld is None else int(ld)
+    q = _c(q_idx, np.uint16).reshape(R, 32, 128)
+    ww = _c(w, np.float32).reshape(R, 32)
+    kc = _c(k_idx, np.uint16)
+    out = np.full((R, ld), np.nan, np.float64)
+    _lib().oracle_indexer_scores(R, _p(vis), _p(base), _p(q), _p(ww), _p(kc), float(index_scale), _p(out), ld)
+    return out
+
+
+def round_to_f32(x):
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.float32)
+    _lib().oracle_round_to_f32(x.size, _p(x), _p(out))
+    return out
+
+
+def topk(visible_len, scores_f32, k):
+    """int32 [R, k]: the k_r best positions ascending, then -1."""
+    vis = _c(visible_len, np.int32)
+    s = _c(scores_f32, np.float32)
+    R, ld = s.shape
+    out = np.empty((R, k), np.int32)
+    _lib().oracle_topk(R, _p(vis), _p(s), ld, int(k), _p(out))
+    return out
+
+
+def sparse_mla(row_cache_base, q_abs, kv_latent, indices, softmax_scale):
+    """(out [R,64,512] fp64, lse [R,64] fp64) over entries indices >= 0."""
+    base = _c(row_cache_base, np.int64)
+    R = base.shape[0]
+    qa = _c(q_abs, np.uint16).reshape(R, 64, 576)
+    kv = _c(kv_latent, np.uint16)
+    idx = _c(indices, np.int32)
+    k = idx.shape[1]
+    out = np.empty((R, 64, 512), np.float64)
+    lse = np.empty((R, 64), np.float64)
+    _lib().oracle_sparse_mla(R, _p(base), _p(qa), _p(kv), _p(idx), k, float(softmax_scale), _p(out), _p(lse))
+    return out, lse
+
+
+def decode_step(visible_len, row_cache_base, q_idx, w, k_idx, q_abs, kv_latent, k, index_scale, softmax_scale):
+    """The whole path: fp64 scores, rounded to fp32 for the top-k, then attention."""
+    s64 = indexer_scores(visible_len, row_cache_base, q_idx, w, k_idx, index_scale)
+    s32 = round_to_f32(np.nan_to_num(s64, nan=0.0))
+    idx = topk(visible_len, s32, k)
+    out, lse = sparse_mla(row_cache_base, q_abs, kv_latent, idx, softmax_scale)
+    return s64, s32, idx, out, lse
+
+
+def version():
+    return _lib().oracle_version().decode()

@@ -1,0 +1,208 @@
+/*
+ * dsa_oracle.c -- plain, slow, obviously-correct fp64 CPU oracle for the DSA
+ * hot path (lightning indexer -> causal top-k -> absorbed sparse MLA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or constant with the HIP
+ * path: geometry constants below are restated from the pages on purpose.
+ *
+ * Sources (pages, by title and section):
+ *  [P1] "GLM-5.1 架构深度拆解" (cctoctofx.netlify.app, GLM-5.1 architecture
+ *       teardown): CH3 §3.2 "Indexer 公式" steps 4-7, CH3 §3.6
+ *       "GlmMoeDsaIndexer.forward" steps 4, 5 and 7, CH4 §4.1 and §4.5
+ *       "GlmMoeDsaAttention.forward" steps 2, 6 and 7.
+ *  [P2] GLM-5 explainer (ailearn.mscapital.top): the indexer paragraph
+ *       ("32 x 128 index queries, one 128-d key per position, ReLU, 32
+ *       weights, causal Top-2,048"), the "shorter than 2,048 keeps all"
+ *       paragraph and the 202,752-token window table.
+ *  [P5] "GLM-5.2 架构 QA" (pillumina.github.io), Q1.1 config listing
+ *       (qk_nope_head_dim 192 + qk_rope_head_dim 64 = qk_head_dim 256).
+ *
+ * Every floating-point input arrives as the exact bytes the GPU path reads
+ * (bf16 bit patterns as uint16, fp32 weights); each is widened exactly to
+ * fp64 and all arithmetic below is fp64 in the plain loop order written.
+ * Parallelism is only over independent query rows (OpenMP); the arithmetic
+ * inside a row is a single ordered loop nest.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Geometry, restated from [P1] CH3 §3.6 step 1-2 (32 index heads x 128 dims,
+ * one 128-d key per position) and CH4 §4.1 (kv_lora_rank 512 + rope 64). */
+#define OR_IDX_HEADS 32
+#define OR_IDX_DIM 128
+#define OR_HEADS 64
+#define OR_LATENT 512
+#define OR_ROW 576
+
+static double bf16_to_f64(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+const char* oracle_version(void) { return "dsa-oracle fp64 1"; }
+
+/*
+ * Lightning-indexer scores ([P1] §3.6 step 5, §3.2 steps 4-5; [P2] indexer
+ * paragraph):
+ *     d_h    = scale * sum_d q[r,h,d] * K[base_r + t, d]
+ *     s[r,t] = sum_h w[r,h] * max(0, d_h)          for 0 <= t < n_r
+ * The causal mask of [P1] §3.2 step 6 is the loop bound t < n_r: a query sees
+ * its own position and every earlier one.  w is taken as given (already
+ * multiplied by 32^-1/2 upstream, [P1] §3.6 step 4).
+ *
+ * q: [R,32,128] bf16 bits; w: [R,32] fp32; k: packed key cache [*,128] bf16
+ * bits; out: [R, ld] fp64, only columns [0, n_r) are written.
+ */
+void oracle_indexer_scores(int32_t R, const int32_t* n, const int64_t* base, const uint16_t* q,
+                           const float* w, const uint16_t* k, double scale, double* out, int64_t ld)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t r = 0; r < R; r++) {
+        double qd[OR_IDX_HEADS][OR_IDX_DIM];
+        double wd[OR_IDX_HEADS];
+        for (int h = 0; h < OR_IDX_HEADS; h++) {
+            wd[h] = (double)w[(int64_t)r * OR_IDX_HEADS + h];
+            for (int d = 0; d < OR_IDX_DIM; d++)
+                qd[h][d] = bf16_to_f64(q[((int64_t)r * OR_IDX_HEADS + h) * OR_IDX_DIM + d]);
+        }
+        for (int32_t t = 0; t < n[r]; t++) {
+            const uint16_t* krow = k + (base[r] + t) * OR_IDX_DIM;
+            double kd[OR_IDX_DIM];
+            for (int d = 0; d < OR_IDX_DIM; d++) kd[d] = bf16_to_f64(krow[d]);
+            double s = 0.0;
+            for (int h = 0; h < OR_IDX_HEADS; h++) {
+                double dot = 0.0;
+                for (int d = 0; d < OR_IDX_DIM; d++) dot += qd[h][d] * kd[d];
+                double dh = scale * dot;
+                if (dh > 0.0) s += wd[h] * dh;
+            }
+            out[(int64_t)r * ld + t] = s;
+        }
+    }
+}
+
+/* Round fp64 scores to fp32 with round-to-nearest-even (the C conversion
+ * under the default rounding mode), to feed the top-k exactly like the GPU
+ * path's fp32 scores. */
+void oracle_round_to_f32(int64_t count, const double* in, float* out)
+{
+    for (int64_t i = 0; i < count; i++) out[i] = (float)in[i];
+}
+
+/*
+ * Top-k ordering key ([P1] §3.6 step 7 "topk = min(index_topk, total_len)",
+ * §3.4 determinism requirement; [P2] "shorter than 2,048 keeps all"):
+ * larger score first; IEEE comparison so -0.0 equals +0.0; equal scores are
+ * broken toward the lower position; NaN orders below every number.
+ */
+typedef struct {
+    float s;
+    int32_t t;
+} oracle_entry;
+
+static int cmp_entry(const void* pa, const void* pb)
+{
+    const oracle_entry* a = (const oracle_entry*)pa;
+    const oracle_entry* b = (const oracle_entry*)pb;
+    int an = isnan(a->s), bn = isnan(b->s);
+    if (an != bn) return an ? 1 : -1;
+    if (!an) {
+        if (a->s > b->s) return -1;
+        if (a->s < b->s) return 1;
+    }
+    return (a->t < b->t) ? -1 : (a->t > b->t ? 1 : 0);
+}
+
+static int cmp_i32(const void* pa, const void* pb)
+{
+    int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    return (a < b) ? -1 : (a > b);
+}
+
+/*
+ * For each row: sort positions [0, n_r) by the key above, keep the first
+ * k_r = min(k, n_r), return them in ascending position order, pad with -1.
+ * scores: [R, ld] fp32; idx: [R, k] int32.
+ */
+void oracle_topk(int32_t R, const int32_t* n, const float* scores, int64_t ld, int32_t k, int32_t* idx)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t r = 0; r < R; r++) {
+        int32_t nr = n[r];
+        oracle_entry* e = (oracle_entry*)malloc(sizeof(oracle_entry) * (size_t)(nr > 0 ? nr : 1));
+        for (int32_t t = 0; t < nr; t++) {
+            e[t].s = scores[(int64_t)r * ld + t];
+            e[t].t = t;
+        }
+        qsort(e, (size_t)nr, sizeof(oracle_entry), cmp_entry);
+        int32_t kr = nr < k ? nr : k;
+        int32_t* out = idx + (int64_t)r * k;
+        for (int32_t j = 0; j < kr; j++) out[j] = e[j].t;
+        qsort(out, (size_t)kr, sizeof(int32_t), cmp_i32);
+        for (int32_t j = kr; j < k; j++) out[j] = -1;
+        free(e);
+    }
+}
+
+/*
+ * Absorbed-MLA attention over a given index list ([P1] §4.5 steps 2, 6, 7;
+ * [P2] "the Top-2,048 IDs only drive the gather"; [P5] Q1.1 qk_head_dim 256):
+ *     z_j    = softmax_scale * sum_{d<576} qa[r,h,d] * L[base_r + idx_j, d]
+ *     p_j    = exp(z_j - m) / sum_j exp(z_j - m),   m = max_j z_j
+ *     o[h,c] = sum_j p_j * L[base_r + idx_j, c]      for c < 512
+ *     lse[h] = m + log sum_j exp(z_j - m)
+ * over the entries idx_j >= 0 of the row (entries < 0 are padding).  The
+ * absorbed query qa = [W_UK^T q_nope (512) || q_pe (64)] and the 576-wide
+ * latent row [c_kv (512) || k_pe (64)] make the 64-head dot products equal to
+ * the expanded 192+64 ones, because kv_b_proj is linear; values are the
+ * 512-wide c_kv part, before the per-head V up-projection.
+ *
+ * qa: [R,64,576] bf16 bits; kv: packed latent cache [*,576] bf16 bits;
+ * idx: [R, k] int32; out: [R,64,512] fp64; lse: [R,64] fp64 (may be NULL).
+ */
+void oracle_sparse_mla(int32_t R, const int64_t* base, const uint16_t* qa, const uint16_t* kv,
+                       const int32_t* idx, int32_t k, double softmax_scale, double* out, double* lse)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t r = 0; r < R; r++) {
+        const int32_t* ir = idx + (int64_t)r * k;
+        int32_t m_valid = 0;
+        for (int32_t j = 0; j < k; j++)
+            if (ir[j] >= 0) m_valid++;
+        double* z = (double*)malloc(sizeof(double) * (size_t)(m_valid > 0 ? m_valid : 1));
+        const uint16_t** rows = (const uint16_t**)malloc(sizeof(void*) * (size_t)(m_valid > 0 ? m_valid : 1));
+        int32_t jj = 0;
+        for (int32_t j = 0; j < k; j++)
+            if (ir[j] >= 0) rows[jj++] = kv + (base[r] + ir[j]) * OR_ROW;
+        for (int h = 0; h < OR_HEADS; h++) {
+            const uint16_t* qh = qa + ((int64_t)r * OR_HEADS + h) * OR_ROW;
+            double qd[OR_ROW];
+            for (int d = 0; d < OR_ROW; d++) qd[d] = bf16_to_f64(qh[d]);
+            double m = -INFINITY;
+            for (int32_t j = 0; j < m_valid; j++) {
+                double dot = 0.0;
+                for (int d = 0; d < OR_ROW; d++) dot += qd[d] * bf16_to_f64(rows[j][d]);
+                z[j] = softmax_scale * dot;
+                if (z[j] > m) m = z[j];
+            }
+            double denom = 0.0;
+            for (int32_t j = 0; j < m_valid; j++) denom += exp(z[j] - m);
+            double* o = out + ((int64_t)r * OR_HEADS + h) * OR_LATENT;
+            for (int c = 0; c < OR_LATENT; c++) o[c] = 0.0;
+            for (int32_t j = 0; j < m_valid; j++) {
+                double p = exp(z[j] - m) / denom;
+                for (int c = 0; c < OR_LATENT; c++) o[c] += p * bf16_to_f64(rows[j][c]);
+            }
+            if (lse) lse[(int64_t)r * OR_HEADS + h] = m + log(denom);
+        }
+        free(rows);
+        free(z);
+    }
+}

@@ -1,0 +1,213 @@
+"""Python binding of libdsa (the DSA hot path on MI355X / gfx950).
+
+Argument marshalling only: every function below checks tensor placement and
+dtype, turns tensors into device pointers and calls the C ABI entry point of
+the same name declared in include/dsa.h.  All arithmetic runs in the HIP
+kernels of libdsa.so.  There is no fallback: if the library is missing or the
+device is not a gfx950, calls raise.
+
+PyTorch supplies device memory and streams only.  bf16 inputs are
+torch.bfloat16 tensors (or int16/uint16 views of the same bits).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DsaError", "Rows", "library_path", "load_library", "dsa_version", "exported_symbols",
+    "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk_select",
+    "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn",
+    "dsa_decode_step_workspace_size", "dsa_decode_step", "workspace",
+    "INDEX_HEADS", "INDEX_DIM", "HEADS", "LATENT_DIM", "ROPE_DIM", "ROW_DIM", "TOPK_MAX",
+]
+
+INDEX_HEADS = 32
+INDEX_DIM = 128
+HEADS = 64
+LATENT_DIM = 512
+ROPE_DIM = 64
+ROW_DIM = 576
+TOPK_MAX = 2048
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS_NAMES = {
+    0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_MISALIGNED",
+    3: "DSA_ERR_WORKSPACE_TOO_SMALL", 4: "DSA_ERR_NO_DEVICE", 5: "DSA_ERR_HIP",
+}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class _CRows(ctypes.Structure):
+    _fields_ = [
+        ("num_rows", ctypes.c_int32),
+        ("max_visible", ctypes.c_int32),
+        ("visible_len", ctypes.c_void_p),
+        ("row_cache_base", ctypes.c_void_p),
+    ]
+
+
+def library_path():
+    return os.path.join(_PKG_DIR, "libdsa.so")
+
+
+def load_library():
+    """Load libdsa.so (built by __graft_entry__.build()); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    rows_p = ctypes.POINTER(_CRows)
+    sigs = {
+        "dsa_version": ([], ctypes.c_char_p),
+        "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "dsa_last_error_detail": ([], ctypes.c_char_p),
+        "dsa_indexer_scores": ([rows_p, P, P, P, f32, P, i64, P], ctypes.c_int),
+        "dsa_topk_workspace_size": ([i32, i32, i32], sz),
+        "dsa_topk_select": ([rows_p, P, i64, i32, P, P, sz, P], ctypes.c_int),
+        "dsa_sparse_mla_workspace_size": ([i32, i32], sz),
+        "dsa_sparse_mla_attn": ([rows_p, P, P, P, i32, f32, P, P, P, sz, P], ctypes.c_int),
+        "dsa_decode_step_workspace_size": ([i32, i32, i32], sz),
+        "dsa_decode_step": ([rows_p, P, P, P, f32, P, P, f32, i32, P, P, P, P, sz, P], ctypes.c_int),
+    }
+    for name, (argtypes, restype) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    _LIB = lib
+    return lib
+
+
+def exported_symbols():
+    """Names of the C ABI entry points the binding expects."""
+    return [
+        "dsa_version", "dsa_status_string", "dsa_last_error_detail", "dsa_indexer_scores",
+        "dsa_topk_workspace_size", "dsa_topk_select", "dsa_sparse_mla_workspace_size",
+        "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step",
+    ]
+
+
+def dsa_version():
+    return load_library().dsa_version().decode()
+
+
+def _check(status):
+    if status != 0:
+        lib = load_library()
+        raise DsaError(status, lib.dsa_last_error_detail().decode())
+
+
+def _ptr(t, name, dtypes=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream, ref):
+    if stream is None:
+        return torch.cuda.current_stream(ref.device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Rows:
+    """Query-row description (dsa_rows_t): device visible_len [R] int32,
+    device row_cache_base [R] int64 and the host bound max_visible."""
+
+    def __init__(self, visible_len, row_cache_base, max_visible):
+        if visible_len.dtype != torch.int32 or row_cache_base.dtype != torch.int64:
+            raise TypeError("visible_len must be int32 and row_cache_base int64")
+        if visible_len.numel() != row_cache_base.numel():
+            raise ValueError("visible_len and row_cache_base differ in length")
+        self.visible_len = visible_len
+        self.row_cache_base = row_cache_base
+        self.num_rows = int(visible_len.numel())
+        self.max_visible = int(max_visible)
+        self._c = _CRows(self.num_rows, self.max_visible, _ptr(visible_len, "visible_len", (torch.int32,)),
+                         _ptr(row_cache_base, "row_cache_base", (torch.int64,)))
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def workspace(nbytes, device):
+    """A device byte buffer of at least nbytes (torch allocations are 256-B aligned)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def dsa_indexer_scores(rows, q_idx, w, k_idx, index_scale, scores, ld=None, stream=None):
+    lib = load_library()
+    ld = scores.shape[-1] if ld is None else ld
+    _check(lib.dsa_indexer_scores(rows.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
+                                  _ptr(k_idx, "k_idx", _BF16), float(index_scale),
+                                  _ptr(scores, "scores", (torch.float32,)), int(ld), _stream(stream, scores)))
+
+
+def dsa_topk_workspace_size(num_rows, max_visible, k):
+    return int(load_library().dsa_topk_workspace_size(int(num_rows), int(max_visible), int(k)))
+
+
+def dsa_topk_select(rows, scores, k, indices, ws, ld=None, stream=None):
+    lib = load_library()
+    ld = scores.shape[-1] if ld is None else ld
+    _check(lib.dsa_topk_select(rows.c, _ptr(scores, "scores", (torch.float32,)), int(ld), int(k),
+                               _ptr(indices, "indices", (torch.int32,)), _ptr(ws, "ws"),
+                               ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream, scores)))
+
+
+def dsa_sparse_mla_workspace_size(num_rows, k):
+    return int(load_library().dsa_sparse_mla_workspace_size(int(num_rows), int(k)))
+
+
+def dsa_sparse_mla_attn(rows, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse=None, ws=None,
+                        stream=None):
+    lib = load_library()
+    _check(lib.dsa_sparse_mla_attn(rows.c, _ptr(q_abs, "q_abs", _BF16), _ptr(kv_latent, "kv_latent", _BF16),
+                                   _ptr(indices, "indices", (torch.int32,)), int(k), float(softmax_scale),
+                                   _ptr(out_latent, "out_latent", (torch.float32,)),
+                                   _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(stream, out_latent)))
+
+
+def dsa_decode_step_workspace_size(num_rows, max_visible, k):
+    return int(load_library().dsa_decode_step_workspace_size(int(num_rows), int(max_visible), int(k)))
+
+
+def dsa_decode_step(rows, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices, out_latent,
+                    out_lse=None, ws=None, stream=None):
+    lib = load_library()
+    _check(lib.dsa_decode_step(rows.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
+                               _ptr(k_idx, "k_idx", _BF16), float(index_scale), _ptr(q_abs, "q_abs", _BF16),
+                               _ptr(kv_latent, "kv_latent", _BF16), float(softmax_scale), int(k),
+                               _ptr(indices, "indices", (torch.int32,)),
+                               _ptr(out_latent, "out_latent", (torch.float32,)),
+                               _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
+                               ws.numel() * ws.element_size() if ws is not None else 0,
+                               _stream(stream, out_latent)))

@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle to facts other than itself (no GPU needed).
+
+Each test ties an oracle function to a closed form, a special case that
+reduces to a library routine, brute force on tiny inputs, an invariant, or a
+number the pages print (tests/golden/page_counts.json).  A plausible slip in
+the oracle (a dropped term, a wrong sign or index, a transposed operand, an
+off-by-one in the causal bound, a wrong tie rule or scale) fails one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_counts.json")
+
+
+def golden(key):
+    with open(GOLDEN) as f:
+        return json.load(f)[key]["value"]
+
+
+def bf16(shape, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    return wl.f32_to_bf16_bits(g.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def f(bits):
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- inputs
+
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(100000).astype(np.float32) * 7,
+                        np.array([0.0, -0.0, 1.0, 3.0039062, -2.0078125, 65504.0], np.float32)])
+    ours = wl.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_generator_is_deterministic_and_stream_separated():
+    a = wl.config("c1").generate()
+    b = wl.config("c1").generate()
+    for key in ("q_idx", "w", "k_idx", "q_abs", "kv_latent"):
+        assert np.array_equal(a[key], b[key]), key
+    # streams differ between tensors and rows
+    assert not np.array_equal(a["q_idx"].reshape(-1)[:64], a["q_abs"].reshape(-1)[:64])
+    w = wl.decode(2, 16, seed=5).generate()["w"]
+    assert not np.array_equal(w[0], w[1])
+    # w = fp32(bf16(N)) * fp32(32^-1/2)
+    draw = wl.bf16_bits_to_f32(wl.normal_bf16(5, wl.T_W, 1, (32,)))
+    assert np.array_equal(w[1], (draw * wl.W_SCALE).astype(np.float32))
+
+
+def test_tie_variant_gives_at_most_eight_scores_per_row(oracle_mod):
+    w = wl.prefill(300, seed=1, tie_keys=True)
+    x = w.generate()
+    s = oracle_mod.indexer_scores(x["visible_len"], x["row_cache_base"], x["q_idx"], x["w"], x["k_idx"])
+    for r in (50, 150, 299):
+        assert len(np.unique(s[r, : r + 1])) <= 8
+
+
+# --------------------------------------------------------------------------- indexer
+
+def _idx_inputs(R=3, T=40, seed=1):
+    q = bf16((R, 32, 128), seed)
+    w = (wl.bf16_bits_to_f32(bf16((R, 32), seed + 1)) * wl.W_SCALE).astype(np.float32)
+    k = bf16((T, 128), seed + 2)
+    vis = np.array([T, T // 2, 1][:R], np.int32)
+    base = np.zeros(R, np.int64)
+    return vis, base, q, w, k
+
+
+def test_indexer_one_hot_weight_is_relu_of_numpy_dot(oracle_mod):
+    vis, base, q, _, k = _idx_inputs()
+    for h in (0, 7, 31):
+        w = np.zeros((3, 32), np.float32)
+        w[:, h] = 1.0
+        s = oracle_mod.indexer_scores(vis, base, q, w, k, index_scale=1.0)
+        for r in range(3):
+            ref = np.maximum(f(k[: vis[r]]) @ f(q[r, h]), 0.0)
+            np.testing.assert_allclose(s[r, : vis[r]], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_indexer_sign_flip_identity(oracle_mod):
+    # ReLU(x) - ReLU(-x) = x  and  ReLU(x) + ReLU(-x) = |x|, so
+    # s(q) - s(-q) = sum_h w_h (q_h . k) = (w^T Q) k  (a plain matrix product)
+    vis, base, q, w, k = _idx_inputs(seed=11)
+    neg = q ^ np.uint16(0x8000)
+    sp = oracle_mod.indexer_scores(vis, base, q, w, k, index_scale=0.75)
+    sn = oracle_mod.indexer_scores(vis, base, neg, w, k, index_scale=0.75)
+    for r in range(3):
+        n = vis[r]
+        d = f(k[:n]) @ f(q[r]).T * 0.75                 # [n, 32]
+        np.testing.assert_allclose(sp[r, :n] - sn[r, :n], d @ w[r].astype(np.float64), rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(sp[r, :n] + sn[r, :n], np.abs(d) @ w[r].astype(np.float64), rtol=1e-11, atol=1e-11)
+
+
+def test_indexer_linear_in_weights_and_homogeneous_in_scale(oracle_mod):
+    vis, base, q, _, k = _idx_inputs(seed=21)
+    # bf16-valued weights: the fp32 sum of two of them is exact.
+    w = wl.bf16_bits_to_f32(bf16((3, 32), 22))
+    w2 = wl.bf16_bits_to_f32(bf16((3, 32), 23))
+    s1 = oracle_mod.indexer_scores(vis, base, q, w, k)
+    s2 = oracle_mod.indexer_scores(vis, base, q, w2, k)
+    s12 = oracle_mod.indexer_scores(vis, base, q, (w.astype(np.float64) + w2).astype(np.float32), k)
+    exact = (w.astype(np.float64) + w2) == (w.astype(np.float64) + w2).astype(np.float32)
+    assert exact.all()
+    m = ~np.isnan(s1)
+    np.testing.assert_allclose(s12[m], s1[m] + s2[m], rtol=1e-12, atol=1e-12)
+    s3 = oracle_mod.indexer_scores(vis, base, q, w, k, index_scale=4.0)
+    np.testing.assert_allclose(s3[m], 4.0 * s1[m], rtol=1e-13, atol=0)
+
+
+def test_indexer_all_negative_dots_give_exact_zero(oracle_mod):
+    k = bf16((1, 128), 3)
+    q = np.repeat((k[0] ^ np.uint16(0x8000))[None, None, :], 32, axis=1)  # q_h = -k
+    w = np.ones((1, 32), np.float32)
+    s = oracle_mod.indexer_scores(np.array([1], np.int32), np.zeros(1, np.int64), q, w, k)
+    assert s[0, 0] == 0.0
+
+
+def test_indexer_reads_only_visible_rows_of_its_sequence(oracle_mod):
+    vis, base, q, w, k = _idx_inputs(seed=31)
+    s = oracle_mod.indexer_scores(vis, base, q, w, k)
+    # Move the cache behind 7 poisoned rows (NaN bit patterns) and append NaN rows.
+    pad = np.full((7, 128), 0x7FC0, np.uint16)
+    k2 = np.concatenate([pad, k, pad])
+    s2 = oracle_mod.indexer_scores(vis, base + 7, q, w, k2)
+    for r in range(3):
+        assert np.array_equal(s[r, : vis[r]], s2[r, : vis[r]])
+        assert np.all(np.isnan(s2[r, vis[r]:]))  # columns past n_r untouched
+
+
+# --------------------------------------------------------------------------- top-k
+
+def brute_topk(scores, n, k):
+    """Reference selection by numpy's lexsort: (-score, position), NaN last."""
+    s = scores[:n].astype(np.float64)
+    key = np.where(np.isnan(s), np.inf, -s)
+    key = np.where(key == 0.0, 0.0, key)  # -0.0 and +0.0 compare equal
+    order = np.lexsort((np.arange(n), key))
+    kr = min(k, n)
+    sel = np.sort(order[:kr])
+    return np.concatenate([sel, -np.ones(k - kr, np.int64)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "signed_zeros", "coarse"])
+def test_topk_matches_lexsort_brute_force(oracle_mod, kind):
+    s = wl.random_scores(7, 12, 64, kind=kind)
+    s[3, 5] = -np.inf
+    s[4, :10] = np.inf
+    s[5, 2] = np.nan
+    s[5, 9] = np.nan
+    for n in (1, 2, 3, 17, 63, 64):
+        for k in (1, 3, n - 1, n, n + 5):
+            if k < 1:
+                continue
+            vis = np.full(12, n, np.int32)
+            got = oracle_mod.topk(vis, s, k)
+            for r in range(12):
+                assert np.array_equal(got[r], brute_topk(s[r], n, k)), (kind, n, k, r)
+
+
+def test_topk_invariants_on_ties(oracle_mod):
+    s = wl.random_scores(8, 6, 5000, kind="ties")
+    vis = np.array([5000, 4097, 2049, 2048, 100, 1], np.int32)
+    idx = oracle_mod.topk(vis, s, 2048)
+    for r in range(6):
+        n = vis[r]
+        kr = min(2048, n)
+        sel = idx[r][idx[r] >= 0]
+        assert len(sel) == kr and np.all(np.diff(sel) > 0) and np.all(idx[r][kr:] == -1)
+        mask = np.zeros(n, bool)
+        mask[sel] = True
+        row = s[r, :n]
+        if kr < n:
+            assert row[mask].min() >= row[~mask].max()
+            theta = row[mask].min()
+            tie_in = np.nonzero(mask & (row == theta))[0]
+            tie_out = np.nonzero(~mask & (row == theta))[0]
+            if len(tie_out):
+                assert tie_in.max() < tie_out.min()  # the lower positions win a tie
+
+
+def test_topk_counts_match_printed_pair_counts(oracle_mod):
+    # k_r = min(2048, n_r) with n_r = position + 1 (self included).
+    for n in (1, 2, 2047, 2048, 2049, 4096, 202752):
+        s = wl.random_scores(9, 1, n)
+        idx = oracle_mod.topk(np.array([n], np.int32), s, 2048)
+        assert int((idx >= 0).sum()) == min(2048, n)
+    L, K = golden("max_position_embeddings"), golden("index_topk")
+    t = np.arange(1, L + 1, dtype=np.int64)
+    assert int(np.minimum(t, K).sum()) == golden("dsa_causal_pairs")
+    assert L * (L + 1) // 2 == golden("dense_causal_pairs")
+    assert round(100 * K / L, 4) == golden("decode_fraction_percent")
+    assert round(100 * golden("dsa_causal_pairs") / golden("dense_causal_pairs"), 2) == golden("dsa_over_dense_percent")
+    assert round(golden("dense_causal_pairs") / golden("dsa_causal_pairs"), 2) == golden("dense_over_dsa_ratio")
+
+
+def test_topk_full_causal_prefill_count(oracle_mod):
+    T = 4096
+    s = wl.random_scores(10, T, T)
+    vis = np.arange(1, T + 1, dtype=np.int32)
+    idx = oracle_mod.topk(vis, s, 2048)
+    assert int((idx >= 0).sum()) == int(np.minimum(np.arange(1, T + 1), 2048).sum()) == 6292480
+
+
+# --------------------------------------------------------------------------- attention
+
+def _attn_inputs(R=2, T=50, seed=3):
+    qa = bf16((R, 64, 576), seed)
+    kv = bf16((T, 576), seed + 1)
+    return qa, kv
+
+
+def test_attention_identical_rows_return_that_row(oracle_mod):
+    qa, kv = _attn_inputs()
+    kv[:] = kv[7]
+    idx = np.array([[0, 3, 9, 11, -1, -1], [1, 2, 4, 5, 6, 8]], np.int32)
+    out, lse = oracle_mod.sparse_mla(np.zeros(2, np.int64), qa, kv, idx, 1 / 16)
+    for r in range(2):
+        np.testing.assert_allclose(out[r], np.broadcast_to(f(kv[7, :512]), (64, 512)), rtol=0, atol=1e-12)
+        m = int((idx[r] >= 0).sum())
+        z = f(qa[r]) @ f(kv[7]) / 16
+        np.testing.assert_allclose(lse[r], z + math.log(m), rtol=1e-12)
+
+
+def test_attention_zero_query_is_mean_of_selected(oracle_mod):
+    qa, kv = _attn_inputs(seed=5)
+    qa[:] = 0
+    idx = np.array([[4, 8, 15, 16, 23, 42], [0, 1, 2, -1, -1, -1]], np.int32)
+    out, lse = oracle_mod.sparse_mla(np.zeros(2, np.int64), qa, kv, idx, 1 / 16)
+    for r in range(2):
+        sel = idx[r][idx[r] >= 0]
+        np.testing.assert_allclose(out[r], np.broadcast_to(f(kv[sel, :512]).mean(0), (64, 512)), atol=1e-12)
+        np.testing.assert_allclose(lse[r], math.log(len(sel)), atol=1e-12)
+
+
+def test_attention_one_and_two_position_closed_forms(oracle_mod):
+    qa, kv = _attn_inputs(R=1, seed=6)
+    out, lse = oracle_mod.sparse_mla(np.zeros(1, np.int64), qa, kv, np.array([[13, -1]], np.int32), 0.0625)
+    np.testing.assert_allclose(out[0], np.broadcast_to(f(kv[13, :512]), (64, 512)), atol=1e-12)
+    np.testing.assert_allclose(lse[0], f(qa[0]) @ f(kv[13]) * 0.0625, rtol=1e-12)
+    out, lse = oracle_mod.sparse_mla(np.zeros(1, np.int64), qa, kv, np.array([[2, 30]], np.int32), 0.0625)
+    z1 = f(qa[0]) @ f(kv[2]) * 0.0625
+    z2 = f(qa[0]) @ f(kv[30]) * 0.0625
+    p1 = 1.0 / (1.0 + np.exp(z2 - z1))
+    ref = p1[:, None] * f(kv[2, :512])[None] + (1 - p1)[:, None] * f(kv[30, :512])[None]
+    np.testing.assert_allclose(out[0], ref, atol=1e-12)
+    np.testing.assert_allclose(lse[0], np.logaddexp(z1, z2), rtol=1e-12)
+
+
+def test_attention_absorbed_equals_expanded_mla_via_torch_sdpa(oracle_mod):
+    """Absorbed form (576-wide rows, 512-wide latent output) against the
+    expanded form the teardown's §4.5 describes (k = [W_UK c || k_pe],
+    v = W_UV c, 256-wide QK heads, scale 1/sqrt(256)), run through torch's
+    scaled_dot_product_attention in fp64 on the CPU."""
+    g = np.random.default_rng(12)
+    T, H = 40, 64
+    kv = bf16((T, 576), 13)                       # [c_kv (512) || k_pe (64)]
+    c = f(kv[:, :512])
+    k_pe = f(kv[:, 512:])
+    # W_UK [H, 192, 512] with 3 nonzeros (+-1) per latent column keeps
+    # q_abs = W_UK^T q_nope exact in bf16 for small-integer q_nope.
+    W_UK = np.zeros((H, 192, 512))
+    for h in range(H):
+        for col in range(512):
+            rows = g.choice(192, 3, replace=False)
+            W_UK[h, rows, col] = g.choice([-1.0, 1.0], 3)
+    W_UV = g.standard_normal((H, 256, 512)) / 16
+    q_nope = g.integers(-2, 3, size=(H, 192)).astype(np.float64)
+    q_pe = f(bf16((H, 64), 14))
+    q_abs = np.concatenate([np.einsum("hdc,hd->hc", W_UK, q_nope), q_pe], axis=1)
+    q_abs_bits = wl.f32_to_bf16_bits(q_abs.astype(np.float32))
+    assert np.array_equal(f(q_abs_bits), q_abs)   # exactly representable
+    idx = np.array([[1, 5, 6, 17, 22, 31, 39, -1]], np.int32)
+    sel = idx[0][idx[0] >= 0]
+    out, lse = oracle_mod.sparse_mla(np.zeros(1, np.int64), q_abs_bits[None], kv, idx, 1 / 16)
+    absorbed = np.einsum("hvc,hc->hv", W_UV, out[0])        # per-head V up-projection
+    k_nope = np.einsum("hdc,tc->htd", W_UK, c[sel])          # [H, m, 192]
+    k_full = np.concatenate([k_nope, np.broadcast_to(k_pe[sel], (H, len(sel), 64))], axis=2)
+    v_full = np.einsum("hvc,tc->htv", W_UV, c[sel])          # [H, m, 256]
+    q_full = np.concatenate([q_nope, q_pe], axis=1)[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q_full), torch.from_numpy(np.ascontiguousarray(k_full)),
+        torch.from_numpy(np.ascontiguousarray(v_full)), scale=1 / 16)[:, 0].numpy()
+    np.testing.assert_allclose(absorbed, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_dsa_equals_dense_causal_attention_when_at_most_k_visible(oracle_mod):
+    """Rows that see <= 2048 positions must reproduce dense causal MLA
+    (GLM-5 explainer: shorter than 2,048 keeps every position); dense causal
+    attention here is torch's scaled_dot_product_attention(is_causal=True)."""
+    T = 96
+    w = wl.prefill(T, seed=2)
+    x = w.generate()
+    _, _, idx, out, lse = oracle_mod.decode_step(x["visible_len"], x["row_cache_base"], x["q_idx"], x["w"],
+                                                 x["k_idx"], x["q_abs"], x["kv_latent"], 2048, 1.0, 1 / 16)
+    assert np.array_equal(idx[:, :T], np.where(np.arange(T)[None] <= np.arange(T)[:, None], np.arange(T)[None], -1))
+    q = torch.from_numpy(f(x["q_abs"])).permute(1, 0, 2)             # [64, T, 576]
+    kvf = torch.from_numpy(f(x["kv_latent"]))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, kvf[None].expand(64, T, 576), kvf[None, :, :512].expand(64, T, 512), is_causal=True, scale=1 / 16)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- printed sizes
+
+def test_printed_cache_and_flop_numbers():
+    L = golden("num_layers")
+    assert L * (512 + 64) * 2 / 1024 == golden("latent_cache_kib_per_token_78_layers")
+    assert L * 128 * 2 / 1024 == golden("index_cache_kib_per_token_78_layers")
+    T = golden("max_position_embeddings")
+    assert round(L * 576 * 2 * T / 2 ** 30, 2) == golden("latent_cache_gib_at_202752")
+    assert round(L * 128 * 2 * T / 2 ** 30, 2) == golden("index_cache_gib_at_202752")
+    assert L * golden("index_topk") * 4 == golden("index_replay_bytes_per_token")
+    assert round(2 * 64 * 196608 * 256 / 1e9, 2) == golden("full_qk_gflop_per_layer_192k")
