@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""DSA decode benchmark on one MI355X.
+
+One step = one dsa_decode_step call (lightning indexer -> causal top-2048 ->
+absorbed sparse MLA attention) over one batch of decode rows whose inputs are
+already resident in HBM.  Default workload: 64 sequences x 32,768 positions,
+one query row each (batched decode), seeded synthetic bf16 N(0,1) inputs.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Roofline: the dominant kernel is the indexer (it streams 256 bytes of index
+key per visible position).  Its average launch duration is measured here with
+HIP events around back-to-back launches of the same call on the same stream;
+achieved = algorithmic bytes per launch / that duration, against the 8 TB/s
+HBM3E peak.  Algorithmic bytes per row = 256 n (keys) + 8192 (q) + 128 (w).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+METRIC = "DSA decode tokens/s (indexer+top2048+sparse MLA) & % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+K_TOP = 2048
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="c3", help="workload: c1 | c3 | c4 | c5")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (oracle)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(REPO, "sparse_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_label(w):
+    vis = w.visible_len
+    if w.name == "c3":
+        return "batched decode: 64 sequences x 32,768 positions, one query row each, top-2048"
+    if w.name == "c4":
+        return "long-context decode: 16 sequences x 202,752 positions, one query row each, top-2048"
+    if w.name == "c1":
+        return "decode: 1 sequence x 4,096 positions, top-2048"
+    return f"{w.description} ({len(vis)} rows)"
+
+
+def traffic_from_profiles(kernel, workload, current_hash):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel source."""
+    path = os.path.join(REPO, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != current_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s):
+    import oracle
+    from sparse_attention_amd import workloads as wl
+
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+
+    def run(rows):
+        y = {k: v for k, v in x.items()}
+        for key in ("q_idx", "w", "q_abs", "visible_len", "row_cache_base"):
+            y[key] = x[key][rows]
+        t = time.perf_counter()
+        oracle.decode_step(y["visible_len"], y["row_cache_base"], y["q_idx"], y["w"], y["k_idx"], y["q_abs"],
+                           y["kv_latent"], K_TOP, wl.INDEX_SCALE, wl.SOFTMAX_SCALE)
+        return time.perf_counter() - t
+
+    R = w.num_rows
+    # rows are spread evenly over the batch; the sample grows until it costs
+    # about budget_s of wall time on all host cores
+    t1 = run([0])
+    m = int(max(1, min(R, budget_s / max(t1, 1e-3) * 0.8)))
+    rows = np.unique(np.linspace(0, R - 1, m).astype(np.int64))
+    dt = run(rows)
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {R} decode rows of the same workload (full rows: indexer over every "
+                      f"visible position, top-{K_TOP}, 64-head attention), fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): this build has "
+              f"no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_amd as dsa
+    from sparse_attention_amd import workloads as wl
+
+    dsa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.config(args.config)
+    log(f"[bench] generating {w.name}: {w.num_rows} rows, {w.cache_rows} cache rows")
+    t = time.perf_counter()
+    x = w.generate()
+    log(f"[bench] inputs ready in {time.perf_counter() - t:.1f} s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R, maxv = w.num_rows, w.max_visible
+    q_idx, wts, k_idx = bf(x["q_idx"]), torch.from_numpy(x["w"]).to(dev), bf(x["k_idx"])
+    q_abs, kv = bf(x["q_abs"]), bf(x["kv_latent"])
+    rows = dsa.Rows(torch.from_numpy(x["visible_len"]).to(dev), torch.from_numpy(x["row_cache_base"]).to(dev), maxv)
+    idx = torch.empty((R, K_TOP), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=dev)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, maxv, K_TOP), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dsa.dsa_decode_step(rows, q_idx, wts, k_idx, wl.INDEX_SCALE, q_abs, kv, wl.SOFTMAX_SCALE, K_TOP, idx, out,
+                            lse, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] decode step: {ms_step * 1e3:.1f} us/step over {args.steps} steps")
+
+    # Dominant kernel alone: the indexer, same rows and launch configuration.
+    ld = (maxv + 3) // 4 * 4
+    scores = torch.empty((R, ld), dtype=torch.float32, device=dev)
+
+    def idx_launch():
+        dsa.dsa_indexer_scores(rows, q_idx, wts, k_idx, wl.INDEX_SCALE, scores, stream=stream)
+
+    for _ in range(args.warmup):
+        idx_launch()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        idx_launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_idx = e0.elapsed_time(e1) / args.steps
+    n = x["visible_len"].astype(np.int64)
+    alg_bytes = int(np.sum(256 * n + 8192 + 128))
+    achieved = alg_bytes / (ms_idx * 1e-3) / 1e9
+    log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+
+    # Step-level algorithmic bytes (whole path) for context.
+    step_bytes = int(np.sum(256 * n + 1152 * np.minimum(n, K_TOP) + 82048 + 139264))
+    traffic = traffic_from_profiles("indexer", w.name, src_hash(["indexer.hip", "dsa_device.h"]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of rows")
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} cores")
+
+    value = R / (ms_step * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_label(w), "rows": R, "max_visible": maxv, "topk": K_TOP,
+                   "index_heads": 32, "index_dim": 128, "heads": 64, "latent_row": 576},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "indexer_rows_kernel", "kernel_us": round(ms_idx * 1e3, 2),
+                     "alg_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+        "step_alg_bytes": step_bytes,
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

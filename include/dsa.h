@@ -1,0 +1,185 @@
+/*
+ * dsa.h -- C ABI of libdsa: the DSA hot path (lightning indexer -> causal
+ * top-k -> absorbed sparse MLA attention) for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one the GLM-5 / GLM-5.1 pages describe:
+ *  - "GLM-5.1 架构深度拆解" (GLM-5.1 architecture teardown,
+ *    cctoctofx.netlify.app), CH3 §3.2 "Indexer 公式" and §3.6
+ *    "GlmMoeDsaIndexer.forward" (indexer score, causal mask, top-k), CH4 §4.1
+ *    and §4.5 "GlmMoeDsaAttention.forward" (MLA latent rows, sparse attention).
+ *  - GLM-5 explainer (ailearn.mscapital.top): the indexer paragraph (one
+ *    128-d key per position, 32 x 128 queries, ReLU, 32 weights, causal
+ *    Top-2,048 returning position IDs), the latent-cache paragraph (512 latent
+ *    + 64 RoPE key per position; the IDs only drive the gather) and the
+ *    "shorter than 2,048 keeps every position" rule.
+ *  - "GLM-5.2 架构 QA" (pillumina.github.io), Q1.1 config listing
+ *    (qk_nope_head_dim 192 + qk_rope_head_dim 64 = qk_head_dim 256).
+ *
+ * Conventions for every entry point:
+ *  - Every array pointer is a DEVICE pointer unless marked "host".  The caller
+ *    owns every buffer and the stream; the library allocates nothing and keeps
+ *    no mutable global state besides a per-device properties cache and a
+ *    thread-local error message.
+ *  - bf16 arrays are passed as `const void*` holding IEEE bfloat16 bit
+ *    patterns.  Row-major layouts, innermost dimension last.
+ *  - All work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL
+ *    means the null stream).  No call synchronizes the host.
+ *  - Host-side validation runs first and in full.  On any error nothing is
+ *    enqueued and every output is left untouched.  HIP launch failures map to
+ *    DSA_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Device array contents (visible lengths, cache bases, index lists) are
+ *    trusted: values outside the documented ranges are undefined behaviour.
+ *  - Results are deterministic: identical inputs give bitwise-identical
+ *    outputs (no floating-point atomics anywhere).
+ *  - Calls are re-entrant; calls on different streams may overlap as long as
+ *    they do not share output or workspace buffers.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported with default visibility. */
+#if defined(__GNUC__) || defined(__clang__)
+#define DSA_API __attribute__((visibility("default")))
+#else
+#define DSA_API
+#endif
+
+/* Geometry (fixed at compile time).  32 index heads x 128 dims with one
+ * 128-d key per position (teardown §3.6 steps 1-2); 64 attention heads over a
+ * 576-wide latent row = 512 c_kv + 64 RoPE key (teardown CH4 §4.1, §4.2);
+ * top-k up to index_topk = 2048 (teardown CH2 constraint 1, §3.6 step 7). */
+#define DSA_INDEX_HEADS 32
+#define DSA_INDEX_DIM 128
+#define DSA_HEADS 64
+#define DSA_LATENT_DIM 512
+#define DSA_ROPE_DIM 64
+#define DSA_ROW_DIM 576
+#define DSA_TOPK_MAX 2048
+/* Largest visible length a row may have (positions per sequence). */
+#define DSA_MAX_VISIBLE (1 << 24)
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, bad size, bad scale ... */
+    DSA_ERR_MISALIGNED = 2,          /* a pointer or stride breaks its alignment rule */
+    DSA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_size value */
+    DSA_ERR_NO_DEVICE = 4,           /* no HIP device, or the current device is not gfx950 */
+    DSA_ERR_HIP = 5                  /* a HIP runtime call or kernel launch failed */
+} dsa_status_t;
+
+/*
+ * Query rows.  Row r belongs to a sequence whose caches start at packed cache
+ * row row_cache_base[r]; it sees positions [0, visible_len[r]) of that
+ * sequence (causal, its own position included: keys are appended before
+ * scoring, teardown §3.6 step 3 and §4.5 steps 5-6).  A decode row of a
+ * sequence of length T has visible_len = T; prefill row i has i + 1.
+ */
+typedef struct {
+    int32_t num_rows;              /* host: R >= 1 */
+    int32_t max_visible;           /* host: >= every visible_len[r]; <= DSA_MAX_VISIBLE */
+    const int32_t* visible_len;    /* [R], each in [1, max_visible] */
+    const int64_t* row_cache_base; /* [R], each >= 0 */
+} dsa_rows_t;
+
+/* Library version string (static storage). */
+DSA_API const char* dsa_version(void);
+/* Human-readable name of a status code (static storage; never NULL). */
+DSA_API const char* dsa_status_string(dsa_status_t status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+DSA_API const char* dsa_last_error_detail(void);
+
+/*
+ * Lightning-indexer scores (teardown §3.6 step 5, §3.2 steps 4-6; explainer
+ * indexer paragraph):
+ *     scores[r, t] = sum_h w[r,h] * ReLU(index_scale * sum_d q_idx[r,h,d] * k_idx[base_r + t, d])
+ * for 0 <= t < visible_len[r].  Columns >= visible_len[r] are not written.
+ *  q_idx  [R, 32, 128] bf16, 16-B aligned (post-RoPE index queries)
+ *  w      [R, 32] fp32, 16-B aligned (already multiplied by 32^-1/2 upstream,
+ *         teardown §3.6 step 4)
+ *  k_idx  [*, 128] bf16 packed index-key cache, 16-B aligned
+ *  index_scale  > 0 and finite
+ *  scores [R, ld] fp32, 16-B aligned; ld >= max_visible and ld % 4 == 0
+ * Products are exact in fp32 (bf16 x bf16); sums are fp32.
+ */
+DSA_API dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const float* w,
+                                const void* k_idx, float index_scale, float* scores, int64_t ld,
+                                void* hip_stream);
+
+/* Workspace bytes dsa_topk_select needs for these sizes (host arithmetic only). */
+DSA_API size_t dsa_topk_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k);
+
+/*
+ * Causal top-k select (teardown §3.6 step 7 "topk = min(index_topk,
+ * total_len)", §3.4 determinism requirement; explainer "shorter than 2,048
+ * keeps all; the top-k is a set of positions").
+ * For each row picks k_r = min(k, visible_len[r]) positions of scores[r, 0:n_r)
+ * with the largest scores.  Order: larger score first; -0.0 equals +0.0; equal
+ * scores go to the lower position; NaN ranks below every number.
+ *  scores   [R, ld] fp32, 16-B aligned, ld >= max_visible, ld % 4 == 0
+ *  k        1 .. 2048
+ *  indices  [R, k] int32, 4-B aligned: the k_r positions in ascending order,
+ *           then -1 padding up to k
+ *  ws       device workspace of ws_bytes >= dsa_topk_workspace_size(R, max_visible, k),
+ *           256-B aligned; contents need no initialisation and are clobbered
+ */
+DSA_API dsa_status_t dsa_topk_select(const dsa_rows_t* rows, const float* scores, int64_t ld, int32_t k,
+                             int32_t* indices, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Workspace bytes dsa_sparse_mla_attn needs for these sizes (host arithmetic only). */
+DSA_API size_t dsa_sparse_mla_workspace_size(int32_t num_rows, int32_t k);
+
+/*
+ * Absorbed-MLA attention over the selected positions (teardown §4.5 steps 2,
+ * 6, 7; explainer latent-cache paragraph; GLM-5.2 QA Q1.1 for the 256-wide
+ * original QK head that fixes softmax_scale = 1/sqrt(256)):
+ *     z[h,j]   = softmax_scale * sum_{d<576} q_abs[r,h,d] * kv[base_r + idx_j, d]
+ *     p[h,j]   = softmax_j(z[h,:])
+ *     out[r,h,c] = sum_j p[h,j] * kv[base_r + idx_j, c]        c < 512
+ *     lse[r,h] = log sum_j exp(z[h,j])
+ * over the entries idx_j >= 0 of indices[r, 0:k] (negative entries are
+ * padding and are skipped).  q_abs = [W_UK^T q_nope (512) || q_pe (64)] per
+ * head; the latent row is [c_kv (512) || k_pe (64)]; the output is the
+ * 512-wide latent before the per-head V up-projection.
+ *  q_abs      [R, 64, 576] bf16, 16-B aligned
+ *  kv_latent  [*, 576] bf16 packed latent cache, 16-B aligned
+ *  indices    [R, k] int32, entries in [0, visible_len[r]) or negative
+ *  k          1 .. 2048;  softmax_scale > 0 and finite
+ *  out_latent [R, 64, 512] fp32, 16-B aligned
+ *  out_lse    [R, 64] fp32 or NULL
+ *  ws         ws_bytes >= dsa_sparse_mla_workspace_size(R, k), 256-B aligned
+ * A row whose entries are all negative gets out = 0 and lse = -inf.
+ * P is rounded to bf16 (round-to-nearest-even) for the P.V product; all sums
+ * are fp32.
+ */
+DSA_API dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_abs, const void* kv_latent,
+                                 const int32_t* indices, int32_t k, float softmax_scale,
+                                 float* out_latent, float* out_lse, void* ws, size_t ws_bytes,
+                                 void* hip_stream);
+
+/* Workspace bytes dsa_decode_step needs for these sizes (host arithmetic only). */
+DSA_API size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k);
+
+/*
+ * The whole path in one call: dsa_indexer_scores into workspace, then
+ * dsa_topk_select into `indices`, then dsa_sparse_mla_attn.  Arguments mean
+ * what they mean above; `indices` [R, k] int32 receives the selection.
+ * ws_bytes >= dsa_decode_step_workspace_size(R, max_visible, k).
+ */
+DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const float* w,
+                             const void* k_idx, float index_scale, const void* q_abs,
+                             const void* kv_latent, float softmax_scale, int32_t k,
+                             int32_t* indices, float* out_latent, float* out_lse, void* ws,
+                             size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

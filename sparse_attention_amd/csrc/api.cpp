@@ -1,0 +1,289 @@
+// api.cpp -- the C ABI of libdsa: argument validation, workspace sizing,
+// device checks and launch sequencing.  See include/dsa.h for the contract.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+dsa_status_t fail(dsa_status_t s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+constexpr int32_t kMaxRows = 1 << 24;
+
+dsa_status_t check_rows(const dsa_rows_t* rows)
+{
+    if (!rows) return fail(DSA_ERR_INVALID_ARGUMENT, "rows is NULL");
+    if (rows->num_rows < 1 || rows->num_rows > kMaxRows)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows=%d outside [1, %d]", rows->num_rows, kMaxRows);
+    if (rows->max_visible < 1 || rows->max_visible > DSA_MAX_VISIBLE)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "max_visible=%d outside [1, %d]", rows->max_visible, DSA_MAX_VISIBLE);
+    if (!rows->visible_len) return fail(DSA_ERR_INVALID_ARGUMENT, "rows->visible_len is NULL");
+    if (!rows->row_cache_base) return fail(DSA_ERR_INVALID_ARGUMENT, "rows->row_cache_base is NULL");
+    if (!aligned(rows->visible_len, 4)) return fail(DSA_ERR_MISALIGNED, "visible_len not 4-byte aligned");
+    if (!aligned(rows->row_cache_base, 8)) return fail(DSA_ERR_MISALIGNED, "row_cache_base not 8-byte aligned");
+    return DSA_OK;
+}
+
+dsa_status_t check_ptr16(const void* p, const char* name)
+{
+    if (!p) return fail(DSA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(DSA_ERR_MISALIGNED, "%s not 16-byte aligned", name);
+    return DSA_OK;
+}
+
+dsa_status_t check_k(int32_t k)
+{
+    if (k < 1 || k > DSA_TOPK_MAX) return fail(DSA_ERR_INVALID_ARGUMENT, "k=%d outside [1, %d]", k, DSA_TOPK_MAX);
+    return DSA_OK;
+}
+
+dsa_status_t check_ld(const dsa_rows_t* rows, int64_t ld)
+{
+    if (ld < rows->max_visible) return fail(DSA_ERR_INVALID_ARGUMENT, "ld=%lld < max_visible=%d", (long long)ld, rows->max_visible);
+    if (ld % 4 != 0) return fail(DSA_ERR_MISALIGNED, "ld=%lld is not a multiple of 4", (long long)ld);
+    return DSA_OK;
+}
+
+dsa_status_t check_ws(const void* ws, size_t ws_bytes, size_t need)
+{
+    if (ws_bytes < need)
+        return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, need);
+    if (need > 0) {
+        if (!ws) return fail(DSA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+        if (!aligned(ws, 256)) return fail(DSA_ERR_MISALIGNED, "workspace not 256-byte aligned");
+    }
+    return DSA_OK;
+}
+
+// Per-device "is this a gfx950" cache.
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 ok, 2 unsupported
+
+dsa_status_t check_device()
+{
+    int dev = -1;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(DSA_ERR_NO_DEVICE, "no HIP device present");
+    }
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(DSA_ERR_NO_DEVICE, "hipGetDevice failed");
+    }
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (g_dev_state[dev] == 1) return DSA_OK;
+        if (g_dev_state[dev] == 2) return fail(DSA_ERR_NO_DEVICE, "device %d is not gfx950", dev);
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DSA_ERR_NO_DEVICE, "hipGetDeviceProperties(%d) failed", dev);
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        g_dev_state[dev] = ok ? 1 : 2;
+    }
+    if (!ok) return fail(DSA_ERR_NO_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    return DSA_OK;
+}
+
+dsa_status_t after_launch(hipStream_t stream, const char* what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    if (dsa::sync_debug()) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    }
+    return DSA_OK;
+}
+
+size_t scores_ld(int32_t max_visible) { return dsa::align_up((size_t)max_visible, 4); }
+
+#define DSA_TRY(expr)                        \
+    do {                                     \
+        dsa_status_t _s = (expr);            \
+        if (_s != DSA_OK) return _s;         \
+    } while (0)
+
+}  // namespace
+
+namespace dsa {
+bool sync_debug()
+{
+    static const bool on = [] {
+        const char* e = std::getenv("DSA_SYNC_DEBUG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+}  // namespace dsa
+
+extern "C" {
+
+const char* dsa_version(void) { return "libdsa 0.1.0 (gfx950)"; }
+
+const char* dsa_status_string(dsa_status_t s)
+{
+    switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+    case DSA_ERR_MISALIGNED: return "DSA_ERR_MISALIGNED";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL";
+    case DSA_ERR_NO_DEVICE: return "DSA_ERR_NO_DEVICE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    }
+    return "DSA_ERR_UNKNOWN_STATUS";
+}
+
+const char* dsa_last_error_detail(void) { return g_detail; }
+
+dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                                float index_scale, float* scores, int64_t ld, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_ptr16(q_idx, "q_idx"));
+    DSA_TRY(check_ptr16(w, "w"));
+    DSA_TRY(check_ptr16(k_idx, "k_idx"));
+    DSA_TRY(check_ptr16(scores, "scores"));
+    DSA_TRY(check_ld(rows, ld));
+    if (!good_scale(index_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "index_scale must be finite and > 0");
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::launch_indexer_scores(rows->num_rows, rows->max_visible, rows->visible_len, rows->row_cache_base,
+                               (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, index_scale, scores, ld, st);
+    return after_launch(st, "indexer");
+}
+
+size_t dsa_topk_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
+{
+    (void)k;
+    if (num_rows < 1 || max_visible < 1) return 0;
+    return dsa::topk_workspace_bytes(num_rows, max_visible);
+}
+
+dsa_status_t dsa_topk_select(const dsa_rows_t* rows, const float* scores, int64_t ld, int32_t k, int32_t* indices,
+                             void* ws, size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_ptr16(scores, "scores"));
+    DSA_TRY(check_ld(rows, ld));
+    DSA_TRY(check_k(k));
+    if (!indices) return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+    if (!aligned(indices, 4)) return fail(DSA_ERR_MISALIGNED, "indices not 4-byte aligned");
+    DSA_TRY(check_ws(ws, ws_bytes, dsa_topk_workspace_size(rows->num_rows, rows->max_visible, k)));
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::TopkWorkspace tw = dsa::topk_workspace_carve(ws, rows->num_rows, rows->max_visible);
+    dsa::launch_topk(rows->num_rows, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);
+    return after_launch(st, "topk");
+}
+
+size_t dsa_sparse_mla_workspace_size(int32_t num_rows, int32_t k)
+{
+    if (num_rows < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
+    return dsa::attn_workspace_bytes(num_rows, k);
+}
+
+dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_abs, const void* kv_latent,
+                                 const int32_t* indices, int32_t k, float softmax_scale, float* out_latent,
+                                 float* out_lse, void* ws, size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_ptr16(q_abs, "q_abs"));
+    DSA_TRY(check_ptr16(kv_latent, "kv_latent"));
+    DSA_TRY(check_k(k));
+    if (!indices) return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+    if (!aligned(indices, 4)) return fail(DSA_ERR_MISALIGNED, "indices not 4-byte aligned");
+    DSA_TRY(check_ptr16(out_latent, "out_latent"));
+    if (out_lse && !aligned(out_lse, 4)) return fail(DSA_ERR_MISALIGNED, "out_lse not 4-byte aligned");
+    if (!good_scale(softmax_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    DSA_TRY(check_ws(ws, ws_bytes, dsa_sparse_mla_workspace_size(rows->num_rows, k)));
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::launch_sparse_mla(rows->num_rows, rows->row_cache_base, (const uint16_t*)q_abs,
+                           (const uint16_t*)kv_latent, indices, k, softmax_scale, out_latent, out_lse, ws, st);
+    return after_launch(st, "sparse_mla");
+}
+
+size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
+{
+    if (num_rows < 1 || max_visible < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
+    size_t b = dsa::align_up((size_t)num_rows * scores_ld(max_visible) * 4, 256);
+    b += dsa::align_up(dsa_topk_workspace_size(num_rows, max_visible, k), 256);
+    b += dsa::align_up(dsa_sparse_mla_workspace_size(num_rows, k), 256);
+    return b;
+}
+
+dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                             float index_scale, const void* q_abs, const void* kv_latent, float softmax_scale,
+                             int32_t k, int32_t* indices, float* out_latent, float* out_lse, void* ws,
+                             size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_ptr16(q_idx, "q_idx"));
+    DSA_TRY(check_ptr16(w, "w"));
+    DSA_TRY(check_ptr16(k_idx, "k_idx"));
+    DSA_TRY(check_ptr16(q_abs, "q_abs"));
+    DSA_TRY(check_ptr16(kv_latent, "kv_latent"));
+    DSA_TRY(check_k(k));
+    if (!indices) return fail(DSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+    if (!aligned(indices, 4)) return fail(DSA_ERR_MISALIGNED, "indices not 4-byte aligned");
+    DSA_TRY(check_ptr16(out_latent, "out_latent"));
+    if (out_lse && !aligned(out_lse, 4)) return fail(DSA_ERR_MISALIGNED, "out_lse not 4-byte aligned");
+    if (!good_scale(index_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "index_scale must be finite and > 0");
+    if (!good_scale(softmax_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    DSA_TRY(check_ws(ws, ws_bytes, dsa_decode_step_workspace_size(rows->num_rows, rows->max_visible, k)));
+    DSA_TRY(check_device());
+
+    hipStream_t st = (hipStream_t)hip_stream;
+    const int32_t R = rows->num_rows;
+    const int64_t ld = (int64_t)scores_ld(rows->max_visible);
+    char* p = (char*)ws;
+    float* scores = (float*)p;
+    p += dsa::align_up((size_t)R * ld * 4, 256);
+    void* tws = p;
+    p += dsa::align_up(dsa_topk_workspace_size(R, rows->max_visible, k), 256);
+    void* aws = p;
+
+    dsa::launch_indexer_scores(R, rows->max_visible, rows->visible_len, rows->row_cache_base, (const uint16_t*)q_idx,
+                               w, (const uint16_t*)k_idx, index_scale, scores, ld, st);
+    DSA_TRY(after_launch(st, "decode_step/indexer"));
+    dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, R, rows->max_visible);
+    dsa::launch_topk(R, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);
+    DSA_TRY(after_launch(st, "decode_step/topk"));
+    dsa::launch_sparse_mla(R, rows->row_cache_base, (const uint16_t*)q_abs, (const uint16_t*)kv_latent, indices, k,
+                           softmax_scale, out_latent, out_lse, aws, st);
+    return after_launch(st, "decode_step/sparse_mla");
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// dsa_device.h -- device-side helpers shared by the libdsa kernels (gfx950).
+//
+// MFMA lane layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l supplies row (l & 15) and 8 consecutive k values of k-group (l >> 4)
+//     B: lane l supplies column (l & 15) and the same 8 k values of k-group (l >> 4)
+//     D: lane l, element v holds D[4 * (l >> 4) + v][l & 15]
+//   Which k an (A, B) slot pair stands for is free as long as A and B agree,
+//   so callers pick k orders that make their loads contiguous.
+//
+//   ds_read_tr16_b64 (per 16-lane group): source lane s = c + 4 * k (c, k in
+//   0..3) names an 8-byte chunk; result lane 4 * c + e receives element e of
+//   the chunks named by lanes c, c + 4, c + 8, c + 12, in that order.  With
+//   source lane (c, k) pointing at row k, columns 4c..4c+3 of a row-major
+//   16-bit matrix, result lane j gets column j of rows 0..3: a 4x16 -> 16x4
+//   transpose, which turns row-major LDS tiles into MFMA operands whose k
+//   runs over rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global load of 8 bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
+{
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 load_u32x4(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Two transposing LDS reads glued into one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint16_t* lo, const uint16_t* hi)
+{
+    shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lo));
+    shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(hi));
+    typedef short shortx8 __attribute__((ext_vector_type(8)));
+    shortx8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Order-preserving 32-bit key of an fp32 score: a larger key means a larger
+// score; -0.0 and +0.0 share a key; every NaN maps to 0, below -inf.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max_16(float v)
+{
+    // reduce across the 16 lanes that share (lane >> 4)
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_16(float v)
+{
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+}  // namespace dsa

@@ -1,0 +1,53 @@
+// dsa_internal.h -- host-side launcher declarations shared by api.cpp and the
+// kernel translation units.  Launchers only enqueue work; validation happens
+// in api.cpp before any of them is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// ---- indexer -------------------------------------------------------------
+// Positions one indexer workgroup scores (a multiple of 256).
+int indexer_pick_chunk(int32_t num_rows, int32_t max_visible);
+void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis,
+                           const int64_t* base, const uint16_t* q, const float* w,
+                           const uint16_t* kc, float scale, float* scores, int64_t ld,
+                           hipStream_t stream);
+
+// ---- top-k ---------------------------------------------------------------
+constexpr int TK_CHUNK = 4096;     // scores one top-k workgroup owns
+constexpr int TK_BINS = 4096;      // 12-bit top radix digit
+constexpr int TK_CAP = 4096;       // candidate slots per row
+constexpr int TK_ROWST = 8;        // u32 words of per-row state
+constexpr int TK_CHUNKST = 4;      // u32 words of per-chunk state
+constexpr int TK_MAX_CHUNKS = 4096;  // DSA_MAX_VISIBLE / TK_CHUNK
+
+struct TopkWorkspace {
+    uint32_t* hist;            // [R][TK_BINS]
+    uint32_t* rowst;           // [R][TK_ROWST]
+    uint32_t* chunkst;         // [R][CH][TK_CHUNKST]
+    unsigned long long* cand;  // [R][TK_CAP]
+    int32_t chunks;            // CH
+};
+size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible);
+TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visible);
+void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, const float* scores,
+                 int64_t ld, int32_t k, int32_t* indices, const TopkWorkspace& tw,
+                 hipStream_t stream);
+
+// ---- sparse MLA attention --------------------------------------------------
+int attn_pick_splits(int32_t num_rows, int32_t k);
+size_t attn_workspace_bytes(int32_t num_rows, int32_t k);
+void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa,
+                       const uint16_t* kv, const int32_t* idx, int32_t k, float softmax_scale,
+                       float* out, float* lse, void* ws, hipStream_t stream);
+
+// Debug aid: when DSA_SYNC_DEBUG=1, synchronize after every launch.
+bool sync_debug();
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace dsa

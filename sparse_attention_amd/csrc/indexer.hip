@@ -1,0 +1,131 @@
+// indexer.hip -- lightning-indexer scores on gfx950.
+//
+// Computes scores[r, t] = sum_h w[r,h] * ReLU(scale * q[r,h,:] . K[base_r + t, :])
+// for t < n_r ("GLM-5.1 架构深度拆解" §3.6 step 5 and §3.2 steps 4-6; the
+// GLM-5 explainer's indexer paragraph: one 128-d key per position shared by
+// all 32 index heads).
+//
+// Design (decode rows, each row streaming its own key cache):
+//  - One workgroup = one row x `chunk` positions; 4 waves split the chunk into
+//    contiguous quarters.  The work is HBM-bound (256 key bytes per position
+//    against 8192 MFMA flops), so the kernel's job is keeping enough 16-byte
+//    loads in flight.
+//  - The contraction runs on v_mfma_f32_16x16x32_bf16 with the 32 index heads
+//    as M (two 16-row blocks) and 16 positions as N: the key rows are the B
+//    operand and are loaded straight from HBM into registers.  Lane (j, g)
+//    loads bytes [64 s + 16 g, +16) of position j's 256-byte row at k-step s,
+//    so the four lanes of a position read 64 contiguous bytes per load; Q uses
+//    the same k order and stays in registers for the whole chunk.
+//  - The output layout puts 4 heads of one position in each lane, so the
+//    ReLU and head weighting stay in registers and the head sum needs only two
+//    cross-lane steps (lanes j, j+16, j+32, j+48).  Every lane ends with the
+//    full score, so each lane group stores a different 16-position group and
+//    one store covers 64 consecutive scores.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int IDX_WAVES = 4;
+constexpr int IDX_GROUPS = 4;  // 16-position groups per wave per iteration
+
+__global__ __launch_bounds__(256) void indexer_rows_kernel(
+    const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
+    const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
+    int64_t ld, int chunk)
+{
+    const int r = blockIdx.y;
+    const int n = vis[r];
+    const int c0 = blockIdx.x * chunk;
+    if (c0 >= n) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const int per_wave = chunk / IDX_WAVES;
+    const int p_lo = c0 + wave * per_wave;
+    const int p_hi = min(n, p_lo + per_wave);
+    if (p_lo >= p_hi) return;
+
+    // A operands: Q[r][16 hb + j][32 s + 8 g .. +8] for head blocks hb = 0, 1.
+    const uint16_t* qr = q + (int64_t)r * (32 * 128);
+    bf16x8 qa[2][4];
+#pragma unroll
+    for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) qa[hb][s] = load_bf16x8(qr + (hb * 16 + j) * 128 + 32 * s + 8 * g);
+    // Head weights of the output rows this lane holds: heads 4g+v and 16+4g+v.
+    float w0[4], w1[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        w0[v] = w[r * 32 + 4 * g + v];
+        w1[v] = w[r * 32 + 16 + 4 * g + v];
+    }
+
+    const uint16_t* kb = kc + base[r] * 128;
+    float* srow = scores + (int64_t)r * ld;
+
+    for (int p0 = p_lo; p0 < p_hi; p0 += 16 * IDX_GROUPS) {
+        bf16x8 kv[IDX_GROUPS][4];
+#pragma unroll
+        for (int u = 0; u < IDX_GROUPS; u++) {
+            // Reads past the row's visible range are clamped onto its last
+            // position; their results are never stored.
+            const int pc = min(p0 + 16 * u + j, n - 1);
+            const uint16_t* kp = kb + (int64_t)pc * 128 + 8 * g;
+#pragma unroll
+            for (int s = 0; s < 4; s++) kv[u][s] = load_bf16x8(kp + 32 * s);
+        }
+        float part[IDX_GROUPS];
+#pragma unroll
+        for (int u = 0; u < IDX_GROUPS; u++) {
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f};
+            floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                a0 = mfma_16x16x32(qa[0][s], kv[u][s], a0);
+                a1 = mfma_16x16x32(qa[1][s], kv[u][s], a1);
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; v++) acc += w0[v] * fmaxf(a0[v] * scale, 0.f);
+#pragma unroll
+            for (int v = 0; v < 4; v++) acc += w1[v] * fmaxf(a1[v] * scale, 0.f);
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            part[u] = acc;
+        }
+        // Lane group g stores group u == g: 64 consecutive scores per store.
+        float mine = part[0];
+#pragma unroll
+        for (int u = 1; u < IDX_GROUPS; u++) mine = (g == u) ? part[u] : mine;
+        const int pos = p0 + 16 * g + j;
+        if (pos < p_hi) srow[pos] = mine;
+    }
+}
+
+}  // namespace
+
+int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
+{
+    // Aim for >= 2048 workgroups (8 per CU) without going below 256
+    // positions (one 64-position iteration per wave).
+    int chunk = 4096;
+    while (chunk > 256 && (int64_t)num_rows * ((max_visible + chunk - 1) / chunk) < 2048) chunk /= 2;
+    return chunk;
+}
+
+void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis, const int64_t* base,
+                           const uint16_t* q, const float* w, const uint16_t* kc, float scale, float* scores,
+                           int64_t ld, hipStream_t stream)
+{
+    const int chunk = indexer_pick_chunk(num_rows, max_visible);
+    dim3 grid((max_visible + chunk - 1) / chunk, num_rows);
+    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld,
+                       chunk);
+}
+
+}  // namespace dsa

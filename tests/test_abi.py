@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/dsa.h declares, sizes workspaces, and rejects bad arguments before it
+touches the device (so on a machine without a GPU a fully valid call reports
+DSA_ERR_NO_DEVICE and nothing else)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch
+
+import sparse_attention_amd as m
+
+# A fully valid call with the fake pointers below would launch kernels on a
+# real device, so those calls are made only where no GPU is present.
+HAS_GPU = torch.cuda.is_available()
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsa.h")
+
+OK, INVALID, MISALIGNED, WS_SMALL, NO_DEVICE, HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.library_path()):
+        from sparse_attention_amd.build import build_library
+        build_library()
+    return m.load_library()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DSA_API\s+[\w\s\*]+?\b(dsa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_symbols() == sorted(m.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in m.STATUS_NAMES.items():
+        assert lib.dsa_status_string(code).decode() == name
+    assert lib.dsa_status_string(99).decode() == "DSA_ERR_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes(lib):
+    assert m.dsa_topk_workspace_size(0, 10, 2048) == 0
+    assert m.dsa_sparse_mla_workspace_size(1, 0) == 0
+    assert m.dsa_decode_step_workspace_size(1, 1, 2049) == 0
+    a = m.dsa_topk_workspace_size(16, 202752, 2048)
+    b = m.dsa_topk_workspace_size(32, 202752, 2048)
+    assert 0 < a < b and a % 256 == 0
+    # decode-step workspace holds the fp32 scores of every row
+    d = m.dsa_decode_step_workspace_size(64, 32768, 2048)
+    assert d >= 64 * 32768 * 4 + m.dsa_topk_workspace_size(64, 32768, 2048)
+    # many rows need no split partials
+    assert m.dsa_sparse_mla_workspace_size(8192, 2048) == 0
+    assert m.dsa_sparse_mla_workspace_size(16, 2048) > 0
+
+
+def _rows(R=4, maxv=100, vis=0x10000, base=0x20000):
+    return m._CRows(R, maxv, vis, base)
+
+
+def _call_topk(lib, rows, scores=0x1000, ld=100, k=2048, idx=0x3000, ws=0x100000, ws_bytes=1 << 30):
+    return lib.dsa_topk_select(ctypes.byref(rows) if rows is not None else None, scores, ld, k, idx, ws, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("case, expect", [
+    (dict(rows=None), INVALID),
+    (dict(rows=_rows(R=0)), INVALID),
+    (dict(rows=_rows(maxv=0)), INVALID),
+    (dict(rows=_rows(maxv=(1 << 24) + 1)), INVALID),
+    (dict(rows=_rows(vis=0)), INVALID),
+    (dict(rows=_rows(base=0)), INVALID),
+    (dict(rows=_rows(base=0x20004)), MISALIGNED),
+    (dict(scores=0), INVALID),
+    (dict(scores=0x1004), MISALIGNED),
+    (dict(ld=99), INVALID),
+    (dict(ld=102, rows=_rows(maxv=100)), MISALIGNED),
+    (dict(k=0), INVALID),
+    (dict(k=2049), INVALID),
+    (dict(idx=0), INVALID),
+    (dict(idx=0x3002), MISALIGNED),
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(ws=0), INVALID),
+    (dict(ws=0x100010), MISALIGNED),
+    (dict(), NO_DEVICE),
+])
+def test_topk_validation(lib, case, expect):
+    case = dict(case)
+    rows = case.pop("rows", _rows())
+    if expect == NO_DEVICE and HAS_GPU:
+        pytest.skip("a GPU is present: a valid call would launch on fake pointers")
+    status = _call_topk(lib, rows, **case)
+    assert status == expect, lib.dsa_last_error_detail()
+    assert lib.dsa_last_error_detail().decode() != ""
+
+
+def test_indexer_validation(lib):
+    r = _rows()
+    f = lambda **kw: lib.dsa_indexer_scores(ctypes.byref(r), kw.get("q", 0x1000), kw.get("w", 0x2000),
+                                            kw.get("k", 0x3000), kw.get("scale", 1.0), kw.get("s", 0x4000),
+                                            kw.get("ld", 100), None)
+    assert f(q=0) == INVALID
+    assert f(q=0x1008) == MISALIGNED
+    assert f(w=0x2004) == MISALIGNED
+    assert f(k=0) == INVALID
+    assert f(s=0x4008) == MISALIGNED
+    assert f(scale=0.0) == INVALID
+    assert f(scale=float("nan")) == INVALID
+    assert f(scale=float("inf")) == INVALID
+    assert f(scale=-1.0) == INVALID
+    assert f(ld=96) == INVALID
+    if not HAS_GPU:
+        assert f() == NO_DEVICE
+
+
+def test_attention_and_decode_step_validation(lib):
+    r = _rows(R=16)
+    ws_need = m.dsa_sparse_mla_workspace_size(16, 2048)
+    f = lambda **kw: lib.dsa_sparse_mla_attn(ctypes.byref(r), kw.get("qa", 0x1000), kw.get("kv", 0x2000),
+                                             kw.get("idx", 0x3000), kw.get("k", 2048), kw.get("scale", 0.0625),
+                                             kw.get("out", 0x4000), kw.get("lse", None), kw.get("ws", 0x100000),
+                                             kw.get("ws_bytes", ws_need), None)
+    assert f(qa=0) == INVALID
+    assert f(kv=0x2001) == MISALIGNED
+    assert f(idx=0) == INVALID
+    assert f(k=0) == INVALID
+    assert f(scale=0.0) == INVALID
+    assert f(out=0x4004) == MISALIGNED
+    assert f(lse=0x5002) == MISALIGNED
+    assert f(ws_bytes=ws_need - 1) == WS_SMALL
+    if not HAS_GPU:
+        assert f() == NO_DEVICE
+    need = m.dsa_decode_step_workspace_size(16, 100, 2048)
+    g = lambda **kw: lib.dsa_decode_step(ctypes.byref(r), 0x1000, 0x2000, 0x3000, kw.get("iscale", 1.0), 0x4000,
+                                         0x5000, kw.get("scale", 0.0625), kw.get("k", 2048), 0x6000, 0x7000, None,
+                                         0x100000, kw.get("ws_bytes", need), None)
+    assert g(iscale=0.0) == INVALID
+    assert g(scale=float("nan")) == INVALID
+    assert g(k=4096) == INVALID
+    assert g(ws_bytes=need - 256) == WS_SMALL
+    if not HAS_GPU:
+        assert g() == NO_DEVICE
