@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--config", default="c3", help="workload: c1 | c3 | c4 | c5")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU baseline budget (oracle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mode", default="decode", choices=["decode", "copy"],
+                   help="copy: a plain device-to-device copy of --copy-mib MiB, repeated --steps times, to "
+                        "calibrate HBM byte counters against a kernel of known traffic")
+    p.add_argument("--copy-mib", type=int, default=1024)
     return p.parse_args()
 
 
@@ -118,6 +122,18 @@ def main():
 
     import sparse_attention_amd as dsa
     from sparse_attention_amd import workloads as wl
+
+    if args.mode == "copy":
+        dev = torch.device("cuda:0")
+        nbytes = args.copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
 
     dsa.load_library()
     dev = torch.device("cuda:0")

@@ -72,22 +72,36 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Cross-lane steps on the VALU (DPP), all inside a 16-lane row: swap
+// neighbours, swap pairs, mirror each half-row, mirror the row.  After the
+// four steps every lane of the row holds the reduction of all 16 lanes, and
+// both partners of every step combine the same two values, so all 16 lanes
+// end bitwise equal.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_1032 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
 __device__ __forceinline__ float wave_max_16(float v)
 {
-    // reduce across the 16 lanes that share (lane >> 4)
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
+    v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_MIRROR>(v));
     return v;
 }
 
 __device__ __forceinline__ float wave_sum_16(float v)
 {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+    v += dpp_f32<DPP_QUAD_1032>(v);
+    v += dpp_f32<DPP_QUAD_2301>(v);
+    v += dpp_f32<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f32<DPP_ROW_MIRROR>(v);
     return v;
 }
 

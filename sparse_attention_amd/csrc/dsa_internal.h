@@ -10,7 +10,7 @@
 namespace dsa {
 
 // ---- indexer -------------------------------------------------------------
-// Positions one indexer workgroup scores (a multiple of 256).
+// Indexer workgroups per row.
 int indexer_pick_chunk(int32_t num_rows, int32_t max_visible);
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis,
                            const int64_t* base, const uint16_t* q, const float* w,

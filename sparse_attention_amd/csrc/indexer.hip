@@ -6,10 +6,10 @@
 // all 32 index heads).
 //
 // Design (decode rows, each row streaming its own key cache):
-//  - One workgroup = one row x `chunk` positions; 4 waves split the chunk into
-//    contiguous quarters.  The work is HBM-bound (256 key bytes per position
-//    against 8192 MFMA flops), so the kernel's job is keeping enough 16-byte
-//    loads in flight.
+//  - The work is HBM-bound (256 key bytes per position against 8192 MFMA
+//    flops), so the kernel's job is keeping enough 16-byte loads in flight
+//    with good DRAM locality: the waves of a row sweep it together in
+//    interleaved 64-position blocks, each wave prefetching its next block.
 //  - The contraction runs on v_mfma_f32_16x16x32_bf16 with the 32 index heads
 //    as M (two 16-row blocks) and 16 positions as N: the key rows are the B
 //    operand and are loaded straight from HBM into registers.  Lane (j, g)
@@ -29,26 +29,29 @@ namespace dsa {
 namespace {
 
 constexpr int IDX_WAVES = 4;
-constexpr int IDX_GROUPS = 4;  // 16-position groups per wave per iteration
+constexpr int IDX_GROUPS = 4;               // 16-position groups per block
+constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 
+// Grid: (waves_per_row / 4, rows).  The waves of one row sweep it together:
+// wave wr of the row scores 64-position blocks wr, wr + NW, wr + 2 NW, ...
+// (NW = waves per row), so the waves in flight read one compact, advancing
+// window of the key cache per row instead of thousands of scattered streams,
+// which keeps DRAM pages open.  Each wave loads its next block before
+// scoring the current one.
 __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
     const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
-    int64_t ld, int chunk)
+    int64_t ld)
 {
     const int r = blockIdx.y;
     const int n = vis[r];
-    const int c0 = blockIdx.x * chunk;
-    if (c0 >= n) return;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g = lane >> 4;
-
-    const int per_wave = chunk / IDX_WAVES;
-    const int p_lo = c0 + wave * per_wave;
-    const int p_hi = min(n, p_lo + per_wave);
-    if (p_lo >= p_hi) return;
+    const int nw = gridDim.x * IDX_WAVES;
+    const int wr = blockIdx.x * IDX_WAVES + wave;
+    if (wr * IDX_BLOCK >= n) return;
 
     // A operands: Q[r][16 hb + j][32 s + 8 g .. +8] for head blocks hb = 0, 1.
     const uint16_t* qr = q + (int64_t)r * (32 * 128);
@@ -68,8 +71,8 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const uint16_t* kb = kc + base[r] * 128;
     float* srow = scores + (int64_t)r * ld;
 
-    for (int p0 = p_lo; p0 < p_hi; p0 += 16 * IDX_GROUPS) {
-        bf16x8 kv[IDX_GROUPS][4];
+    bf16x8 kv[IDX_GROUPS][4];
+    auto load = [&](int p0) {
 #pragma unroll
         for (int u = 0; u < IDX_GROUPS; u++) {
             // Reads past the row's visible range are clamped onto its last
@@ -79,6 +82,11 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
 #pragma unroll
             for (int s = 0; s < 4; s++) kv[u][s] = load_bf16x8(kp + 32 * s);
         }
+    };
+
+    load(wr * IDX_BLOCK);
+    for (int b = wr; b * IDX_BLOCK < n; b += nw) {
+        const int p0 = b * IDX_BLOCK;
         float part[IDX_GROUPS];
 #pragma unroll
         for (int u = 0; u < IDX_GROUPS; u++) {
@@ -98,12 +106,13 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
             acc += __shfl_xor(acc, 32);
             part[u] = acc;
         }
+        if ((b + nw) * IDX_BLOCK < n) load((b + nw) * IDX_BLOCK);
         // Lane group g stores group u == g: 64 consecutive scores per store.
         float mine = part[0];
 #pragma unroll
         for (int u = 1; u < IDX_GROUPS; u++) mine = (g == u) ? part[u] : mine;
         const int pos = p0 + 16 * g + j;
-        if (pos < p_hi) srow[pos] = mine;
+        if (pos < n) srow[pos] = mine;
     }
 }
 
@@ -111,21 +120,22 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
 
 int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
 {
-    // Aim for >= 2048 workgroups (8 per CU) without going below 256
-    // positions (one 64-position iteration per wave).
-    int chunk = 4096;
-    while (chunk > 256 && (int64_t)num_rows * ((max_visible + chunk - 1) / chunk) < 2048) chunk /= 2;
-    return chunk;
+    // Workgroups per row: about 4096 in total, but never more waves than
+    // 64-position blocks in the longest row.
+    const int64_t blocks = (max_visible + IDX_BLOCK - 1) / IDX_BLOCK;
+    int64_t cx = (4096 + num_rows - 1) / num_rows;
+    const int64_t cap = (blocks + IDX_WAVES - 1) / IDX_WAVES;
+    if (cx > cap) cx = cap;
+    if (cx < 1) cx = 1;
+    return (int)cx;
 }
 
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis, const int64_t* base,
                            const uint16_t* q, const float* w, const uint16_t* kc, float scale, float* scores,
                            int64_t ld, hipStream_t stream)
 {
-    const int chunk = indexer_pick_chunk(num_rows, max_visible);
-    dim3 grid((max_visible + chunk - 1) / chunk, num_rows);
-    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld,
-                       chunk);
+    dim3 grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
+    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld);
 }
 
 }  // namespace dsa
