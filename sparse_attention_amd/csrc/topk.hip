@@ -7,10 +7,12 @@
 // rows shorter than 2,048 keep every position).  Order: larger score first,
 // -0.0 == +0.0, equal scores go to the lower position, NaN lowest.
 //
-// Design: a radix select on the order-preserving 32-bit key of each score,
-// split over workgroups so that a few very long rows (decode at 202,752
-// positions) still fill the chip.  Only integer counts are combined across
-// workgroups, so the result does not depend on scheduling.
+// Design: a radix select on the order-preserving 32-bit key of each score.
+// When every row has at most 65,536 positions, each row takes one 1024-thread
+// workgroup (one streaming pass over the row, the rest in LDS; see
+// topk_rows_kernel).  Longer rows are split over workgroups, because a single
+// CU streams too slowly for them; only integer counts are combined across
+// workgroups, so the result does not depend on scheduling:
 //   1. zero     per-row histogram and counters
 //   2. hist     rows x chunks: LDS histogram of the top 12 key bits, merged
 //               into the row histogram with integer atomics
@@ -386,10 +388,298 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(const int32_t* _
         }
 }
 
+// ---------------------------------------------------------------------------
+// One workgroup per row, for rows of at most TR_MAXN positions.
+//
+// Fast path (sampled bound):
+//   1. A strided sample of about 4096 scores gives a conservative lower bound
+//      theta_lo on the k-th largest key: the lower edge of the 12-bit key bin
+//      holding the sample's rho-th largest, rho about 1.5x the rank the k-th
+//      largest has in the sample plus a margin.
+//   2. One streaming pass appends every element with key >= theta_lo
+//      (key, position) to its wave's private segment of an LDS candidate list
+//      (a wave-uniform counter: no atomics).
+//   3. If at least k candidates were found and no segment overflowed, the k-th
+//      largest key lies among them, and a radix select over the candidates
+//      alone is exact.  Its bins are taken relative to the candidates' own key
+//      range (12 bits per round, at most three rounds), which spreads them
+//      over the histogram instead of piling onto a few hot bins.
+// Fallback (exact for any input, e.g. huge tie groups or a misleading
+// sample): an LDS histogram of the top 12 key bits of the whole row gives the
+// threshold bin b0; elements above b0 go straight to the result bitmap and
+// those inside b0 become the candidates (if they overflow, the radix rounds
+// rescan the row instead of the list).
+// Finally candidates above theta join a position bitmap, theta-valued ones go
+// to a tie bitmap, and an ordered pass over the bitmaps (one block scan for
+// ties, one for output offsets) keeps the first need_eq ties in position
+// order and writes the selected positions in ascending order.
+constexpr int TR_THREADS = 1024;
+constexpr int TR_WAVES = TR_THREADS / 64;
+constexpr int TR_SEG = 512;                    // candidate slots per wave
+constexpr int TR_CAP = TR_SEG * TR_WAVES;      // 8192
+constexpr int TR_BATCH = 8;  // 16-byte loads in flight per thread in row passes
+
+// Appends (key, t) to the calling wave's segment; `count` is the wave's
+// (uniform) fill level.  Must be called by every lane of the wave.
+__device__ __forceinline__ void append_candidate(bool want, uint32_t key, int t, uint32_t& count,
+                                                 unsigned long long* seg)
+{
+    const unsigned long long m = __ballot(want);
+    if (m == 0) return;
+    const int lane = threadIdx.x & 63;
+    if (want) {
+        const uint32_t slot = count + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        if (slot < (uint32_t)TR_SEG) seg[slot] = ((unsigned long long)key << 32) | (uint32_t)t;
+    }
+    count += (uint32_t)__popcll(m);
+}
+
+// Visits every candidate: wave segments are dense prefixes of length segn[w].
+template <class F>
+__device__ __forceinline__ void for_each_candidate(const unsigned long long* cand, const uint32_t* segn, F f)
+{
+    for (int i = threadIdx.x; i < TR_CAP; i += TR_THREADS) {
+        const int w = i / TR_SEG;
+        if ((uint32_t)(i - w * TR_SEG) < segn[w]) f(cand[i]);
+    }
+}
+
+__device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0; }
+
+__global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __restrict__ vis,
+                                                               const float* __restrict__ scores, int64_t ld,
+                                                               int k, int32_t* __restrict__ indices)
+{
+    const int r = blockIdx.x;
+    const int n = vis[r];
+    int32_t* out = indices + (int64_t)r * k;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    if (n <= k) {
+        for (int t = tid; t < k; t += TR_THREADS) out[t] = t < n ? t : -1;
+        return;
+    }
+    __shared__ uint32_t hist[TK_BINS];
+    __shared__ uint32_t gtbits[TR_MAXN / 32];
+    __shared__ uint32_t eqbits[TR_MAXN / 32];
+    __shared__ unsigned long long cand[TR_CAP];
+    __shared__ uint32_t segn[TR_WAVES];
+    __shared__ uint32_t sh[TR_THREADS / 64];
+    __shared__ uint32_t s_bin, s_above, s_max;
+
+    const int nwords = (n + 31) >> 5;
+    const float* row = scores + (int64_t)r * ld;
+    unsigned long long* seg = cand + wave * TR_SEG;
+    for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
+    for (int i = tid; i < nwords; i += TR_THREADS) {
+        gtbits[i] = 0u;
+        eqbits[i] = 0u;
+    }
+    if (tid == 0) s_max = 0u;
+    __syncthreads();
+
+    // ---- 1. sampled lower bound -------------------------------------------
+    const int stride = max(1, n >> 12);
+    const int msamp = (n + stride - 1) / stride;
+    const uint32_t rho = (uint32_t)min((int64_t)msamp, ((int64_t)3 * k * msamp) / (2 * (int64_t)n) + 32);
+#pragma unroll 4
+    for (int i = tid; i < msamp; i += TR_THREADS) atomicAdd(&hist[score_key(row[(int64_t)i * stride]) >> 20], 1u);
+    __syncthreads();
+    find_threshold_bin<TR_THREADS, TK_BINS>(hist, rho, &s_bin, &s_above, sh);
+    const uint32_t theta_lo = (rho >= (uint32_t)msamp) ? 0u : (s_bin << 20);
+
+    // ---- 2. filter pass ------------------------------------------------------
+    // TR_BATCH independent 16-byte loads per thread are issued before any is
+    // used, so each wave keeps several KB in flight.
+    uint32_t count = 0;  // wave-uniform
+    for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
+        float4 v[TR_BATCH];
+#pragma unroll
+        for (int u = 0; u < TR_BATCH; u++) {
+            const int b = bb + 4 * (tid + TR_THREADS * u);
+            // A 4-aligned group starting below n lies inside the row
+            // allocation because ld is a multiple of 4 and n <= ld.
+            v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < TR_BATCH; u++) {
+            const int b = bb + 4 * (tid + TR_THREADS * u);
+            const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t key = score_key(e[q]);
+                append_candidate(b + q < n && key >= theta_lo, key, b + q, count, seg);
+            }
+        }
+    }
+    if (lane == 0) segn[wave] = count;
+    __syncthreads();
+    uint32_t total = 0;
+    bool seg_over = false;
+#pragma unroll
+    for (int w = 0; w < TR_WAVES; w++) {
+        total += segn[w];
+        seg_over |= segn[w] > (uint32_t)TR_SEG;
+    }
+    const bool fast = total >= (uint32_t)k && !seg_over;
+
+    uint32_t need = (uint32_t)k;
+    uint32_t lo, hi;            // every key still in play lies in [lo, hi]
+    bool from_row = false;      // candidates overflowed: rescan the row
+    if (fast) {
+        lo = theta_lo;
+        uint32_t mx = 0;
+        for_each_candidate(cand, segn, [&](unsigned long long c) { mx = max(mx, (uint32_t)(c >> 32)); });
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
+        if (lane == 0) atomicMax(&s_max, mx);
+        __syncthreads();
+        hi = s_max;
+    } else {
+        // ---- fallback: whole-row histogram --------------------------------
+        for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
+        __syncthreads();
+        for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
+            float4 v[TR_BATCH];
+#pragma unroll
+            for (int u = 0; u < TR_BATCH; u++) {
+                const int b = bb + 4 * (tid + TR_THREADS * u);
+                v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < TR_BATCH; u++) {
+                const int b = bb + 4 * (tid + TR_THREADS * u);
+                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (b + q < n) atomicAdd(&hist[score_key(e[q]) >> 20], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold_bin<TR_THREADS, TK_BINS>(hist, need, &s_bin, &s_above, sh);
+        const uint32_t b0 = s_bin;
+        need -= s_above;
+        lo = b0 << 20;
+        hi = lo | 0xfffffu;
+        count = 0;
+        for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
+            float4 v[TR_BATCH];
+#pragma unroll
+            for (int u = 0; u < TR_BATCH; u++) {
+                const int b = bb + 4 * (tid + TR_THREADS * u);
+                v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < TR_BATCH; u++) {
+                const int b = bb + 4 * (tid + TR_THREADS * u);
+                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int t = b + q;
+                    const uint32_t key = score_key(e[q]);
+                    const uint32_t bin = key >> 20;
+                    if (t < n && bin > b0) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
+                    append_candidate(t < n && bin == b0, key, t, count, seg);
+                }
+            }
+        }
+        __syncthreads();  // every wave has read segn (above) before it changes
+        if (lane == 0) segn[wave] = count;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < TR_WAVES; w++) from_row |= segn[w] > (uint32_t)TR_SEG;
+    }
+
+    // ---- 3. radix rounds on [lo, hi], 12 bits at a time --------------------
+    // Each round histograms (key - lo) >> shift over the keys in [lo, hi]
+    // and narrows [lo, hi] to the bin holding the need-th largest.
+    while (true) {
+        const uint32_t span = hi - lo;
+        const int shift = max(0, bitlen(span) - 12);
+        for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
+        __syncthreads();
+        if (!from_row) {
+            for_each_candidate(cand, segn, [&](unsigned long long c) {
+                const uint32_t key = (uint32_t)(c >> 32);
+                if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+            });
+        } else {
+            for (int t = tid; t < n; t += TR_THREADS) {
+                const uint32_t key = score_key(row[t]);
+                if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold_bin<TR_THREADS, TK_BINS>(hist, need, &s_bin, &s_above, sh);
+        need -= s_above;
+        const uint32_t nlo = lo + (s_bin << shift);
+        const uint32_t nhi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
+        lo = nlo;
+        hi = nhi;
+        if (shift == 0) break;
+    }
+    const uint32_t theta = lo;
+    const uint32_t need_eq = need;
+
+    // Candidates above theta join the result; theta ties are marked.  (In the
+    // fallback, elements above the top-12-bit bin are already in gtbits and
+    // only elements of that bin are candidates.)
+    if (!from_row) {
+        for_each_candidate(cand, segn, [&](unsigned long long c) {
+            const uint32_t key = (uint32_t)(c >> 32);
+            const int t = (int)(uint32_t)c;
+            if (key > theta) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
+            else if (key == theta) atomicOr(&eqbits[t >> 5], 1u << (t & 31));
+        });
+    } else {
+        const uint32_t b0 = theta >> 20;
+        for (int t = tid; t < n; t += TR_THREADS) {
+            const uint32_t key = score_key(row[t]);
+            if ((key >> 20) != b0) continue;
+            if (key > theta) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
+            else if (key == theta) atomicOr(&eqbits[t >> 5], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+
+    // ---- ordered output.  Thread tid owns the contiguous words [w0, w1). ----
+    const int per = (nwords + TR_THREADS - 1) / TR_THREADS;
+    const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+    uint32_t my_eq = 0;
+    for (int w = w0; w < w1; w++) my_eq += __popc(eqbits[w]);
+    uint32_t tot;
+    uint32_t eq_before = block_exclusive_scan<TR_THREADS>(my_eq, &tot, sh);
+    uint32_t my_sel = 0;
+    for (int w = w0; w < w1; w++) {
+        uint32_t e = eqbits[w];
+        uint32_t keep = 0;
+        while (e && eq_before < need_eq) {
+            const uint32_t low = e & (0u - e);
+            keep |= low;
+            e ^= low;
+            eq_before++;
+        }
+        const uint32_t selw = gtbits[w] | keep;
+        gtbits[w] = selw;  // only this thread touches word w from here on
+        my_sel += __popc(selw);
+    }
+    uint32_t pos = block_exclusive_scan<TR_THREADS>(my_sel, &tot, sh);
+    for (int w = w0; w < w1; w++) {
+        uint32_t selw = gtbits[w];
+        while (selw) {
+            const int bit = __ffs(selw) - 1;
+            selw &= selw - 1u;
+            if (pos < (uint32_t)k) out[pos] = (w << 5) + bit;
+            pos++;
+        }
+    }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible)
 {
+    if (max_visible <= TR_ROW_PATH_MAXN) return 0;  // the one-workgroup-per-row path needs none
     const size_t R = (size_t)num_rows;
     const size_t CH = (size_t)((max_visible + TK_CHUNK - 1) / TK_CHUNK);
     size_t b = 0;
@@ -420,16 +710,19 @@ TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visib
 void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, const float* scores, int64_t ld,
                  int32_t k, int32_t* indices, const TopkWorkspace& tw, hipStream_t stream)
 {
+    if (max_visible <= TR_ROW_PATH_MAXN) {
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
+                           indices);
+        return;
+    }
     const int CH = tw.chunks;
     dim3 g2(CH, num_rows);
-    if (max_visible > k) {
-        hipLaunchKernelGGL(topk_zero_kernel, dim3(num_rows), dim3(256), 0, stream, tw.hist, tw.rowst);
-        hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist);
-        hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist,
-                           tw.rowst, tw.chunkst, CH, tw.cand);
-        hipLaunchKernelGGL(topk_resolve_kernel, dim3(num_rows), dim3(RS_THREADS), 0, stream, vis, scores, ld, k,
-                           tw.rowst, tw.chunkst, CH, tw.cand);
-    }
+    hipLaunchKernelGGL(topk_zero_kernel, dim3(num_rows), dim3(256), 0, stream, tw.hist, tw.rowst);
+    hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist);
+    hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist,
+                       tw.rowst, tw.chunkst, CH, tw.cand);
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3(num_rows), dim3(RS_THREADS), 0, stream, vis, scores, ld, k,
+                       tw.rowst, tw.chunkst, CH, tw.cand);
     hipLaunchKernelGGL(topk_write_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.rowst,
                        tw.chunkst, CH, indices);
 }

@@ -53,12 +53,17 @@ def test_workspace_sizes(lib):
     assert m.dsa_topk_workspace_size(0, 10, 2048) == 0
     assert m.dsa_sparse_mla_workspace_size(1, 0) == 0
     assert m.dsa_decode_step_workspace_size(1, 1, 2049) == 0
-    a = m.dsa_topk_workspace_size(16, 202752, 2048)
-    b = m.dsa_topk_workspace_size(32, 202752, 2048)
+    # rows up to 65,536 positions need no top-k workspace; longer rows do
+    assert m.dsa_topk_workspace_size(64, 32768, 2048) == 0
+    assert m.dsa_topk_workspace_size(16, 202752, 2048) > 0
+    a = m.dsa_topk_workspace_size(16, 300000, 2048)
+    b = m.dsa_topk_workspace_size(32, 300000, 2048)
     assert 0 < a < b and a % 256 == 0
     # decode-step workspace holds the fp32 scores of every row
     d = m.dsa_decode_step_workspace_size(64, 32768, 2048)
     assert d >= 64 * 32768 * 4 + m.dsa_topk_workspace_size(64, 32768, 2048)
+    d = m.dsa_decode_step_workspace_size(4, 300000, 2048)
+    assert d >= 4 * 300000 * 4 + m.dsa_topk_workspace_size(4, 300000, 2048)
     # many rows need no split partials
     assert m.dsa_sparse_mla_workspace_size(8192, 2048) == 0
     assert m.dsa_sparse_mla_workspace_size(16, 2048) > 0
@@ -89,15 +94,17 @@ def _call_topk(lib, rows, scores=0x1000, ld=100, k=2048, idx=0x3000, ws=0x100000
     (dict(k=2049), INVALID),
     (dict(idx=0), INVALID),
     (dict(idx=0x3002), MISALIGNED),
-    (dict(ws_bytes=16), WS_SMALL),
-    (dict(ws=0), INVALID),
-    (dict(ws=0x100010), MISALIGNED),
+    # rows longer than 65,536 positions need a workspace
+    (dict(ws_bytes=16, rows=_rows(maxv=300000), ld=300000), WS_SMALL),
+    (dict(ws=0, rows=_rows(maxv=300000), ld=300000), INVALID),
+    (dict(ws=0x100010, rows=_rows(maxv=300000), ld=300000), MISALIGNED),
+    (dict(ws=0, ws_bytes=0), NO_DEVICE),  # no workspace needed for short rows
     (dict(), NO_DEVICE),
 ])
 def test_topk_validation(lib, case, expect):
     case = dict(case)
     rows = case.pop("rows", _rows())
-    if expect == NO_DEVICE and HAS_GPU:
+    if expect == NO_DEVICE and HAS_GPU:  # noqa: SIM102
         pytest.skip("a GPU is present: a valid call would launch on fake pointers")
     status = _call_topk(lib, rows, **case)
     assert status == expect, lib.dsa_last_error_detail()

@@ -186,14 +186,30 @@ def test_topk_bitexact_synthetic(dsa, oracle_mod, kind, k):
 
 
 def test_topk_bitexact_long_rows_and_overflow(dsa, oracle_mod):
-    # 202,752-position rows: normal scores (candidate path) and 8-valued ties
-    # and all-equal rows (candidate list overflows; whole-row fallback).
-    lens = np.array([202752, 202752, 202752, 131072], np.int32)
-    s = np.concatenate([wl.random_scores(1, 1, 202752, kind="normal"), wl.random_scores(2, 1, 202752, kind="ties"),
-                        wl.random_scores(3, 1, 202752, kind="zeros"), wl.random_scores(4, 1, 202752, kind="coarse")])
-    got = run_topk(dsa, lens, s, 2048)
-    ref = oracle_mod.topk(lens, s, 2048)
-    assert np.array_equal(got, ref)
+    # 65,536-position rows (one workgroup per row): normal scores (sampled
+    # fast path), 8-valued ties and all-equal rows (candidate overflow, exact
+    # whole-row fallback), coarse values; and 202,752-position rows (multi-
+    # workgroup path).
+    for n in (65536, 202752):
+        lens = np.array([n, n, n, n - 1000], np.int32)
+        s = np.concatenate([wl.random_scores(1, 1, n, kind="normal"), wl.random_scores(2, 1, n, kind="ties"),
+                            wl.random_scores(3, 1, n, kind="zeros"), wl.random_scores(4, 1, n, kind="coarse")])
+        got = run_topk(dsa, lens, s, 2048)
+        ref = oracle_mod.topk(lens, s, 2048)
+        assert np.array_equal(got, ref), n
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros"])
+def test_topk_bitexact_rows_beyond_one_workgroup(dsa, oracle_mod, kind):
+    # Calls with rows longer than 65,536 positions take the multi-workgroup
+    # path (for every row of the call): normal scores, 8-valued ties,
+    # all-equal rows.
+    lens = np.array([300000, 65537, 5000, 2049, 1], np.int32)
+    s = wl.random_scores(zlib.crc32(kind.encode()) % 1000, len(lens), int(lens.max()), kind=kind)
+    for k in (2048, 5):
+        got = run_topk(dsa, lens, s, k)
+        ref = oracle_mod.topk(lens, s, k)
+        assert np.array_equal(got, ref), k
 
 
 @pytest.mark.parametrize("name, rows", [("c1", [0]), ("c4", [3, 9]), ("c2", [0, 2047, 2048, 2049, 5000, 8191])])
