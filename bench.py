@@ -154,7 +154,10 @@ def main():
     R, maxv = w.num_rows, w.max_visible
     q_idx, wts, k_idx = bf(x["q_idx"]), torch.from_numpy(x["w"]).to(dev), bf(x["k_idx"])
     q_abs, kv = bf(x["q_abs"]), bf(x["kv_latent"])
-    rows = dsa.Rows(torch.from_numpy(x["visible_len"]).to(dev), torch.from_numpy(x["row_cache_base"]).to(dev), maxv)
+    # Decode batches promise one query row per sequence (a performance hint).
+    distinct = len(np.unique(x["row_cache_base"])) == R
+    rows = dsa.Rows(torch.from_numpy(x["visible_len"]).to(dev), torch.from_numpy(x["row_cache_base"]).to(dev), maxv,
+                    flags=dsa.ROWS_DISTINCT_SEQUENCES if distinct else 0)
     idx = torch.empty((R, K_TOP), dtype=torch.int32, device=dev)
     out = torch.empty((R, 64, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((R, 64), dtype=torch.float32, device=dev)

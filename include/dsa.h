@@ -86,7 +86,15 @@ typedef struct {
     int32_t max_visible;           /* host: >= every visible_len[r]; <= DSA_MAX_VISIBLE */
     const int32_t* visible_len;    /* [R], each in [1, max_visible] */
     const int64_t* row_cache_base; /* [R], each >= 0 */
+    uint32_t flags;                /* host: DSA_ROWS_* hints (0 = none) */
 } dsa_rows_t;
+
+/* Hint: no two rows read the same sequence (e.g. a decode batch with one query
+ * per sequence).  The indexer then skips its shared-sequence pass (blocks of
+ * 32 consecutive rows on one sequence, as in a prefill chunk, are scored with
+ * query tiles on MFMA).  Hints never change results: with or without the
+ * flag, and whether or not it is true, every call computes the same values. */
+#define DSA_ROWS_DISTINCT_SEQUENCES 1u
 
 /* Library version string (static storage). */
 DSA_API const char* dsa_version(void);

@@ -20,6 +20,7 @@ __all__ = [
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn",
     "dsa_decode_step_workspace_size", "dsa_decode_step", "workspace",
     "INDEX_HEADS", "INDEX_DIM", "HEADS", "LATENT_DIM", "ROPE_DIM", "ROW_DIM", "TOPK_MAX",
+    "ROWS_DISTINCT_SEQUENCES",
 ]
 
 INDEX_HEADS = 32
@@ -52,6 +53,7 @@ class _CRows(ctypes.Structure):
         ("max_visible", ctypes.c_int32),
         ("visible_len", ctypes.c_void_p),
         ("row_cache_base", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -135,11 +137,15 @@ def _stream(stream, ref):
     return int(stream)
 
 
+ROWS_DISTINCT_SEQUENCES = 1
+
+
 class Rows:
     """Query-row description (dsa_rows_t): device visible_len [R] int32,
-    device row_cache_base [R] int64 and the host bound max_visible."""
+    device row_cache_base [R] int64, the host bound max_visible and the
+    DSA_ROWS_* hint flags (performance only; results never depend on them)."""
 
-    def __init__(self, visible_len, row_cache_base, max_visible):
+    def __init__(self, visible_len, row_cache_base, max_visible, flags=0):
         if visible_len.dtype != torch.int32 or row_cache_base.dtype != torch.int64:
             raise TypeError("visible_len must be int32 and row_cache_base int64")
         if visible_len.numel() != row_cache_base.numel():
@@ -148,8 +154,9 @@ class Rows:
         self.row_cache_base = row_cache_base
         self.num_rows = int(visible_len.numel())
         self.max_visible = int(max_visible)
+        self.flags = int(flags)
         self._c = _CRows(self.num_rows, self.max_visible, _ptr(visible_len, "visible_len", (torch.int32,)),
-                         _ptr(row_cache_base, "row_cache_base", (torch.int64,)))
+                         _ptr(row_cache_base, "row_cache_base", (torch.int64,)), self.flags)
 
     @property
     def c(self):

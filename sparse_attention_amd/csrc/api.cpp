@@ -43,6 +43,7 @@ dsa_status_t check_rows(const dsa_rows_t* rows)
     if (!rows->row_cache_base) return fail(DSA_ERR_INVALID_ARGUMENT, "rows->row_cache_base is NULL");
     if (!aligned(rows->visible_len, 4)) return fail(DSA_ERR_MISALIGNED, "visible_len not 4-byte aligned");
     if (!aligned(rows->row_cache_base, 8)) return fail(DSA_ERR_MISALIGNED, "row_cache_base not 8-byte aligned");
+    if (rows->flags & ~DSA_ROWS_DISTINCT_SEQUENCES) return fail(DSA_ERR_INVALID_ARGUMENT, "unknown rows->flags bits 0x%x", rows->flags);
     return DSA_OK;
 }
 
@@ -177,7 +178,8 @@ dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const
     DSA_TRY(check_device());
     hipStream_t st = (hipStream_t)hip_stream;
     dsa::launch_indexer_scores(rows->num_rows, rows->max_visible, rows->visible_len, rows->row_cache_base,
-                               (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, index_scale, scores, ld, st);
+                               (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, index_scale, scores, ld,
+                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, st);
     return after_launch(st, "indexer");
 }
 
@@ -276,7 +278,8 @@ dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const fl
     void* aws = p;
 
     dsa::launch_indexer_scores(R, rows->max_visible, rows->visible_len, rows->row_cache_base, (const uint16_t*)q_idx,
-                               w, (const uint16_t*)k_idx, index_scale, scores, ld, st);
+                               w, (const uint16_t*)k_idx, index_scale, scores, ld,
+                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, st);
     DSA_TRY(after_launch(st, "decode_step/indexer"));
     dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, R, rows->max_visible);
     dsa::launch_topk(R, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);

@@ -15,7 +15,7 @@ int indexer_pick_chunk(int32_t num_rows, int32_t max_visible);
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis,
                            const int64_t* base, const uint16_t* q, const float* w,
                            const uint16_t* kc, float scale, float* scores, int64_t ld,
-                           hipStream_t stream);
+                           bool distinct_sequences, hipStream_t stream);
 
 // ---- top-k ---------------------------------------------------------------
 constexpr int TK_CHUNK = 4096;     // scores one top-k workgroup owns

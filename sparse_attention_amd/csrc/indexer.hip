@@ -32,6 +32,134 @@ constexpr int IDX_WAVES = 4;
 constexpr int IDX_GROUPS = 4;               // 16-position groups per block
 constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 
+// ---------------------------------------------------------------------------
+// Prefill tile kernel.  Rows come in blocks of IDX_TILE_ROWS consecutive rows;
+// a block is "shared" when all its rows exist and read the same sequence
+// (equal cache base), as the rows of one prefill chunk do.  Shared blocks are
+// scored here, every other row by the row kernel; both kernels evaluate the
+// same test, so each row is scored exactly once.
+//
+// One 512-thread workgroup scores a shared block (32 rows x 32 heads = 1024
+// MFMA rows) against 32-position key tiles: each tile is loaded once into LDS
+// (256 B per position, rows padded to 272 B so the 16 rows an operand read
+// touches sit in distinct banks), and each wave multiplies its 4 rows' queries
+// (128 heads, kept in registers) by the tile: 64 MFMAs per 8 KB of keys.  The
+// causal triangle is skipped: a block only visits positions below its longest
+// row, and scores past a row's own length are not stored.  Workgroups of one
+// block take every CX-th tile, for load balance across blocks of different
+// lengths.
+constexpr int IDX_TILE_ROWS = 32;
+constexpr int IDX_TILE_POS = 32;
+constexpr int IDX_KEY_PITCH = 272;  // bytes per staged key row
+
+// Called by whole waves; the result is wave-uniform.
+__device__ __forceinline__ bool block_is_shared(const int64_t* __restrict__ base, int num_rows, int b)
+{
+    const int r0 = b * IDX_TILE_ROWS;
+    if (r0 + IDX_TILE_ROWS > num_rows) return false;
+    const int64_t mine = base[r0 + (threadIdx.x & (IDX_TILE_ROWS - 1))];
+    return __ballot(mine != base[r0]) == 0ull;
+}
+
+__global__ __launch_bounds__(512) void indexer_tile_kernel(
+    const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
+    const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
+    int64_t ld, int num_rows)
+{
+    const int blk = blockIdx.y;
+    if (!block_is_shared(base, num_rows, blk)) return;
+    const int r0 = blk * IDX_TILE_ROWS;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;  // 0..7: rows r0 + 4 wave .. + 3
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    __shared__ __attribute__((aligned(16))) uint8_t keys[2][IDX_TILE_POS * IDX_KEY_PITCH];
+    __shared__ int s_nmax;
+    if (threadIdx.x == 0) s_nmax = 0;
+    __syncthreads();
+    if (threadIdx.x < IDX_TILE_ROWS) atomicMax(&s_nmax, vis[r0 + threadIdx.x]);
+
+    // Queries and head weights of this wave's 4 rows.
+    bf16x8 qa[4][2][4];
+    float wv[4][8];
+    int nrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = r0 + 4 * wave + i;
+        nrow[i] = vis[r];
+        const uint16_t* qr = q + (int64_t)r * (32 * 128);
+#pragma unroll
+        for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+            for (int s = 0; s < 4; s++) qa[i][hb][s] = load_bf16x8(qr + (hb * 16 + j) * 128 + 32 * s + 8 * g);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            wv[i][v] = w[r * 32 + 4 * g + v];
+            wv[i][4 + v] = w[r * 32 + 16 + 4 * g + v];
+        }
+    }
+    __syncthreads();
+    const int nmax = s_nmax;
+    const int ntile = (nmax + IDX_TILE_POS - 1) / IDX_TILE_POS;
+    const uint16_t* kb = kc + base[r0] * 128;
+
+    // Staging roles: thread t moves 16 bytes (position t >> 4, chunk t & 15)
+    // of a 32-position tile.  Positions past nmax are clamped onto nmax - 1.
+    const int sp_pos = threadIdx.x >> 4, sp_chunk = threadIdx.x & 15;
+    auto load_tile = [&](int tt) -> u32x4 {
+        const int pos = min(tt * IDX_TILE_POS + sp_pos, nmax - 1);
+        return load_u32x4(kb + (int64_t)pos * 128 + sp_chunk * 8);
+    };
+    int tt = blockIdx.x;
+    u32x4 pre = {0u, 0u, 0u, 0u};
+    if (tt < ntile) pre = load_tile(tt);
+    int buf = 0;
+    for (; tt < ntile; tt += gridDim.x, buf ^= 1) {
+        *reinterpret_cast<u32x4*>(&keys[buf][sp_pos * IDX_KEY_PITCH + sp_chunk * 16]) = pre;
+        __syncthreads();  // tile visible; the other buffer is free again
+        if (tt + (int)gridDim.x < ntile) pre = load_tile(tt + gridDim.x);
+        const int p0 = tt * IDX_TILE_POS;
+#pragma unroll
+        for (int pg = 0; pg < 2; pg++) {
+            // B operand: position 16 pg + j, k-step s -> bytes 64 s + 16 g.
+            bf16x8 kv[4];
+            const uint8_t* kp = &keys[buf][(16 * pg + j) * IDX_KEY_PITCH + 16 * g];
+#pragma unroll
+            for (int s = 0; s < 4; s++) kv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 64 * s));
+            float part[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                floatx4 a0 = {0.f, 0.f, 0.f, 0.f};
+                floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    a0 = mfma_16x16x32(qa[i][0][s], kv[s], a0);
+                    a1 = mfma_16x16x32(qa[i][1][s], kv[s], a1);
+                }
+                float acc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc += wv[i][v] * fmaxf(a0[v] * scale, 0.f);
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc += wv[i][4 + v] * fmaxf(a1[v] * scale, 0.f);
+                acc += __shfl_xor(acc, 16);
+                acc += __shfl_xor(acc, 32);
+                part[i] = acc;
+            }
+            // Lane group g stores row 4 wave + g: 16 consecutive scores.
+            float mine = part[0];
+            int nmine = nrow[0];
+#pragma unroll
+            for (int i = 1; i < 4; i++) {
+                mine = (g == i) ? part[i] : mine;
+                nmine = (g == i) ? nrow[i] : nmine;
+            }
+            const int pos = p0 + 16 * pg + j;
+            if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
+        }
+    }
+}
+
 // Grid: (waves_per_row / 4, rows).  The waves of one row sweep it together:
 // wave wr of the row scores 64-position blocks wr, wr + NW, wr + 2 NW, ...
 // (NW = waves per row), so the waves in flight read one compact, advancing
@@ -41,7 +169,7 @@ constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
     const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
-    int64_t ld)
+    int64_t ld, int num_rows, int skip_shared)
 {
     const int r = blockIdx.y;
     const int n = vis[r];
@@ -50,6 +178,7 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int j = lane & 15;
     const int g = lane >> 4;
     const int nw = gridDim.x * IDX_WAVES;
+    if (skip_shared && block_is_shared(base, num_rows, r / IDX_TILE_ROWS)) return;  // the tile kernel owns it
     const int wr = blockIdx.x * IDX_WAVES + wave;
     if (wr * IDX_BLOCK >= n) return;
 
@@ -132,10 +261,23 @@ int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
 
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis, const int64_t* base,
                            const uint16_t* q, const float* w, const uint16_t* kc, float scale, float* scores,
-                           int64_t ld, hipStream_t stream)
+                           int64_t ld, bool distinct_sequences, hipStream_t stream)
 {
+    const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
+    if (nblk > 0) {
+        // Workgroups per shared block: enough for ~2 per CU overall, never
+        // more than the block's 32-position tiles.
+        const int tiles = (max_visible + IDX_TILE_POS - 1) / IDX_TILE_POS;
+        int cx = (512 + nblk - 1) / nblk;
+        if (cx > 8) cx = 8;
+        if (cx > tiles) cx = tiles;
+        if (cx < 1) cx = 1;
+        hipLaunchKernelGGL(indexer_tile_kernel, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc, scale,
+                           scores, ld, num_rows);
+    }
     dim3 grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
-    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld);
+    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld,
+                       num_rows, nblk > 0 ? 1 : 0);
 }
 
 }  // namespace dsa

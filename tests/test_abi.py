@@ -69,8 +69,8 @@ def test_workspace_sizes(lib):
     assert m.dsa_sparse_mla_workspace_size(16, 2048) > 0
 
 
-def _rows(R=4, maxv=100, vis=0x10000, base=0x20000):
-    return m._CRows(R, maxv, vis, base)
+def _rows(R=4, maxv=100, vis=0x10000, base=0x20000, flags=0):
+    return m._CRows(R, maxv, vis, base, flags)
 
 
 def _call_topk(lib, rows, scores=0x1000, ld=100, k=2048, idx=0x3000, ws=0x100000, ws_bytes=1 << 30):
@@ -86,6 +86,7 @@ def _call_topk(lib, rows, scores=0x1000, ld=100, k=2048, idx=0x3000, ws=0x100000
     (dict(rows=_rows(vis=0)), INVALID),
     (dict(rows=_rows(base=0)), INVALID),
     (dict(rows=_rows(base=0x20004)), MISALIGNED),
+    (dict(rows=_rows(flags=2)), INVALID),
     (dict(scores=0), INVALID),
     (dict(scores=0x1004), MISALIGNED),
     (dict(ld=99), INVALID),

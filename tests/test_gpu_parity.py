@@ -33,8 +33,8 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def make_rows(dsa, vis, base):
-    return dsa.Rows(dev(vis.astype(np.int32)), dev(base.astype(np.int64)), int(vis.max()))
+def make_rows(dsa, vis, base, flags=0):
+    return dsa.Rows(dev(vis.astype(np.int32)), dev(base.astype(np.int64)), int(vis.max()), flags=flags)
 
 
 def ld_for(maxv):
@@ -66,10 +66,10 @@ def device_inputs(x):
                 q_abs=dev_bf16(x["q_abs"]), kv_latent=dev_bf16(x["kv_latent"]))
 
 
-def run_indexer(dsa, x, d=None):
+def run_indexer(dsa, x, d=None, flags=0):
     d = d or device_inputs(x)
     vis, base = x["visible_len"], x["row_cache_base"]
-    rows = make_rows(dsa, vis, base)
+    rows = make_rows(dsa, vis, base, flags)
     ld = ld_for(int(vis.max()))
     scores = torch.empty((len(vis), ld), dtype=torch.float32, device=DEV)
     dsa.dsa_indexer_scores(rows, d["q_idx"], d["w"], d["k_idx"], 1.0, scores)
@@ -150,6 +150,41 @@ def test_indexer_c1_full(dsa, oracle_mod):
     assert score_rel_err(s[0], ref[0], 4096) <= SCORE_TOL
 
 
+def mixed_block_inputs():
+    # 70 rows: rows 0..31 (one shared sequence, causal), rows 32..63 (one
+    # block whose rows read two sequences: not shared), rows 64..69 (a
+    # partial block).
+    T1, T2 = 3000, 700
+    vis = np.concatenate([np.arange(T1 - 31, T1 + 1), np.full(16, T2), np.full(16, 2 * T2 // 3),
+                          [5, 77, 1024, 1025, 2049, 33]]).astype(np.int32)
+    base = np.concatenate([np.zeros(32), np.full(16, T1), np.full(16, T1 + T2), np.full(6, T1 + 2 * T2)]).astype(np.int64)
+    seq_len = np.array([T1, T2, T2, 2100], np.int64)
+    w = wl.Workload(name="mix", seed=9, visible_len=vis, row_cache_base=base, seq_len=seq_len,
+                    seq_base=np.concatenate([[0], np.cumsum(seq_len)[:-1]]).astype(np.int64),
+                    row_seq=np.zeros(len(vis), np.int64))
+    return w.generate()
+
+
+def test_indexer_shared_blocks_mixed_with_rows(dsa, oracle_mod):
+    # Every row must get its own scores exactly once.
+    x = mixed_block_inputs()
+    s = run_indexer(dsa, x)
+    ref = oracle_mod.indexer_scores(x["visible_len"], x["row_cache_base"], x["q_idx"], x["w"], x["k_idx"])
+    for r, n in enumerate(x["visible_len"]):
+        assert score_rel_err(s[r], ref[r], n) <= SCORE_TOL, r
+
+
+def test_indexer_distinct_sequences_hint_changes_nothing(dsa):
+    # The hint only skips the shared-block pass; set on rows that do share a
+    # sequence, it must still give the very same scores, bit for bit.
+    x = mixed_block_inputs()
+    d = device_inputs(x)
+    a = run_indexer(dsa, x, d)
+    b = run_indexer(dsa, x, d, flags=dsa.ROWS_DISTINCT_SEQUENCES)
+    for r, n in enumerate(x["visible_len"]):
+        assert np.array_equal(a[r, :n].view(np.uint32), b[r, :n].view(np.uint32)), r
+
+
 def test_indexer_ragged_edge_lengths(dsa, oracle_mod):
     lens = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 9000]
     w = wl._decode("edges", 11, lens, "edge lengths")
@@ -160,7 +195,8 @@ def test_indexer_ragged_edge_lengths(dsa, oracle_mod):
         assert score_rel_err(s[r], ref[r], n) <= SCORE_TOL, n
 
 
-@pytest.mark.parametrize("name, rows", [("c3", [0, 31, 63]), ("c4", [0, 15]), ("c2", [0, 1, 2047, 2048, 4095, 8191])])
+@pytest.mark.parametrize("name, rows", [("c3", [0, 31, 63]), ("c4", [0, 15]), ("c2", [0, 1, 31, 32, 2047, 2048, 4095, 8191]),
+                                        ("c5", [0, 57, 127, 128, 129, 159, 160, 8000, 16511])])
 def test_indexer_sampled_rows(dsa, oracle_mod, name, rows):
     w, x = inputs(name)
     s = run_indexer(dsa, x)
