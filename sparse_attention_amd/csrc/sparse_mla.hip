@@ -9,22 +9,27 @@
 // position, and the 64 MLA heads attend inside the selected set; the query is
 // in absorbed form so one 576-wide latent row serves every head).
 //
-// Design:
-//  - One workgroup = one row x one contiguous split of its index list; 4 waves,
-//    wave w owns heads 16w..16w+15 (the MFMA M dimension) for the whole split.
+// Design.  The kernel is bound by LDS instruction issue (four waves per CU,
+// one LDS instruction per ~4 clocks per CU at best), so the work is split to
+// read every staged byte as few times as possible:
+//  - One workgroup = one row x one contiguous split of its index list; 4 waves.
 //  - Per tile of 32 selected positions the workgroup gathers the 32 latent
-//    rows (1152 B each) into LDS with 16-byte loads, one wave-instruction
-//    covering 1 KB of one row.  The row pitch is padded to 1168 B so the MFMA
-//    operand reads do not collide in LDS banks.
-//  - QK: v_mfma_f32_16x16x32_bf16 with the wave's absorbed queries as the A
-//    operand (kept in registers, 72 VGPRs) and latent rows as B (one 16-byte
-//    LDS read per lane and k-step).
-//  - Online softmax in fp32 (base-2 exponent), head statistics reduced across
-//    the 16 lanes of a head with xor-shuffles.
-//  - PV: O[16 heads x 512] += P[16 x 32] . V[32 x 512].  P goes through a small
-//    per-wave LDS buffer (bf16, round-to-nearest-even) and both operands are
-//    read with ds_read_tr16_b64, which delivers the k = position direction
-//    from row-major tiles.  O lives in 128 accumulation registers.
+//    rows (1152 B each) into an LDS ring with direct global->LDS loads, one
+//    wave-instruction covering 1 KB; four tiles are in flight.
+//  - QK: wave w owns heads 16w..16w+15.  S^T[32 positions x 16 heads] on
+//    v_mfma_f32_16x16x32_bf16 with the latent rows as the A operand (one
+//    16-byte LDS read per lane and k-step) and the wave's absorbed queries as
+//    B (kept in registers).  The result leaves each lane with one head and
+//    eight positions, so the softmax statistics need only in-lane work plus
+//    two cross-row swaps.
+//  - Online softmax in fp32 (base-2 exponent) with a lazily moved reference
+//    maximum; P is rounded to bf16 (round-to-nearest-even) and written to LDS
+//    exactly in the layout of the PV A operand (16 bytes per lane).
+//  - PV: wave w owns latent columns 128w..128w+127 for all 64 heads:
+//    O[64 x 128] += P[64 x 32] . V[32 x 128], so each V element is read from
+//    LDS once per workgroup (transposing ds_read_b64_tr_b16 reads give the
+//    k = position direction), and P is read as four plain 16-byte reads.
+//  - Two barriers per tile: "tile landed / previous tile done" and "P ready".
 //  - Splits write unnormalized partials (O, running max, running sum); a
 //    combine kernel merges them in split order, so results do not depend on
 //    scheduling.  A single split normalizes in place.
@@ -38,7 +43,7 @@ namespace {
 constexpr int AT_TILE = 32;        // selected positions per tile
 constexpr int AT_CHUNKS = 72;      // 16-byte chunks per latent row
 constexpr int AT_TILE_BYTES = AT_TILE * AT_CHUNKS * 16;  // 36,864
-constexpr int AT_STAGES = 4;       // tiles in flight per workgroup
+constexpr int AT_STAGES = 4;       // ring slots
 constexpr int AT_MAX_SPLIT = 2048; // largest split (slots)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
@@ -46,27 +51,61 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // Tile layout: 32 rows x 72 16-byte chunks, dense (1152 B per row, the
 // direct global->LDS loads write 64 consecutive chunks per instruction).
-// Logical chunk c of row r sits at chunk c ^ swz(r), swz(r) = (r bit 2, r bit
-// 1, r bit 3) in bits (0, 1, 2).  With the row parity that the 1152-byte pitch
-// already spreads over the two 128-byte halves of a 256-byte bank window:
-//  - QK operand reads (rows 0..15, one logical chunk) hit 16 distinct 16-byte
-//    slots;
-//  - transposing PV reads (rows 8g+4h+{0..3}, two adjacent chunks, 8-byte
-//    halves) hit 16 distinct 8-byte slots;
-// and both read sets stay affine in the unrolled loop index, so the compiler
-// folds them into a few base registers plus immediate offsets.
-__device__ __forceinline__ int swz(int row)
-{
-    return ((row >> 2) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
-}
+// Logical chunk c of row r sits at chunk c ^ (r & 7).  With 1152 = 4.5 x 256
+// the row parity already alternates the 128-byte half of the bank window, and
+// the XOR spreads the rest, so that both operand read patterns are free of
+// bank conflicts: QK reads (rows m0..m0+15, one logical chunk, 16 bytes per
+// lane) and transposing PV reads (rows 4g+k and 16+4g+k of the four lane
+// groups g, two adjacent chunks, 8 bytes per lane).
 __device__ __forceinline__ int tile_chunk_offset(int row, int chunk)
 {
-    return row * (AT_CHUNKS * 16) + 16 * (chunk ^ swz(row));
+    return row * (AT_CHUNKS * 16) + 16 * (chunk ^ (row & 7));
 }
 
-// s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
-// expcnt [6:4] and lgkmcnt [11:8] left at their "no wait" maxima.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Ring synchronisation.  The gathers are direct global->LDS loads issued
+// through inline asm, so the compiler neither sees them as LDS writes (it
+// would otherwise drain every outstanding gather before each LDS read of the
+// ring) nor waits on them: the kernel does.  Each wave issues 9 loads per
+// tile, loads complete in order, and a tile is read only after
+// "vmcnt <= 9 x (tiles issued after it)" on every wave plus a barrier.  The
+// waits and barriers carry memory clobbers so no LDS access moves across them.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane direct load into LDS: lane L's bytes land at
+// lds_base + 16 L.  M0 carries the LDS base; nothing else in this file uses
+// M0, so clobbering it here is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Maximum / sum over the four lanes j, j+16, j+32, j+48 (VALU lane swaps).
+__device__ __forceinline__ float xrow_max(float v)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
                                                            const uint16_t* __restrict__ qa,
@@ -84,222 +123,260 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(const int64_t* __res
     const int wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int tc = lane & 3;         // transposed-read roles inside a 16-lane group
+    const int tc = lane & 3;  // transposed-read roles inside a 16-lane group
     const int tk = (lane >> 2) & 3;
-    const int h0 = wave * 16;
+    const int h0 = wave * 16;  // softmax heads of this wave
+    const int c0 = wave * 128; // output columns of this wave
 
     const int slot_begin = sp * split_len;
     const int slot_end = min(k, slot_begin + split_len);
     const int nslots = slot_end - slot_begin;
-    const int ntiles = (nslots + AT_TILE - 1) / AT_TILE;
 
-    // AT_STAGES tiles of 32 latent rows, filled by direct global->LDS loads.
     __shared__ __attribute__((aligned(1024))) uint8_t ring[AT_STAGES][AT_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint16_t plds[4][AT_TILE * 16];
-    __shared__ int32_t sidx[AT_MAX_SPLIT + AT_TILE];
+    __shared__ __attribute__((aligned(16))) u32x4 plds[4][64];  // P, [softmax wave][lane] (PV A operand)
+    __shared__ __attribute__((aligned(16))) float alpha_l[64];  // per-head rescale factor of this tile
+    __shared__ __attribute__((aligned(16))) int flag_l[4];      // wave w rescaled this tile
+    __shared__ __attribute__((aligned(16))) float lfin[64];
+    __shared__ __attribute__((aligned(16))) int32_t sidx[AT_MAX_SPLIT + AT_TILE];
+    __shared__ int s_last;
 
-    // The split's index list, padded with -1 to a whole number of tiles.
-    const int32_t* irow = idx + (int64_t)r * k + slot_begin;
-    for (int i = threadIdx.x; i < split_len + AT_TILE; i += 256) sidx[i] = i < nslots ? irow[i] : -1;
+    // The split's index list, padded with -1 to a whole number of tiles, and
+    // its last valid slot: tiles past it hold no position and are skipped.
+    if (threadIdx.x == 0) s_last = -1;
+    __syncthreads();
+    {
+        const int32_t* irow = idx + (int64_t)r * k + slot_begin;
+        int last = -1;
+        for (int i = threadIdx.x; i < split_len + AT_TILE; i += 256) {
+            const int32_t v = i < nslots ? irow[i] : -1;
+            sidx[i] = v;
+            if (v >= 0) last = i;
+        }
+        if (last >= 0) atomicMax(&s_last, last);
+    }
 
+    // B operands of QK: Q[r][h0 + j][32 s + 8 g .. +8].
     bf16x8 qreg[18];
     {
         const uint16_t* qrow = qa + ((int64_t)r * 64 + h0 + j) * 576 + 8 * g;
 #pragma unroll
         for (int s = 0; s < 18; s++) qreg[s] = load_bf16x8(qrow + 32 * s);
+        // Consume the loads here: the compiler then waits for them before the
+        // gathers start.  Left to itself it sinks these read-only loads past
+        // the barrier, and its waits for them (which count the gathers it
+        // cannot see) would drain the gather ring at every k-step.
+#pragma unroll
+        for (int s = 0; s < 18; s++) asm volatile("" ::"v"(qreg[s]));
     }
     const uint16_t* kvrow = kv + base[r] * 576;
-    __syncthreads();  // sidx visible; nothing asynchronous is in flight yet
+    __syncthreads();  // sidx and s_last visible; nothing asynchronous is in flight yet
+    const int ntiles = (s_last + AT_TILE) / AT_TILE;
 
-    // Gather roles.  Wave w fills tile chunks [576 w, 576 w + 576): its i-th
-    // load instruction writes 64 consecutive 16-byte LDS chunks (lane order),
-    // and lane L fetches whichever logical chunk belongs at LDS chunk
-    // 576 w + 64 i + L under the swizzle.  Padding slots fetch the sequence's
-    // first latent row (always present); their softmax weight is zero.
+    // Gather roles.  Wave w fills tile rows 8w..8w+7 (LDS chunks [576 w,
+    // 576 w + 576)): its i-th load instruction writes 64 consecutive 16-byte
+    // LDS chunks (lane order), and lane L fetches whichever logical chunk
+    // belongs at LDS chunk 576 w + 64 i + L under the swizzle.  Padding slots
+    // fetch the sequence's first latent row (always present); their softmax
+    // weight is zero.
     auto issue = [&](int t) {
-        uint8_t* dst = ring[t % AT_STAGES] + wave * 9 * 1024;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wave * 9 * 1024));
         const int t0 = t * AT_TILE;
+        int id[9];
+#pragma unroll
+        for (int i = 0; i < 9; i++) id[i] = sidx[t0 + ((wave * 9 + i) * 64 + lane) / AT_CHUNKS];
 #pragma unroll
         for (int i = 0; i < 9; i++) {
             const int p = (wave * 9 + i) * 64 + lane;
             const int row = p / AT_CHUNKS;
-            const int part = (p - row * AT_CHUNKS) ^ swz(row);
-            const int id = sidx[t0 + row];
-            const uint16_t* src = kvrow + (int64_t)(id < 0 ? 0 : id) * 576 + part * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+            const int part = (p - row * AT_CHUNKS) ^ (row & 7);
+            gather16_to_lds(kvrow + (int64_t)max(id[i], 0) * 576 + part * 8, dst + i * 1024);
         }
     };
 
-    float m_run[4], l_run[4];
+    // Softmax state of head h0 + j; l_run is this lane's partial sum over its
+    // positions (the four lanes of a head are summed at the end).
+    float m_run = -INFINITY, l_run = 0.f;
+    // O[16 mb + 4 g + v][c0 + 16 cb + j] = o[mb][cb][v].
+    floatx4 o[4][8];
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-        m_run[v] = -INFINITY;
-        l_run[v] = 0.f;
-    }
-    floatx4 o[32];
+    for (int mb = 0; mb < 4; mb++)
 #pragma unroll
-    for (int cb = 0; cb < 32; cb++) o[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int t = 0; t < AT_STAGES - 1; t++)
         if (t < ntiles) issue(t);
 
+    // Transposed-read bases (tile rows 4g + tk and 16 + 4g + tk, columns
+    // c0 + 16 cb + 4 tc .. +3 = logical chunk 16 w + 2 cb + (tc >> 1), byte
+    // 8 (tc & 1)); cb = 4 m + e -> immediate 128 m on top of base e.
+    const int vrlo = 4 * g + tk, vrhi = 16 + 4 * g + tk;
+    int vlo[4], vhi[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        vlo[e] = tile_chunk_offset(vrlo, 16 * wave + 2 * e + (tc >> 1)) + 8 * (tc & 1);
+        vhi[e] = tile_chunk_offset(vrhi, 16 * wave + 2 * e + (tc >> 1)) + 8 * (tc & 1);
+    }
+    // QK A-operand bases: rows j and 16 + j, logical chunk 4 s + g =
+    // 8 (s >> 1) + (4 (s & 1) + g) -> two bases per row plus immediate 128 (s >> 1).
+    const int qa00 = tile_chunk_offset(j, g), qa01 = tile_chunk_offset(j, 4 + g);
+    const int qa10 = tile_chunk_offset(16 + j, g), qa11 = tile_chunk_offset(16 + j, 4 + g);
+
     for (int t = 0; t < ntiles; t++) {
-        // Keep AT_STAGES - 1 tiles in flight; wait only for tile t's loads.
-        // Raw s_barrier (no fence) so outstanding loads of later tiles are not
-        // drained; the data dependence is carried by the explicit vmcnt wait.
-        if (t + AT_STAGES - 1 < ntiles) {
-            issue(t + AT_STAGES - 1);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(9 * (AT_STAGES - 1)));
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        }
-        __builtin_amdgcn_s_barrier();
+        // Tile t landed (later tiles may still be in flight) and every wave is
+        // done with tile t - 1, whose ring slot the next issue refills.
+        const int ahead = min(ntiles - 1 - t, AT_STAGES - 2);
+        if (ahead >= 2) wait_vm<18>();
+        else if (ahead == 1) wait_vm<9>();
+        else wait_vm<0>();
+        lds_barrier();
+        if (t + AT_STAGES - 1 < ntiles) issue(t + AT_STAGES - 1);
+
         const uint8_t* tl = ring[t % AT_STAGES];
         const int t0 = t * AT_TILE;
-        const bool ok0 = sidx[t0 + j] >= 0;
-        const bool ok1 = sidx[t0 + 16 + j] >= 0;
 
-        // QK: s0 -> positions 0..15 of the tile, s1 -> 16..31.  Logical chunk
-        // 4s + g = 8 (s >> 1) + (4 (s & 1) + g): two per-lane bases per row,
-        // the rest is an immediate 128 (s >> 1).
+        // QK: s0 -> tile positions 0..15, s1 -> 16..31 (rows of S^T); lane
+        // (j, g) ends with S[head h0 + j][position 16 mb + 4 g + v] in s_mb[v].
         floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         {
-            const uint8_t* q0e0 = tl + tile_chunk_offset(j, g);
-            const uint8_t* q0e1 = tl + tile_chunk_offset(j, 4 + g);
-            const uint8_t* q1e0 = tl + tile_chunk_offset(16 + j, g);
-            const uint8_t* q1e1 = tl + tile_chunk_offset(16 + j, 4 + g);
-            // Operand reads run QK_AHEAD steps ahead of the MFMAs that use
-            // them; scheduling barriers keep the compiler from collapsing the
-            // pipeline (LDS reads return in order, so the waits stay partial).
             constexpr int QK_AHEAD = 3;
-            bf16x8 b0[18], b1[18];
+            bf16x8 a0[18], a1[18];
             auto rd = [&](int st) {
                 const int off = 128 * (st >> 1);
-                b0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(((st & 1) ? q0e1 : q0e0) + off));
-                b1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(((st & 1) ? q1e1 : q1e0) + off));
+                a0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa01 : qa00) + off));
+                a1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa11 : qa10) + off));
             };
 #pragma unroll
             for (int st = 0; st < QK_AHEAD; st++) rd(st);
 #pragma unroll
             for (int st = 0; st < 18; st++) {
                 if (st + QK_AHEAD < 18) rd(st + QK_AHEAD);
-                s0 = mfma_16x16x32(qreg[st], b0[st], s0);
-                s1 = mfma_16x16x32(qreg[st], b1[st], s1);
+                s0 = mfma_16x16x32(a0[st], qreg[st], s0);
+                s1 = mfma_16x16x32(a1[st], qreg[st], s1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        // Online softmax.  Lane (j, g) holds heads h0 + 4g + v at positions j, 16 + j.
-        // The reference maximum m_run of a head moves only when the tile's
-        // maximum exceeds it by more than 2^RESCALE_LOG2; weights are then at
-        // most 2^RESCALE_LOG2, far from fp32 or bf16 overflow, and the result
-        // o / l and lse = m_run + log2 l do not depend on which reference is
-        // used.  In steady state no tile rescales the 128 O accumulators.
-        float p0[4], p1[4], z0[4], z1[4], mt[4];
-        bool need = false;
+        // Validity of the tile's 32 slots (bit p = slot t0 + p holds a position).
+        const uint32_t vbits = (uint32_t)__ballot(sidx[t0 + (lane & 31)] >= 0);
+        float z[8];
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            z0[v] = ok0 ? s0[v] * scale_log2 : -INFINITY;
-            z1[v] = ok1 ? s1[v] * scale_log2 : -INFINITY;
-            mt[v] = wave_max_16(fmaxf(z0[v], z1[v]));
-            need |= mt[v] > m_run[v] + RESCALE_LOG2;
+            z[v] = s0[v] * scale_log2;
+            z[4 + v] = s1[v] * scale_log2;
         }
-        if (__builtin_amdgcn_read_exec() & __ballot(need)) {  // wave-uniform
-            float alpha[4];
+        if (vbits != 0xffffffffu) {
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float m_new = fmaxf(m_run[v], mt[v]);
-                alpha[v] = (m_run[v] == -INFINITY) ? 0.f : exp2f(m_run[v] - m_new);
-                l_run[v] *= alpha[v];
-                m_run[v] = m_new;
+            for (int e = 0; e < 8; e++)
+                if (!((vbits >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) z[e] = -INFINITY;
+        }
+        float mt = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; e++) mt = fmaxf(mt, z[e]);
+        mt = xrow_max(mt);
+
+        // Lazy reference maximum: m_run moves only when the tile's maximum
+        // exceeds it by more than 2^RESCALE_LOG2, so weights stay below
+        // 2^RESCALE_LOG2 (far from fp32 or bf16 overflow) and the result
+        // o / l and lse = m_run + log2 l do not depend on the reference used.
+        // In steady state no tile rescales the output accumulators.
+        const bool need = mt > m_run + RESCALE_LOG2;
+        const bool any_need = __ballot(need) != 0ull;  // wave-uniform
+        if (any_need) {
+            const float m_new = need ? fmaxf(m_run, mt) : m_run;
+            const float alpha = need ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
+            l_run *= alpha;
+            m_run = m_new;
+            if (g == 0) alpha_l[h0 + j] = alpha;
+        }
+        if (lane == 0) flag_l[wave] = any_need ? 1 : 0;
+
+        // P = 2^(z - m_run) (zero for empty slots), rounded to bf16, stored as
+        // this lane's PV A operand: row = head h0 + j, k = positions
+        // {4g..4g+3, 16+4g..16+4g+3}.
+        {
+            const bool live = m_run != -INFINITY;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                p[e] = live ? __builtin_amdgcn_exp2f(z[e] - m_run) : 0.f;
+                l_run += p[e];
             }
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            u32x4 pk;
 #pragma unroll
-            for (int cb = 0; cb < 32; cb++)
-#pragma unroll
-                for (int v = 0; v < 4; v++) o[cb][v] *= alpha[v];
+            for (int e = 0; e < 4; e++) {
+                bf16x2 h = {(__bf16)p[2 * e], (__bf16)p[2 * e + 1]};
+                pk[e] = __builtin_bit_cast(uint32_t, h);
+            }
+            plds[wave][lane] = pk;
         }
+        lds_barrier();  // P, alpha and flags of every wave visible
+
+        // Rescale the O rows of heads whose reference maximum moved.
+        {
+            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l);
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const bool live = m_run[v] != -INFINITY;
-            p0[v] = (ok0 && live) ? exp2f(z0[v] - m_run[v]) : 0.f;
-            p1[v] = (ok1 && live) ? exp2f(z1[v] - m_run[v]) : 0.f;
-            l_run[v] += wave_sum_16(p0[v] + p1[v]);
+            for (int mb = 0; mb < 4; mb++) {
+                if (__builtin_amdgcn_readfirstlane(fl[mb])) {
+                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[16 * mb + 4 * g]);
+#pragma unroll
+                    for (int cb = 0; cb < 8; cb++)
+#pragma unroll
+                        for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
+                }
+            }
         }
 
-        // P (bf16) into the wave's buffer, row = tile position, column = head.
-        {
-            uint16_t* pw = plds[wave];
-            typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-            u16x4 a = {f32_to_bf16_rne(p0[0]), f32_to_bf16_rne(p0[1]), f32_to_bf16_rne(p0[2]),
-                       f32_to_bf16_rne(p0[3])};
-            u16x4 b = {f32_to_bf16_rne(p1[0]), f32_to_bf16_rne(p1[1]), f32_to_bf16_rne(p1[2]),
-                       f32_to_bf16_rne(p1[3])};
-            *reinterpret_cast<u16x4*>(&pw[j * 16 + 4 * g]) = a;
-            *reinterpret_cast<u16x4*>(&pw[(16 + j) * 16 + 4 * g]) = b;
-        }
-        // The P buffer is private to the wave and one wave's LDS operations
-        // complete in order, so only the compiler needs fencing here.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // A operand: lane (head j, group g) gets P at tile positions 8g .. 8g+7.
-        const bf16x8 pa = lds_read_tr_pair(&plds[wave][(8 * g + tk) * 16 + 4 * tc],
-                                           &plds[wave][(8 * g + 4 + tk) * 16 + 4 * tc]);
-        // PV over 32 column blocks of 16; B lane (column j, group g) gets V at
-        // the same positions 8g .. 8g+7: source lane (tc, tk) points at row
-        // 8g + tk (+4), columns 16 cb + 4 tc .. +3, i.e. logical chunk
-        // 2 cb + (tc >> 1), byte 8 (tc & 1) inside it.
-        // Column block cb = 4m + e covers logical chunks 8m + 2e + (tc >> 1):
-        // four per-lane bases per row, the rest is an immediate 128 m.
-        const int rlo = 8 * g + tk, rhi = 8 * g + 4 + tk;
-        const uint8_t* vlo[4];
-        const uint8_t* vhi[4];
+        // PV: A operands of the four head blocks, then V column blocks.
+        bf16x8 pa[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            vlo[e] = tl + tile_chunk_offset(rlo, 2 * e + (tc >> 1)) + 8 * (tc & 1);
-            vhi[e] = tl + tile_chunk_offset(rhi, 2 * e + (tc >> 1)) + 8 * (tc & 1);
-        }
-        constexpr int PV_AHEAD = 4;
-        bf16x8 vb[32];
+        for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[mb][lane]);
+        constexpr int PV_AHEAD = 2;
+        bf16x8 vb[8];
         auto rdv = [&](int cb) {
             const int off = 128 * (cb >> 2);
-            vb[cb] = lds_read_tr_pair((const uint16_t*)(vlo[cb & 3] + off), (const uint16_t*)(vhi[cb & 3] + off));
+            vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off), (const uint16_t*)(tl + vhi[cb & 3] + off));
         };
 #pragma unroll
         for (int cb = 0; cb < PV_AHEAD; cb++) rdv(cb);
 #pragma unroll
-        for (int cb = 0; cb < 32; cb++) {
-            if (cb + PV_AHEAD < 32) rdv(cb + PV_AHEAD);
-            o[cb] = mfma_16x16x32(pa, vb[cb], o[cb]);
+        for (int cb = 0; cb < 8; cb++) {
+            if (cb + PV_AHEAD < 8) rdv(cb + PV_AHEAD);
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Every wave is done with this ring slot before it is refilled.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(63) & ~(15 << 8));  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
     }
 
-    // Epilogue.  Lane (j, g) holds O[h0 + 4g + v][16 cb + j].
+    // Epilogue.  Head statistics: the four lanes of a head add their sums.
+    const float l_tot = xrow_sum(l_run);
+    if (g == 0) lfin[h0 + j] = l_tot;
     if (nsplit == 1) {
+        if (lse && g == 0)
+            lse[(int64_t)r * 64 + h0 + j] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
+    } else if (g == 0) {
+        part_ml[((int64_t)r * nsplit + sp) * 64 + h0 + j] = make_float2(m_run, l_tot);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) {
+        const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            const int h = h0 + 4 * g + v;
-            const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
-            float* orow = out + ((int64_t)r * 64 + h) * 512;
+            const int h = 16 * mb + 4 * g + v;
+            float* orow;
+            float scl;
+            if (nsplit == 1) {
+                orow = out + ((int64_t)r * 64 + h) * 512 + c0;
+                scl = lv[v] > 0.f ? 1.f / lv[v] : 0.f;
+            } else {
+                orow = part_o + (((int64_t)r * nsplit + sp) * 64 + h) * 512 + c0;
+                scl = 1.f;
+            }
 #pragma unroll
-            for (int cb = 0; cb < 32; cb++) orow[16 * cb + j] = o[cb][v] * inv;
-            if (lse && j == 0)
-                lse[(int64_t)r * 64 + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * LN2 : -INFINITY;
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int h = h0 + 4 * g + v;
-            float* prow = part_o + (((int64_t)r * nsplit + sp) * 64 + h) * 512;
-#pragma unroll
-            for (int cb = 0; cb < 32; cb++) prow[16 * cb + j] = o[cb][v];
-            if (j == 0) part_ml[((int64_t)r * nsplit + sp) * 64 + h] = make_float2(m_run[v], l_run[v]);
+            for (int cb = 0; cb < 8; cb++) orow[16 * cb + j] = o[mb][cb][v] * scl;
         }
     }
 }
