@@ -9,27 +9,29 @@
 // position, and the 64 MLA heads attend inside the selected set; the query is
 // in absorbed form so one 576-wide latent row serves every head).
 //
-// Design.  The kernel is bound by LDS instruction issue (four waves per CU,
-// one LDS instruction per ~4 clocks per CU at best), so the work is split to
-// read every staged byte as few times as possible:
-//  - One workgroup = one row x one contiguous split of its index list; 4 waves.
-//  - Per tile of 32 selected positions the workgroup gathers the 32 latent
-//    rows (1152 B each) into an LDS ring with direct global->LDS loads, one
-//    wave-instruction covering 1 KB; four tiles are in flight.
-//  - QK: wave w owns heads 16w..16w+15.  S^T[32 positions x 16 heads] on
-//    v_mfma_f32_16x16x32_bf16 with the latent rows as the A operand (one
-//    16-byte LDS read per lane and k-step) and the wave's absorbed queries as
-//    B (kept in registers).  The result leaves each lane with one head and
-//    eight positions, so the softmax statistics need only in-lane work plus
-//    two cross-row swaps.
-//  - Online softmax in fp32 (base-2 exponent) with a lazily moved reference
-//    maximum; P is rounded to bf16 (round-to-nearest-even) and written to LDS
-//    exactly in the layout of the PV A operand (16 bytes per lane).
-//  - PV: wave w owns latent columns 128w..128w+127 for all 64 heads:
-//    O[64 x 128] += P[64 x 32] . V[32 x 128], so each V element is read from
-//    LDS once per workgroup (transposing ds_read_b64_tr_b16 reads give the
-//    k = position direction), and P is read as four plain 16-byte reads.
-//  - Two barriers per tile: "tile landed / previous tile done" and "P ready".
+// Design.  Each phase of a tile saturates a different unit (the address
+// unit for the gathers, the matrix cores for QK and PV, the VALU and LDS
+// round trips for the softmax), so the workgroup is split into two kinds of
+// waves that work on consecutive tiles at the same time:
+//  - One workgroup = one row x one contiguous split of its index list;
+//    8 waves, one "score" wave and one "output" wave per SIMD.
+//  - Tiles of 32 selected positions: the 32 latent rows (1152 B each) are
+//    gathered into a 4-slot LDS ring with direct global->LDS loads.
+//  - Score waves (w = 0..3) own heads 16w..16w+15.  QK computes
+//    S^T[32 positions x 16 heads] on v_mfma_f32_16x16x32_bf16 with the latent
+//    rows as the A operand (16-byte LDS reads) and the absorbed queries as B
+//    (registers); each lane then holds one head and eight positions, so the
+//    online softmax (fp32, base-2 exponent, lazily moved reference maximum)
+//    needs in-lane work plus two cross-row swaps.  P is rounded to bf16
+//    (round-to-nearest-even) and stored in the exact layout of the PV A
+//    operand (16 bytes per lane).
+//  - Output waves (w = 4..7) own latent columns 128(w-4)..+127 for all 64
+//    heads: O[64 x 128] += P[64 x 32] . V[32 x 128] one tile behind the score
+//    waves, reading each V element once (transposing ds_read_b64_tr_b16) and P
+//    as four plain 16-byte reads.  They also issue the gathers.
+//  - One barrier per tile: score waves hand over P(t) while output waves
+//    finish PV(t-1); P, the rescale factors and the selected indices live in
+//    small double / quadruple buffers.
 //  - Splits write unnormalized partials (O, running max, running sum); a
 //    combine kernel merges them in split order, so results do not depend on
 //    scheduling.  A single split normalizes in place.
@@ -107,7 +109,7 @@ __device__ __forceinline__ float xrow_sum(float v)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__global__ __launch_bounds__(256, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
+__global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
                                                            const int32_t* __restrict__ idx, int k,
@@ -121,262 +123,270 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(const int64_t* __res
     const int nsplit = gridDim.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const bool scorer = wave < 4;  // wave-uniform role
+    const int wr = wave & 3;        // head block (score waves) / column block (output waves)
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int tc = lane & 3;  // transposed-read roles inside a 16-lane group
-    const int tk = (lane >> 2) & 3;
-    const int h0 = wave * 16;  // softmax heads of this wave
-    const int c0 = wave * 128; // output columns of this wave
 
     const int slot_begin = sp * split_len;
     const int slot_end = min(k, slot_begin + split_len);
     const int nslots = slot_end - slot_begin;
+    const int32_t* irow = idx + (int64_t)r * k + slot_begin;
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[AT_STAGES][AT_TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) u32x4 plds[4][64];  // P, [softmax wave][lane] (PV A operand)
-    __shared__ __attribute__((aligned(16))) float alpha_l[64];  // per-head rescale factor of this tile
-    __shared__ __attribute__((aligned(16))) int flag_l[4];      // wave w rescaled this tile
+    __shared__ __attribute__((aligned(16))) u32x4 plds[2][4][64];  // P of tile t: [t & 1][head block][lane]
+    __shared__ __attribute__((aligned(16))) float alpha_l[2][64];  // per-head rescale factor of tile t
+    __shared__ __attribute__((aligned(16))) int flag_l[2][4];      // head block rescaled in tile t
+    __shared__ __attribute__((aligned(16))) int32_t sid[AT_STAGES][AT_TILE];  // indices of tile t: [t % 4]
     __shared__ __attribute__((aligned(16))) float lfin[64];
-    __shared__ __attribute__((aligned(16))) int32_t sidx[AT_MAX_SPLIT + AT_TILE];
     __shared__ int s_last;
 
-    // The split's index list, padded with -1 to a whole number of tiles, and
-    // its last valid slot: tiles past it hold no position and are skipped.
+    // Last valid slot of the split: tiles past it hold no position and are skipped.
     if (threadIdx.x == 0) s_last = -1;
     __syncthreads();
     {
-        const int32_t* irow = idx + (int64_t)r * k + slot_begin;
         int last = -1;
-        for (int i = threadIdx.x; i < split_len + AT_TILE; i += 256) {
-            const int32_t v = i < nslots ? irow[i] : -1;
-            sidx[i] = v;
-            if (v >= 0) last = i;
-        }
+        for (int i = threadIdx.x; i < nslots; i += 512)
+            if (irow[i] >= 0) last = i;
         if (last >= 0) atomicMax(&s_last, last);
     }
-
-    // B operands of QK: Q[r][h0 + j][32 s + 8 g .. +8].
-    bf16x8 qreg[18];
-    {
-        const uint16_t* qrow = qa + ((int64_t)r * 64 + h0 + j) * 576 + 8 * g;
-#pragma unroll
-        for (int s = 0; s < 18; s++) qreg[s] = load_bf16x8(qrow + 32 * s);
-        // Consume the loads here: the compiler then waits for them before the
-        // gathers start.  Left to itself it sinks these read-only loads past
-        // the barrier, and its waits for them (which count the gathers it
-        // cannot see) would drain the gather ring at every k-step.
-#pragma unroll
-        for (int s = 0; s < 18; s++) asm volatile("" ::"v"(qreg[s]));
-    }
-    const uint16_t* kvrow = kv + base[r] * 576;
-    __syncthreads();  // sidx and s_last visible; nothing asynchronous is in flight yet
+    __syncthreads();
     const int ntiles = (s_last + AT_TILE) / AT_TILE;
-
-    // Gather roles.  Wave w fills tile rows 8w..8w+7 (LDS chunks [576 w,
-    // 576 w + 576)): its i-th load instruction writes 64 consecutive 16-byte
-    // LDS chunks (lane order), and lane L fetches whichever logical chunk
-    // belongs at LDS chunk 576 w + 64 i + L under the swizzle.  Padding slots
-    // fetch the sequence's first latent row (always present); their softmax
-    // weight is zero.
-    auto issue = [&](int t) {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wave * 9 * 1024));
-        const int t0 = t * AT_TILE;
-        int id[9];
-#pragma unroll
-        for (int i = 0; i < 9; i++) id[i] = sidx[t0 + ((wave * 9 + i) * 64 + lane) / AT_CHUNKS];
-#pragma unroll
-        for (int i = 0; i < 9; i++) {
-            const int p = (wave * 9 + i) * 64 + lane;
-            const int row = p / AT_CHUNKS;
-            const int part = (p - row * AT_CHUNKS) ^ (row & 7);
-            gather16_to_lds(kvrow + (int64_t)max(id[i], 0) * 576 + part * 8, dst + i * 1024);
-        }
+    // Indices of a tile (padding slots past the split read as -1).
+    auto tile_index = [&](int t, int p) -> int32_t {
+        const int i = t * AT_TILE + p;
+        return (t < ntiles && i < nslots) ? irow[i] : -1;
     };
+    if (threadIdx.x < (AT_STAGES - 1) * AT_TILE)
+        sid[threadIdx.x / AT_TILE][threadIdx.x % AT_TILE] = tile_index(threadIdx.x / AT_TILE, threadIdx.x % AT_TILE);
 
-    // Softmax state of head h0 + j; l_run is this lane's partial sum over its
-    // positions (the four lanes of a head are summed at the end).
-    float m_run = -INFINITY, l_run = 0.f;
-    // O[16 mb + 4 g + v][c0 + 16 cb + j] = o[mb][cb][v].
-    floatx4 o[4][8];
-#pragma unroll
-    for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int t = 0; t < AT_STAGES - 1; t++)
-        if (t < ntiles) issue(t);
-
-    // Transposed-read bases (tile rows 4g + tk and 16 + 4g + tk, columns
-    // c0 + 16 cb + 4 tc .. +3 = logical chunk 16 w + 2 cb + (tc >> 1), byte
-    // 8 (tc & 1)); cb = 4 m + e -> immediate 128 m on top of base e.
-    const int vrlo = 4 * g + tk, vrhi = 16 + 4 * g + tk;
-    int vlo[4], vhi[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        vlo[e] = tile_chunk_offset(vrlo, 16 * wave + 2 * e + (tc >> 1)) + 8 * (tc & 1);
-        vhi[e] = tile_chunk_offset(vrhi, 16 * wave + 2 * e + (tc >> 1)) + 8 * (tc & 1);
-    }
-    // QK A-operand bases: rows j and 16 + j, logical chunk 4 s + g =
-    // 8 (s >> 1) + (4 (s & 1) + g) -> two bases per row plus immediate 128 (s >> 1).
-    const int qa00 = tile_chunk_offset(j, g), qa01 = tile_chunk_offset(j, 4 + g);
-    const int qa10 = tile_chunk_offset(16 + j, g), qa11 = tile_chunk_offset(16 + j, 4 + g);
-
-    for (int t = 0; t < ntiles; t++) {
-        // Tile t landed (later tiles may still be in flight) and every wave is
-        // done with tile t - 1, whose ring slot the next issue refills.
-        const int ahead = min(ntiles - 1 - t, AT_STAGES - 2);
-        if (ahead >= 2) wait_vm<18>();
-        else if (ahead == 1) wait_vm<9>();
-        else wait_vm<0>();
-        lds_barrier();
-        if (t + AT_STAGES - 1 < ntiles) issue(t + AT_STAGES - 1);
-
-        const uint8_t* tl = ring[t % AT_STAGES];
-        const int t0 = t * AT_TILE;
-
-        // QK: s0 -> tile positions 0..15, s1 -> 16..31 (rows of S^T); lane
-        // (j, g) ends with S[head h0 + j][position 16 mb + 4 g + v] in s_mb[v].
-        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    if (scorer) {
+        // ------------------------------------------------------------ score waves
+        const int h0 = wr * 16;
+        // B operands of QK: Q[r][h0 + j][32 s + 8 g .. +8].
+        bf16x8 qreg[18];
         {
-            constexpr int QK_AHEAD = 3;
-            bf16x8 a0[18], a1[18];
-            auto rd = [&](int st) {
-                const int off = 128 * (st >> 1);
-                a0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa01 : qa00) + off));
-                a1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa11 : qa10) + off));
-            };
+            const uint16_t* qrow = qa + ((int64_t)r * 64 + h0 + j) * 576 + 8 * g;
 #pragma unroll
-            for (int st = 0; st < QK_AHEAD; st++) rd(st);
-#pragma unroll
-            for (int st = 0; st < 18; st++) {
-                if (st + QK_AHEAD < 18) rd(st + QK_AHEAD);
-                s0 = mfma_16x16x32(a0[st], qreg[st], s0);
-                s1 = mfma_16x16x32(a1[st], qreg[st], s1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int s = 0; s < 18; s++) qreg[s] = load_bf16x8(qrow + 32 * s);
         }
+        __syncthreads();  // indices of tiles 0..2 visible
+        lds_barrier();    // tile 0 landed (the output waves waited for it)
 
-        // Validity of the tile's 32 slots (bit p = slot t0 + p holds a position).
-        const uint32_t vbits = (uint32_t)__ballot(sidx[t0 + (lane & 31)] >= 0);
-        float z[8];
+        // QK A-operand bases: rows j and 16 + j, logical chunk 4 s + g =
+        // 8 (s >> 1) + (4 (s & 1) + g) -> two bases per row plus immediate 128 (s >> 1).
+        const int qa00 = tile_chunk_offset(j, g), qa01 = tile_chunk_offset(j, 4 + g);
+        const int qa10 = tile_chunk_offset(16 + j, g), qa11 = tile_chunk_offset(16 + j, 4 + g);
+        float m_run = -INFINITY, l_run = 0.f;  // head h0 + j; l_run: this lane's positions
+
+        for (int t = 0; t < ntiles; t++) {
+            // Indices of tile t + 3 (one score wave loads them; they are
+            // stored at the end of this step, into the slot of tile t - 1).
+            int32_t next_id = -1;
+            if (wr == 0) next_id = tile_index(t + AT_STAGES - 1, lane & 31);
+
+            const uint8_t* tl = ring[t % AT_STAGES];
+            // QK: s0 -> tile positions 0..15, s1 -> 16..31 (rows of S^T);
+            // lane (j, g) ends with S[head h0 + j][position 16 mb + 4 g + v] in s_mb[v].
+            floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            {
+                constexpr int QK_AHEAD = 3;
+                bf16x8 a0[18], a1[18];
+                auto rd = [&](int st) {
+                    const int off = 128 * (st >> 1);
+                    a0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa01 : qa00) + off));
+                    a1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tl + ((st & 1) ? qa11 : qa10) + off));
+                };
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            z[v] = s0[v] * scale_log2;
-            z[4 + v] = s1[v] * scale_log2;
-        }
-        if (vbits != 0xffffffffu) {
+                for (int st = 0; st < QK_AHEAD; st++) rd(st);
+#pragma unroll
+                for (int st = 0; st < 18; st++) {
+                    if (st + QK_AHEAD < 18) rd(st + QK_AHEAD);
+                    s0 = mfma_16x16x32(a0[st], qreg[st], s0);
+                    s1 = mfma_16x16x32(a1[st], qreg[st], s1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            // Validity of the tile's 32 slots (bit p: slot p holds a position).
+            const uint32_t vbits = (uint32_t)__ballot(sid[t % AT_STAGES][lane & 31] >= 0);
+            float z[8];
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                z[v] = s0[v] * scale_log2;
+                z[4 + v] = s1[v] * scale_log2;
+            }
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                if (!((vbits >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) z[e] = -INFINITY;
-        }
-        float mt = z[0];
-#pragma unroll
-        for (int e = 1; e < 8; e++) mt = fmaxf(mt, z[e]);
-        mt = xrow_max(mt);
+                z[e] = ((vbits >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u) ? z[e] : -INFINITY;
+            float mt = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+            mt = xrow_max(mt);
 
-        // Lazy reference maximum: m_run moves only when the tile's maximum
-        // exceeds it by more than 2^RESCALE_LOG2, so weights stay below
-        // 2^RESCALE_LOG2 (far from fp32 or bf16 overflow) and the result
-        // o / l and lse = m_run + log2 l do not depend on the reference used.
-        // In steady state no tile rescales the output accumulators.
-        const bool need = mt > m_run + RESCALE_LOG2;
-        const bool any_need = __ballot(need) != 0ull;  // wave-uniform
-        if (any_need) {
-            const float m_new = need ? fmaxf(m_run, mt) : m_run;
-            const float alpha = need ? ((m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
+            // Lazy reference maximum: m_run moves only when the tile's maximum
+            // exceeds it by more than 2^RESCALE_LOG2, so weights stay below
+            // 2^RESCALE_LOG2 (far from fp32 or bf16 overflow) and the result
+            // o / l and lse = m_run + log2 l do not depend on the reference
+            // used.  In steady state no tile rescales the output accumulators.
+            const bool need = mt > m_run + RESCALE_LOG2;
+            const float m_new = need ? mt : m_run;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
             l_run *= alpha;
             m_run = m_new;
-            if (g == 0) alpha_l[h0 + j] = alpha;
-        }
-        if (lane == 0) flag_l[wave] = any_need ? 1 : 0;
+            const float m_safe = (m_run == -INFINITY) ? 0.f : m_run;  // then every z is -inf
 
-        // P = 2^(z - m_run) (zero for empty slots), rounded to bf16, stored as
-        // this lane's PV A operand: row = head h0 + j, k = positions
-        // {4g..4g+3, 16+4g..16+4g+3}.
-        {
-            const bool live = m_run != -INFINITY;
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                p[e] = live ? __builtin_amdgcn_exp2f(z[e] - m_run) : 0.f;
-                l_run += p[e];
-            }
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            // P = 2^(z - m_run) (zero for empty slots), rounded to bf16, stored
+            // as this lane's PV A operand: row = head h0 + j, k = positions
+            // {4g..4g+3, 16+4g..16+4g+3}.
             u32x4 pk;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                bf16x2 h = {(__bf16)p[2 * e], (__bf16)p[2 * e + 1]};
+                const float p0 = __builtin_amdgcn_exp2f(z[2 * e] - m_safe);
+                const float p1 = __builtin_amdgcn_exp2f(z[2 * e + 1] - m_safe);
+                l_run += p0 + p1;
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 h = {(__bf16)p0, (__bf16)p1};
                 pk[e] = __builtin_bit_cast(uint32_t, h);
             }
-            plds[wave][lane] = pk;
+            plds[t & 1][wr][lane] = pk;
+            if (g == 0) alpha_l[t & 1][h0 + j] = alpha;
+            const bool any_need = __ballot(need) != 0ull;
+            if (lane == 0) flag_l[t & 1][wr] = any_need ? 1 : 0;
+            if (wr == 0 && lane < AT_TILE) sid[(t + AT_STAGES - 1) % AT_STAGES][lane] = next_id;
+            lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
         }
-        lds_barrier();  // P, alpha and flags of every wave visible
 
-        // Rescale the O rows of heads whose reference maximum moved.
-        {
-            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l);
+        // Row sums (the four lanes of a head), log-sum-exp, split statistics.
+        const float l_tot = xrow_sum(l_run);
+        if (g == 0) {
+            lfin[h0 + j] = l_tot;
+            if (nsplit == 1) {
+                if (lse) lse[(int64_t)r * 64 + h0 + j] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
+            } else {
+                part_ml[((int64_t)r * nsplit + sp) * 64 + h0 + j] = make_float2(m_run, l_tot);
+            }
+        }
+        __syncthreads();  // lfin visible to the output waves
+    } else {
+        // ----------------------------------------------------------- output waves
+        const int c0 = wr * 128;
+        const int tc = lane & 3;  // transposed-read roles inside a 16-lane group
+        const int tk = (lane >> 2) & 3;
+        const uint16_t* kvrow = kv + base[r] * 576;
+
+        // Gather roles.  Output wave b fills tile rows 8b..8b+7 (LDS chunks
+        // [576 b, 576 b + 576)): its i-th load instruction writes 64
+        // consecutive 16-byte LDS chunks (lane order), and lane L fetches
+        // whichever logical chunk belongs at LDS chunk 576 b + 64 i + L under
+        // the swizzle.  Padding slots fetch the sequence's first latent row
+        // (always present); their softmax weight is zero.
+        auto issue = [&](int t) {
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wr * 9 * 1024));
+            int id[9];
+#pragma unroll
+            for (int i = 0; i < 9; i++) id[i] = sid[t % AT_STAGES][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
+#pragma unroll
+            for (int i = 0; i < 9; i++) {
+                const int p = (wr * 9 + i) * 64 + lane;
+                const int row = p / AT_CHUNKS;
+                const int part = (p - row * AT_CHUNKS) ^ (row & 7);
+                gather16_to_lds(kvrow + (int64_t)max(id[i], 0) * 576 + part * 8, dst + i * 1024);
+            }
+        };
+
+        // Transposed-read bases (tile rows 4g + tk and 16 + 4g + tk, columns
+        // c0 + 16 cb + 4 tc .. +3 = logical chunk 16 b + 2 cb + (tc >> 1),
+        // byte 8 (tc & 1)); cb = 4 m + e -> immediate 128 m on top of base e.
+        const int vrlo = 4 * g + tk, vrhi = 16 + 4 * g + tk;
+        int vlo[4], vhi[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            vlo[e] = tile_chunk_offset(vrlo, 16 * wr + 2 * e + (tc >> 1)) + 8 * (tc & 1);
+            vhi[e] = tile_chunk_offset(vrhi, 16 * wr + 2 * e + (tc >> 1)) + 8 * (tc & 1);
+        }
+        // O[16 mb + 4 g + v][c0 + 16 cb + j] = o[mb][cb][v].
+        floatx4 o[4][8];
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+            for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+        // PV of tile t: rescale the O rows of head blocks whose reference
+        // moved, then O[64 x 128] += P[64 x 32] . V[32 x 128].
+        auto pv = [&](int t) {
+            const uint8_t* tl = ring[t % AT_STAGES];
+            bf16x8 pa[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[t & 1][mb][lane]);
+            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[t & 1]);
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
                 if (__builtin_amdgcn_readfirstlane(fl[mb])) {
-                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[16 * mb + 4 * g]);
+                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[t & 1][16 * mb + 4 * g]);
 #pragma unroll
                     for (int cb = 0; cb < 8; cb++)
 #pragma unroll
                         for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
                 }
             }
-        }
-
-        // PV: A operands of the four head blocks, then V column blocks.
-        bf16x8 pa[4];
+            constexpr int PV_AHEAD = 2;
+            bf16x8 vb[8];
+            auto rdv = [&](int cb) {
+                const int off = 128 * (cb >> 2);
+                vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off), (const uint16_t*)(tl + vhi[cb & 3] + off));
+            };
 #pragma unroll
-        for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[mb][lane]);
-        constexpr int PV_AHEAD = 2;
-        bf16x8 vb[8];
-        auto rdv = [&](int cb) {
-            const int off = 128 * (cb >> 2);
-            vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off), (const uint16_t*)(tl + vhi[cb & 3] + off));
-        };
+            for (int cb = 0; cb < PV_AHEAD; cb++) rdv(cb);
 #pragma unroll
-        for (int cb = 0; cb < PV_AHEAD; cb++) rdv(cb);
+            for (int cb = 0; cb < 8; cb++) {
+                if (cb + PV_AHEAD < 8) rdv(cb + PV_AHEAD);
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
-            if (cb + PV_AHEAD < 8) rdv(cb + PV_AHEAD);
-#pragma unroll
-            for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // Epilogue.  Head statistics: the four lanes of a head add their sums.
-    const float l_tot = xrow_sum(l_run);
-    if (g == 0) lfin[h0 + j] = l_tot;
-    if (nsplit == 1) {
-        if (lse && g == 0)
-            lse[(int64_t)r * 64 + h0 + j] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
-    } else if (g == 0) {
-        part_ml[((int64_t)r * nsplit + sp) * 64 + h0 + j] = make_float2(m_run, l_tot);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < 4; mb++) {
-        const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int h = 16 * mb + 4 * g + v;
-            float* orow;
-            float scl;
-            if (nsplit == 1) {
-                orow = out + ((int64_t)r * 64 + h) * 512 + c0;
-                scl = lv[v] > 0.f ? 1.f / lv[v] : 0.f;
-            } else {
-                orow = part_o + (((int64_t)r * nsplit + sp) * 64 + h) * 512 + c0;
-                scl = 1.f;
+                for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        };
+
+        __syncthreads();  // indices of tiles 0..2 visible
+        // Pipeline: at step t the score waves work on tile t and the output
+        // waves on tile t - 1; tiles t + 1 (landed) and t + 2 (in flight) fill
+        // the other two slots.  Loads in flight per output wave after the
+        // issue of step t: tiles t + 1, t + 2.
+        if (ntiles > 0) issue(0);
+        if (ntiles > 1) issue(1);
+        if (ntiles > 1) wait_vm<9>();
+        else wait_vm<0>();
+        lds_barrier();  // tile 0 landed
+        for (int t = 0; t < ntiles; t++) {
+            if (t + 2 < ntiles) issue(t + 2);  // slot of tile t - 2, finished at step t - 1
+            if (t > 0) pv(t - 1);
+            if (t + 1 < ntiles) {
+                if (t + 2 < ntiles) wait_vm<9>();
+                else wait_vm<0>();
+            }
+            lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
+        }
+        if (ntiles > 0) pv(ntiles - 1);
+        __syncthreads();  // lfin visible
+
+        // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j].
 #pragma unroll
-            for (int cb = 0; cb < 8; cb++) orow[16 * cb + j] = o[mb][cb][v] * scl;
+        for (int mb = 0; mb < 4; mb++) {
+            const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int h = 16 * mb + 4 * g + v;
+                float* orow;
+                float scl;
+                if (nsplit == 1) {
+                    orow = out + ((int64_t)r * 64 + h) * 512 + c0;
+                    scl = lv[v] > 0.f ? 1.f / lv[v] : 0.f;
+                } else {
+                    orow = part_o + (((int64_t)r * nsplit + sp) * 64 + h) * 512 + c0;
+                    scl = 1.f;
+                }
+#pragma unroll
+                for (int cb = 0; cb < 8; cb++) orow[16 * cb + j] = o[mb][cb][v] * scl;
+            }
         }
     }
 }
@@ -450,7 +460,7 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
         part_o = (float*)ws;
         part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
     }
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(256), 0, stream, base, qa, kv, idx, k,
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(512), 0, stream, base, qa, kv, idx, k,
                        softmax_scale * LOG2E, split_len, out, lse, part_o, part_ml);
     if (s > 1)
         hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(64, num_rows), dim3(128), 0, stream, part_o, part_ml, s,
