@@ -279,19 +279,26 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         // whichever logical chunk belongs at LDS chunk 576 b + 64 i + L under
         // the swizzle.  Padding slots fetch the sequence's first latent row
         // (always present); their softmax weight is zero.
-        auto issue = [&](int t) {
+        // The address unit takes ~30 clocks per such instruction, so the nine
+        // loads of a refill are spread over the PV MFMAs (gather_one) rather
+        // than issued back to back, which would stall this wave meanwhile.
+        int gid[9];
+        auto gather_ids = [&](int t) {
+#pragma unroll
+            for (int i = 0; i < 9; i++) gid[i] = sid[t % AT_STAGES][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
+        };
+        auto gather_one = [&](int t, int i) {
             const uint32_t dst = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wr * 9 * 1024));
-            int id[9];
+                (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wr * 9 * 1024 + i * 1024));
+            const int p = (wr * 9 + i) * 64 + lane;
+            const int row = p / AT_CHUNKS;
+            const int part = (p - row * AT_CHUNKS) ^ (row & 7);
+            gather16_to_lds(kvrow + (int64_t)max(gid[i], 0) * 576 + part * 8, dst);
+        };
+        auto issue = [&](int t) {
+            gather_ids(t);
 #pragma unroll
-            for (int i = 0; i < 9; i++) id[i] = sid[t % AT_STAGES][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
-#pragma unroll
-            for (int i = 0; i < 9; i++) {
-                const int p = (wr * 9 + i) * 64 + lane;
-                const int row = p / AT_CHUNKS;
-                const int part = (p - row * AT_CHUNKS) ^ (row & 7);
-                gather16_to_lds(kvrow + (int64_t)max(id[i], 0) * 576 + part * 8, dst + i * 1024);
-            }
+            for (int i = 0; i < 9; i++) gather_one(t, i);
         };
 
         // Transposed-read bases (tile rows 4g + tk and 16 + 4g + tk, columns
@@ -312,8 +319,9 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
             for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         // PV of tile t: rescale the O rows of head blocks whose reference
-        // moved, then O[64 x 128] += P[64 x 32] . V[32 x 128].
-        auto pv = [&](int t) {
+        // moved, then O[64 x 128] += P[64 x 32] . V[32 x 128].  With refill
+        // >= 0 the loads of tile `refill` go out between the MFMAs.
+        auto pv = [&](int t, int refill) {
             const uint8_t* tl = ring[t % AT_STAGES];
             bf16x8 pa[4];
 #pragma unroll
@@ -342,8 +350,10 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
                 if (cb + PV_AHEAD < 8) rdv(cb + PV_AHEAD);
 #pragma unroll
                 for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
+                if (refill >= 0) gather_one(refill, cb);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (refill >= 0) gather_one(refill, 8);
         };
 
         __syncthreads();  // indices of tiles 0..2 visible
@@ -357,15 +367,20 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         else wait_vm<0>();
         lds_barrier();  // tile 0 landed
         for (int t = 0; t < ntiles; t++) {
-            if (t + 2 < ntiles) issue(t + 2);  // slot of tile t - 2, finished at step t - 1
-            if (t > 0) pv(t - 1);
+            // Refill: tile t + 2 into the slot of tile t - 2 (finished at step t - 1).
+            const int refill = t + 2 < ntiles ? t + 2 : -1;  // wave-uniform
+            if (refill >= 0) gather_ids(refill);
+            if (t > 0) pv(t - 1, refill);
+            else if (refill >= 0)
+#pragma unroll
+                for (int i = 0; i < 9; i++) gather_one(refill, i);
             if (t + 1 < ntiles) {
                 if (t + 2 < ntiles) wait_vm<9>();
                 else wait_vm<0>();
             }
             lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
         }
-        if (ntiles > 0) pv(ntiles - 1);
+        if (ntiles > 0) pv(ntiles - 1, -1);
         __syncthreads();  // lfin visible
 
         // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j].

@@ -8,11 +8,11 @@
 // -0.0 == +0.0, equal scores go to the lower position, NaN lowest.
 //
 // Design: a radix select on the order-preserving 32-bit key of each score.
-// When every row has at most 65,536 positions, each row takes one 1024-thread
-// workgroup (one streaming pass over the row, the rest in LDS; see
-// topk_rows_kernel).  Longer rows are split over workgroups, because a single
-// CU streams too slowly for them; only integer counts are combined across
-// workgroups, so the result does not depend on scheduling:
+// Rows of at most 65,536 positions take one 1024-thread workgroup each (one
+// streaming pass over the row, the rest in LDS; see topk_rows_kernel).
+// Longer rows are split over workgroups, because a single CU streams too
+// slowly for them; only integer counts are combined across workgroups, so the
+// result does not depend on scheduling:
 //   1. zero     per-row histogram and counters
 //   2. hist     rows x chunks: LDS histogram of the top 12 key bits, merged
 //               into the row histogram with integer atomics
@@ -136,12 +136,12 @@ __device__ __forceinline__ void load_chunk_keys(const float* __restrict__ row, i
 
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const int32_t* __restrict__ vis,
                                                                const float* __restrict__ scores, int64_t ld, int k,
-                                                               uint32_t* __restrict__ hist)
+                                                               uint32_t* __restrict__ hist, int min_n)
 {
     const int r = blockIdx.y;
     const int n = vis[r];
     const int start = blockIdx.x * TK_CHUNK;
-    if (n <= k || start >= n) return;
+    if (n <= k || n <= min_n || start >= n) return;
     const int end = min(n, start + TK_CHUNK);
     __shared__ uint32_t h[TK_BINS];
     for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0u;
@@ -162,13 +162,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(const int32_t* 
                                                                  const uint32_t* __restrict__ hist,
                                                                  uint32_t* __restrict__ rowst,
                                                                  uint32_t* __restrict__ chunkst, int chunks,
-                                                                 unsigned long long* __restrict__ cand)
+                                                                 unsigned long long* __restrict__ cand, int min_n)
 {
     const int r = blockIdx.y;
     const int c = blockIdx.x;
     const int n = vis[r];
     const int start = c * TK_CHUNK;
-    if (n <= k || start >= n) return;
+    if (n <= k || n <= min_n || start >= n) return;
     const int end = min(n, start + TK_CHUNK);
     __shared__ uint32_t h[TK_BINS];
     __shared__ uint32_t sh[TK_THREADS / 64];
@@ -218,11 +218,11 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
                                                                   const float* __restrict__ scores, int64_t ld,
                                                                   int k, uint32_t* __restrict__ rowst,
                                                                   uint32_t* __restrict__ chunkst, int chunks,
-                                                                  const unsigned long long* __restrict__ cand)
+                                                                  const unsigned long long* __restrict__ cand, int min_n)
 {
     const int r = blockIdx.x;
     const int n = vis[r];
-    if (n <= k) return;
+    if (n <= k || n <= min_n) return;
     __shared__ unsigned long long cl[TK_CAP];
     __shared__ uint32_t h[TK_BINS];
     __shared__ uint32_t cgt[TK_MAX_CHUNKS / 2];  // per-chunk counts, see note below
@@ -335,11 +335,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(const int32_t* _
                                                                 const float* __restrict__ scores, int64_t ld, int k,
                                                                 const uint32_t* __restrict__ rowst,
                                                                 const uint32_t* __restrict__ chunkst, int chunks,
-                                                                int32_t* __restrict__ indices)
+                                                                int32_t* __restrict__ indices, int min_n)
 {
     const int r = blockIdx.y;
     const int c = blockIdx.x;
     const int n = vis[r];
+    if (n <= min_n) return;  // the one-workgroup-per-row kernel owns this row
     const int start = c * TK_CHUNK;
     int32_t* out = indices + (int64_t)r * k;
     if (n <= k) {
@@ -448,10 +449,11 @@ __device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0
 
 __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __restrict__ vis,
                                                                const float* __restrict__ scores, int64_t ld,
-                                                               int k, int32_t* __restrict__ indices)
+                                                               int k, int32_t* __restrict__ indices, int max_n)
 {
     const int r = blockIdx.x;
     const int n = vis[r];
+    if (n > max_n) return;  // the multi-workgroup kernels own this row
     int32_t* out = indices + (int64_t)r * k;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -710,21 +712,23 @@ TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visib
 void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, const float* scores, int64_t ld,
                  int32_t k, int32_t* indices, const TopkWorkspace& tw, hipStream_t stream)
 {
-    if (max_visible <= TR_ROW_PATH_MAXN) {
-        hipLaunchKernelGGL(topk_rows_kernel, dim3(num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
-                           indices);
-        return;
-    }
+    // Rows of up to TR_ROW_PATH_MAXN positions take one workgroup each; longer
+    // rows (present only when max_visible exceeds it) are split over
+    // workgroups.  Each kernel skips the rows the other path owns.
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
+                       indices, (int)TR_ROW_PATH_MAXN);
+    if (max_visible <= TR_ROW_PATH_MAXN) return;
     const int CH = tw.chunks;
+    const int min_n = TR_ROW_PATH_MAXN;
     dim3 g2(CH, num_rows);
     hipLaunchKernelGGL(topk_zero_kernel, dim3(num_rows), dim3(256), 0, stream, tw.hist, tw.rowst);
-    hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist);
+    hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist, min_n);
     hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist,
-                       tw.rowst, tw.chunkst, CH, tw.cand);
+                       tw.rowst, tw.chunkst, CH, tw.cand, min_n);
     hipLaunchKernelGGL(topk_resolve_kernel, dim3(num_rows), dim3(RS_THREADS), 0, stream, vis, scores, ld, k,
-                       tw.rowst, tw.chunkst, CH, tw.cand);
+                       tw.rowst, tw.chunkst, CH, tw.cand, min_n);
     hipLaunchKernelGGL(topk_write_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.rowst,
-                       tw.chunkst, CH, indices);
+                       tw.chunkst, CH, indices, min_n);
 }
 
 }  // namespace dsa

@@ -235,6 +235,18 @@ def test_topk_bitexact_long_rows_and_overflow(dsa, oracle_mod):
         assert np.array_equal(got, ref), n
 
 
+def test_topk_bitexact_mixed_paths_in_one_call(dsa, oracle_mod):
+    # One call whose rows straddle the per-row dispatch: rows of at most
+    # 65,536 positions (one workgroup each, including rows with n <= k) and
+    # longer rows (split over workgroups) must each be owned by exactly one path.
+    lens = np.array([100, 5000, 65536, 65537, 131072, 2048, 70001, 2049], np.int32)
+    kinds = ["normal", "ties", "normal", "ties", "normal", "coarse", "zeros", "normal"]
+    s = np.concatenate([wl.random_scores(20 + i, 1, int(lens.max()), kind=kd) for i, kd in enumerate(kinds)])
+    got = run_topk(dsa, lens, s, 2048)
+    ref = oracle_mod.topk(lens, s, 2048)
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("kind", ["normal", "ties", "zeros"])
 def test_topk_bitexact_rows_beyond_one_workgroup(dsa, oracle_mod, kind):
     # Calls with rows longer than 65,536 positions take the multi-workgroup
