@@ -407,29 +407,44 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
 }
 
 // Merges split partials in split order: one workgroup per (head, row), each
-// thread four latent columns.
+// thread four latent columns.  Every split's loads are issued before any is
+// used (one memory round trip per thread); the arithmetic still runs in
+// split order, so results do not depend on scheduling.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __restrict__ part_o,
                                                                 const float2* __restrict__ part_ml, int nsplit,
                                                                 float* __restrict__ out, float* __restrict__ lse)
 {
+    constexpr int MAXS = 16;  // attn_pick_splits never returns more
     const int h = blockIdx.x;
     const int r = blockIdx.y;
     const float2* ml = part_ml + (int64_t)r * nsplit * 64 + h;
+    const float* po = part_o + ((int64_t)r * nsplit * 64 + h) * 512 + 4 * threadIdx.x;
+    float2 e[MAXS];
+    float4 p[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; s++) {
+        if (s < nsplit) {
+            e[s] = ml[(int64_t)s * 64];
+            p[s] = *reinterpret_cast<const float4*>(po + (int64_t)s * 64 * 512);
+        }
+    }
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; s++) M = fmaxf(M, ml[(int64_t)s * 64].x);
+#pragma unroll
+    for (int s = 0; s < MAXS; s++)
+        if (s < nsplit) M = fmaxf(M, e[s].x);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < nsplit; s++) {
-            const float2 e = ml[(int64_t)s * 64];
-            const float f = exp2f(e.x - M);
-            L += e.y * f;
-            const float4 p = *reinterpret_cast<const float4*>(
-                part_o + (((int64_t)r * nsplit + s) * 64 + h) * 512 + 4 * threadIdx.x);
-            acc.x += p.x * f;
-            acc.y += p.y * f;
-            acc.z += p.z * f;
-            acc.w += p.w * f;
+#pragma unroll
+        for (int s = 0; s < MAXS; s++) {
+            if (s < nsplit) {
+                const float f = exp2f(e[s].x - M);
+                L += e[s].y * f;
+                acc.x += p[s].x * f;
+                acc.y += p[s].y * f;
+                acc.z += p[s].z * f;
+                acc.w += p[s].w * f;
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
