@@ -87,6 +87,21 @@ constexpr int DPP_QUAD_2301 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
 
+// Inclusive prefix sum over the 64 lanes of a wave on the VALU (DPP): a
+// Hillis-Steele scan inside each 16-lane row (shifts 1, 2, 4, 8; lanes
+// without a source add 0), then each row adds the totals of the rows before
+// it (broadcast of lane 15 into rows 1 and 3, of lane 31 into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 __device__ __forceinline__ float wave_max_16(float v)
 {
     v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));

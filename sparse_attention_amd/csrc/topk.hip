@@ -49,12 +49,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* sh /*[NT/64]*/)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) sh[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
