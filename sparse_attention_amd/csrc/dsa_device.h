@@ -87,6 +87,24 @@ constexpr int DPP_QUAD_2301 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
 
+// Maximum / sum over the four lanes j, j+16, j+32, j+48 of a wave (gfx950
+// VALU lane swaps: lanes l and l ^ 32, then l and l ^ 16; every lane ends
+// with the same value).
+__device__ __forceinline__ float xrow_max(float v)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave on the VALU (DPP): a
 // Hillis-Steele scan inside each 16-lane row (shifts 1, 2, 4, 8; lanes
 // without a source add 0), then each row adds the totals of the rows before

@@ -18,7 +18,7 @@
 //    the same k order and stays in registers for the whole chunk.
 //  - The output layout puts 4 heads of one position in each lane, so the
 //    ReLU and head weighting stay in registers and the head sum needs only two
-//    cross-lane steps (lanes j, j+16, j+32, j+48).  Every lane ends with the
+//    cross-lane swaps on the VALU (lanes j, j+16, j+32, j+48).  Every lane ends with the
 //    full score, so each lane group stores a different 16-position group and
 //    one store covers 64 consecutive scores.
 #include "dsa_device.h"
@@ -142,9 +142,7 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
                 for (int v = 0; v < 4; v++) acc += wv[i][v] * fmaxf(a0[v] * scale, 0.f);
 #pragma unroll
                 for (int v = 0; v < 4; v++) acc += wv[i][4 + v] * fmaxf(a1[v] * scale, 0.f);
-                acc += __shfl_xor(acc, 16);
-                acc += __shfl_xor(acc, 32);
-                part[i] = acc;
+                part[i] = xrow_sum(acc);
             }
             // Lane group g stores row 4 wave + g: 16 consecutive scores.
             float mine = part[0];
@@ -231,9 +229,7 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
             for (int v = 0; v < 4; v++) acc += w0[v] * fmaxf(a0[v] * scale, 0.f);
 #pragma unroll
             for (int v = 0; v < 4; v++) acc += w1[v] * fmaxf(a1[v] * scale, 0.f);
-            acc += __shfl_xor(acc, 16);
-            acc += __shfl_xor(acc, 32);
-            part[u] = acc;
+            part[u] = xrow_sum(acc);
         }
         if ((b + nw) * IDX_BLOCK < n) load((b + nw) * IDX_BLOCK);
         // Lane group g stores group u == g: 64 consecutive scores per store.

@@ -93,22 +93,6 @@ __device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_ba
 }
 #pragma clang diagnostic pop
 
-// Maximum / sum over the four lanes j, j+16, j+32, j+48 (VALU lane swaps).
-__device__ __forceinline__ float xrow_max(float v)
-{
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float xrow_sum(float v)
-{
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
