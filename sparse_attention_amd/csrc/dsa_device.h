@@ -105,6 +105,27 @@ __device__ __forceinline__ float xrow_sum(float v)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Reduce-scatter over the four 16-lane groups of a wave: lane group g
+// returns x[g] summed over the four lanes j, j+16, j+32, j+48 (its own and
+// the three other groups' values of entry g).  Three lane swaps: entries
+// {0,1} / {2,3} meet across the wave halves, then across the rows.
+__device__ __forceinline__ float xrow_reduce_scatter4(const float (&x)[4])
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]), false, false);
+    const float r02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // groups 0,1: entry 0; 2,3: entry 2
+    const float r13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // groups 0,1: entry 1; 2,3: entry 3
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(r02), __float_as_uint(r13), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// max(x, 0) on the bit pattern: one integer op, and no NaN quieting of the
+// input is needed (a negative float is a negative integer).
+__device__ __forceinline__ float relu_bits(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave on the VALU (DPP): a
 // Hillis-Steele scan inside each 16-lane row (shifts 1, 2, 4, 8; lanes
 // without a source add 0), then each row adds the totals of the rows before

@@ -17,10 +17,10 @@
 //    so the four lanes of a position read 64 contiguous bytes per load; Q uses
 //    the same k order and stays in registers for the whole chunk.
 //  - The output layout puts 4 heads of one position in each lane, so the
-//    ReLU and head weighting stay in registers and the head sum needs only two
-//    cross-lane swaps on the VALU (lanes j, j+16, j+32, j+48).  Every lane ends with the
-//    full score, so each lane group stores a different 16-position group and
-//    one store covers 64 consecutive scores.
+//    ReLU and head weighting stay in registers; a reduce-scatter over the
+//    lanes j, j+16, j+32, j+48 (three VALU lane swaps for four position
+//    groups) leaves each lane group the full score of a different 16-position
+//    group, so one store covers 64 consecutive scores.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     __syncthreads();
     if (threadIdx.x < IDX_TILE_ROWS) atomicMax(&s_nmax, vis[r0 + threadIdx.x]);
 
-    // Queries and head weights of this wave's 4 rows.
+    // Queries and head weights of this wave's 4 rows (the positive index
+    // scale is folded into the weights: ReLU(s x) = s ReLU(x) for s > 0).
     bf16x8 qa[4][2][4];
     float wv[4][8];
     int nrow[4];
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
             for (int s = 0; s < 4; s++) qa[i][hb][s] = load_bf16x8(qr + (hb * 16 + j) * 128 + 32 * s + 8 * g);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-            wv[i][v] = w[r * 32 + 4 * g + v];
-            wv[i][4 + v] = w[r * 32 + 16 + 4 * g + v];
+            wv[i][v] = w[r * 32 + 4 * g + v] * scale;
+            wv[i][4 + v] = w[r * 32 + 16 + 4 * g + v] * scale;
         }
     }
     __syncthreads();
@@ -120,38 +121,64 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
         __syncthreads();  // tile visible; the other buffer is free again
         if (tt + (int)gridDim.x < ntile) pre = load_tile(tt + gridDim.x);
         const int p0 = tt * IDX_TILE_POS;
+        // B operands: position 16 pg + j, k-step s -> bytes 64 s + 16 g.
+        bf16x8 kv[2][4];
 #pragma unroll
         for (int pg = 0; pg < 2; pg++) {
-            // B operand: position 16 pg + j, k-step s -> bytes 64 s + 16 g.
-            bf16x8 kv[4];
             const uint8_t* kp = &keys[buf][(16 * pg + j) * IDX_KEY_PITCH + 16 * g];
 #pragma unroll
-            for (int s = 0; s < 4; s++) kv[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 64 * s));
-            float part[4];
+            for (int s = 0; s < 4; s++) kv[pg][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 64 * s));
+        }
+        // Eight units (position group pg, row i), software-pipelined: the
+        // MFMAs of unit u + 1 are issued before the ReLU / head weighting of
+        // unit u, so the VALU work runs in the MFMA shadow.  Each lane sums
+        // its 8 heads; one reduce-scatter per position group then leaves row
+        // 4 wave + g's 32-head score in lane group g.
+        float part[2][4];
+        floatx4 acc[2][2];
+        auto mm = [&](int u) {
+            const int pg = u >> 2, i = u & 3;
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f};
+            floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                floatx4 a0 = {0.f, 0.f, 0.f, 0.f};
-                floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; s++) {
+                a0 = mfma_16x16x32(qa[i][0][s], kv[pg][s], a0);
+                a1 = mfma_16x16x32(qa[i][1][s], kv[pg][s], a1);
+            }
+            acc[u & 1][0] = a0;
+            acc[u & 1][1] = a1;
+        };
+        auto epi = [&](int u) {
+            const int pg = u >> 2, i = u & 3;
+            const floatx4 a0 = acc[u & 1][0], a1 = acc[u & 1][1];
+            float sum = 0.f;
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    a0 = mfma_16x16x32(qa[i][0][s], kv[s], a0);
-                    a1 = mfma_16x16x32(qa[i][1][s], kv[s], a1);
+            for (int v = 0; v < 4; v++) sum += wv[i][v] * relu_bits(a0[v]);
+#pragma unroll
+            for (int v = 0; v < 4; v++) sum += wv[i][4 + v] * relu_bits(a1[v]);
+            part[pg][i] = sum;
+        };
+        mm(0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            if (u + 1 < 8) mm(u + 1);
+            epi(u);
+            if (u + 1 < 8) {
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
                 }
-                float acc = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; v++) acc += wv[i][v] * fmaxf(a0[v] * scale, 0.f);
-#pragma unroll
-                for (int v = 0; v < 4; v++) acc += wv[i][4 + v] * fmaxf(a1[v] * scale, 0.f);
-                part[i] = xrow_sum(acc);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int nmine = nrow[0];
+#pragma unroll
+        for (int i = 1; i < 4; i++) nmine = (g == i) ? nrow[i] : nmine;
+#pragma unroll
+        for (int pg = 0; pg < 2; pg++) {
             // Lane group g stores row 4 wave + g: 16 consecutive scores.
-            float mine = part[0];
-            int nmine = nrow[0];
-#pragma unroll
-            for (int i = 1; i < 4; i++) {
-                mine = (g == i) ? part[i] : mine;
-                nmine = (g == i) ? nrow[i] : nmine;
-            }
+            const float mine = xrow_reduce_scatter4(part[pg]);
             const int pos = p0 + 16 * pg + j;
             if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
         }
@@ -187,12 +214,13 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     for (int hb = 0; hb < 2; hb++)
 #pragma unroll
         for (int s = 0; s < 4; s++) qa[hb][s] = load_bf16x8(qr + (hb * 16 + j) * 128 + 32 * s + 8 * g);
-    // Head weights of the output rows this lane holds: heads 4g+v and 16+4g+v.
+    // Head weights of the output rows this lane holds: heads 4g+v and 16+4g+v,
+    // with the positive index scale folded in (ReLU(s x) = s ReLU(x), s > 0).
     float w0[4], w1[4];
 #pragma unroll
     for (int v = 0; v < 4; v++) {
-        w0[v] = w[r * 32 + 4 * g + v];
-        w1[v] = w[r * 32 + 16 + 4 * g + v];
+        w0[v] = w[r * 32 + 4 * g + v] * scale;
+        w1[v] = w[r * 32 + 16 + 4 * g + v] * scale;
     }
 
     const uint16_t* kb = kc + base[r] * 128;
@@ -226,16 +254,15 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
             }
             float acc = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; v++) acc += w0[v] * fmaxf(a0[v] * scale, 0.f);
+            for (int v = 0; v < 4; v++) acc += w0[v] * relu_bits(a0[v]);
 #pragma unroll
-            for (int v = 0; v < 4; v++) acc += w1[v] * fmaxf(a1[v] * scale, 0.f);
-            part[u] = xrow_sum(acc);
+            for (int v = 0; v < 4; v++) acc += w1[v] * relu_bits(a1[v]);
+            part[u] = acc;  // this lane's 8 heads
         }
         if ((b + nw) * IDX_BLOCK < n) load((b + nw) * IDX_BLOCK);
-        // Lane group g stores group u == g: 64 consecutive scores per store.
-        float mine = part[0];
-#pragma unroll
-        for (int u = 1; u < IDX_GROUPS; u++) mine = (g == u) ? part[u] : mine;
+        // Lane group g takes group u == g, summed over all 32 heads: 64
+        // consecutive scores per store.
+        const float mine = xrow_reduce_scatter4(part);
         const int pos = p0 + 16 * g + j;
         if (pos < n) srow[pos] = mine;
     }
