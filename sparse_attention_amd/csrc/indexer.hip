@@ -40,16 +40,16 @@ constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 // same test, so each row is scored exactly once.
 //
 // One 512-thread workgroup scores a shared block (32 rows x 32 heads = 1024
-// MFMA rows) against 32-position key tiles: each tile is loaded once into LDS
+// MFMA rows) against 64-position key tiles: each tile is loaded once into LDS
 // (256 B per position, rows padded to 272 B so the 16 rows an operand read
 // touches sit in distinct banks), and each wave multiplies its 4 rows' queries
-// (128 heads, kept in registers) by the tile: 64 MFMAs per 8 KB of keys.  The
-// causal triangle is skipped: a block only visits positions below its longest
-// row, and scores past a row's own length are not stored.  Workgroups of one
-// block take every CX-th tile, for load balance across blocks of different
-// lengths.
+// (128 heads, kept in registers) by the tile: 128 MFMAs per 16 KB of keys and
+// one barrier.  The causal triangle is skipped: a block only visits positions
+// below its longest row, and scores past a row's own length are not stored.
+// Workgroups of one block take every CX-th tile, for load balance across
+// blocks of different lengths.
 constexpr int IDX_TILE_ROWS = 32;
-constexpr int IDX_TILE_POS = 32;
+constexpr int IDX_TILE_POS = 64;
 constexpr int IDX_KEY_PITCH = 272;  // bytes per staged key row
 
 // Called by whole waves; the result is wave-uniform.
@@ -105,36 +105,46 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     const int ntile = (nmax + IDX_TILE_POS - 1) / IDX_TILE_POS;
     const uint16_t* kb = kc + base[r0] * 128;
 
-    // Staging roles: thread t moves 16 bytes (position t >> 4, chunk t & 15)
-    // of a 32-position tile.  Positions past nmax are clamped onto nmax - 1.
+    // Staging roles: thread t moves 16 bytes (chunk t & 15) of positions
+    // (t >> 4) and (t >> 4) + 32 of a 64-position tile.  Positions past nmax
+    // are clamped onto nmax - 1.
     const int sp_pos = threadIdx.x >> 4, sp_chunk = threadIdx.x & 15;
-    auto load_tile = [&](int tt) -> u32x4 {
-        const int pos = min(tt * IDX_TILE_POS + sp_pos, nmax - 1);
-        return load_u32x4(kb + (int64_t)pos * 128 + sp_chunk * 8);
+    auto load_tile = [&](int tt, u32x4 (&dst)[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int pos = min(tt * IDX_TILE_POS + sp_pos + 32 * h, nmax - 1);
+            dst[h] = load_u32x4(kb + (int64_t)pos * 128 + sp_chunk * 8);
+        }
     };
     int tt = blockIdx.x;
-    u32x4 pre = {0u, 0u, 0u, 0u};
-    if (tt < ntile) pre = load_tile(tt);
+    u32x4 pre[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (tt < ntile) load_tile(tt, pre);
     int buf = 0;
-    for (; tt < ntile; tt += gridDim.x, buf ^= 1) {
-        *reinterpret_cast<u32x4*>(&keys[buf][sp_pos * IDX_KEY_PITCH + sp_chunk * 16]) = pre;
-        __syncthreads();  // tile visible; the other buffer is free again
-        if (tt + (int)gridDim.x < ntile) pre = load_tile(tt + gridDim.x);
-        const int p0 = tt * IDX_TILE_POS;
-        // B operands: position 16 pg + j, k-step s -> bytes 64 s + 16 g.
-        bf16x8 kv[2][4];
+    int nmine = nrow[0];
 #pragma unroll
-        for (int pg = 0; pg < 2; pg++) {
+    for (int i = 1; i < 4; i++) nmine = (g == i) ? nrow[i] : nmine;
+    for (; tt < ntile; tt += gridDim.x, buf ^= 1) {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+            *reinterpret_cast<u32x4*>(&keys[buf][(sp_pos + 32 * h) * IDX_KEY_PITCH + sp_chunk * 16]) = pre[h];
+        __syncthreads();  // tile visible; the other buffer is free again
+        if (tt + (int)gridDim.x < ntile) load_tile(tt + gridDim.x, pre);
+        const int p0 = tt * IDX_TILE_POS;
+        // B operands of position group pg (positions 16 pg + j, k-step s ->
+        // bytes 64 s + 16 g), read one group ahead into a double buffer.
+        bf16x8 kv[2][4];
+        auto ldkv = [&](int pg) {
             const uint8_t* kp = &keys[buf][(16 * pg + j) * IDX_KEY_PITCH + 16 * g];
 #pragma unroll
-            for (int s = 0; s < 4; s++) kv[pg][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 64 * s));
-        }
-        // Eight units (position group pg, row i), software-pipelined: the
+            for (int s = 0; s < 4; s++) kv[pg & 1][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 64 * s));
+        };
+        // Sixteen units (position group pg, row i), software-pipelined: the
         // MFMAs of unit u + 1 are issued before the ReLU / head weighting of
         // unit u, so the VALU work runs in the MFMA shadow.  Each lane sums
-        // its 8 heads; one reduce-scatter per position group then leaves row
-        // 4 wave + g's 32-head score in lane group g.
-        float part[2][4];
+        // its 8 heads; once a position group is done, one reduce-scatter
+        // leaves row 4 wave + g's 32-head score in lane group g, and its store
+        // overlaps the next group's MFMAs.
+        float part[4];
         floatx4 acc[2][2];
         auto mm = [&](int u) {
             const int pg = u >> 2, i = u & 3;
@@ -142,28 +152,38 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
             floatx4 a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                a0 = mfma_16x16x32(qa[i][0][s], kv[pg][s], a0);
-                a1 = mfma_16x16x32(qa[i][1][s], kv[pg][s], a1);
+                a0 = mfma_16x16x32(qa[i][0][s], kv[pg & 1][s], a0);
+                a1 = mfma_16x16x32(qa[i][1][s], kv[pg & 1][s], a1);
             }
             acc[u & 1][0] = a0;
             acc[u & 1][1] = a1;
         };
         auto epi = [&](int u) {
-            const int pg = u >> 2, i = u & 3;
+            const int i = u & 3;
             const floatx4 a0 = acc[u & 1][0], a1 = acc[u & 1][1];
             float sum = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; v++) sum += wv[i][v] * relu_bits(a0[v]);
 #pragma unroll
             for (int v = 0; v < 4; v++) sum += wv[i][4 + v] * relu_bits(a1[v]);
-            part[pg][i] = sum;
+            part[i] = sum;
         };
+        ldkv(0);
+        ldkv(1);
         mm(0);
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            if (u + 1 < 8) mm(u + 1);
+        for (int u = 0; u < 16; u++) {
+            if (u + 1 < 16) mm(u + 1);
             epi(u);
-            if (u + 1 < 8) {
+            if ((u & 3) == 3) {
+                const int pg = u >> 2;
+                if (pg + 2 < 4) ldkv(pg + 2);  // its buffer's last reader was unit u
+                // Lane group g stores row 4 wave + g: 16 consecutive scores.
+                const float mine = xrow_reduce_scatter4(part);
+                const int pos = p0 + 16 * pg + j;
+                if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
+            }
+            if (u + 1 < 16) {
 #pragma unroll
                 for (int q = 0; q < 8; q++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -171,16 +191,6 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
-        int nmine = nrow[0];
-#pragma unroll
-        for (int i = 1; i < 4; i++) nmine = (g == i) ? nrow[i] : nmine;
-#pragma unroll
-        for (int pg = 0; pg < 2; pg++) {
-            // Lane group g stores row 4 wave + g: 16 consecutive scores.
-            const float mine = xrow_reduce_scatter4(part[pg]);
-            const int pos = p0 + 16 * pg + j;
-            if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
         }
     }
 }
@@ -289,7 +299,7 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
     const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
     if (nblk > 0) {
         // Workgroups per shared block: enough for ~2 per CU overall, never
-        // more than the block's 32-position tiles.
+        // more than the block's 64-position tiles.
         const int tiles = (max_visible + IDX_TILE_POS - 1) / IDX_TILE_POS;
         int cx = (512 + nblk - 1) / nblk;
         if (cx > 8) cx = 8;
