@@ -49,7 +49,7 @@ constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 // Workgroups of one block take every CX-th tile, for load balance across
 // blocks of different lengths.
 constexpr int IDX_TILE_ROWS = 32;
-constexpr int IDX_TILE_POS = 64;
+constexpr int IDX_TILE_POS = 128;
 constexpr int IDX_KEY_PITCH = 272;  // bytes per staged key row
 
 // Called by whole waves; the result is wave-uniform.
@@ -109,15 +109,18 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     // (t >> 4) and (t >> 4) + 32 of a 64-position tile.  Positions past nmax
     // are clamped onto nmax - 1.
     const int sp_pos = threadIdx.x >> 4, sp_chunk = threadIdx.x & 15;
-    auto load_tile = [&](int tt, u32x4 (&dst)[2]) {
+    constexpr int NH = IDX_TILE_POS / 32;  // staging loads per thread per tile
+    auto load_tile = [&](int tt, u32x4 (&dst)[NH]) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
+        for (int h = 0; h < NH; h++) {
             const int pos = min(tt * IDX_TILE_POS + sp_pos + 32 * h, nmax - 1);
             dst[h] = load_u32x4(kb + (int64_t)pos * 128 + sp_chunk * 8);
         }
     };
     int tt = blockIdx.x;
-    u32x4 pre[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    u32x4 pre[NH];
+#pragma unroll
+    for (int h = 0; h < NH; h++) pre[h] = u32x4{0u, 0u, 0u, 0u};
     if (tt < ntile) load_tile(tt, pre);
     int buf = 0;
     int nmine = nrow[0];
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     for (int i = 1; i < 4; i++) nmine = (g == i) ? nrow[i] : nmine;
     for (; tt < ntile; tt += gridDim.x, buf ^= 1) {
 #pragma unroll
-        for (int h = 0; h < 2; h++)
+        for (int h = 0; h < NH; h++)
             *reinterpret_cast<u32x4*>(&keys[buf][(sp_pos + 32 * h) * IDX_KEY_PITCH + sp_chunk * 16]) = pre[h];
         __syncthreads();  // tile visible; the other buffer is free again
         if (tt + (int)gridDim.x < ntile) load_tile(tt + gridDim.x, pre);
@@ -168,22 +171,23 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
             for (int v = 0; v < 4; v++) sum += wv[i][4 + v] * relu_bits(a1[v]);
             part[i] = sum;
         };
+        constexpr int NU = 4 * (IDX_TILE_POS / 16);  // units per tile
         ldkv(0);
         ldkv(1);
         mm(0);
 #pragma unroll
-        for (int u = 0; u < 16; u++) {
-            if (u + 1 < 16) mm(u + 1);
+        for (int u = 0; u < NU; u++) {
+            if (u + 1 < NU) mm(u + 1);
             epi(u);
             if ((u & 3) == 3) {
                 const int pg = u >> 2;
-                if (pg + 2 < 4) ldkv(pg + 2);  // its buffer's last reader was unit u
+                if (pg + 2 < NU / 4) ldkv(pg + 2);  // its buffer's last reader was unit u
                 // Lane group g stores row 4 wave + g: 16 consecutive scores.
                 const float mine = xrow_reduce_scatter4(part);
                 const int pos = p0 + 16 * pg + j;
                 if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
             }
-            if (u + 1 < 16) {
+            if (u + 1 < NU) {
 #pragma unroll
                 for (int q = 0; q < 8; q++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
