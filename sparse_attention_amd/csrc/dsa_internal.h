@@ -24,7 +24,7 @@ constexpr int TK_CAP = 4096;       // candidate slots per row
 constexpr int TK_ROWST = 8;        // u32 words of per-row state
 constexpr int TK_CHUNKST = 4;      // u32 words of per-chunk state
 constexpr int TK_MAX_CHUNKS = 4096;  // DSA_MAX_VISIBLE / TK_CHUNK
-constexpr int TR_MAXN = 262144;    // longest row the one-workgroup-per-row kernel can take
+
 constexpr int TR_ROW_PATH_MAXN = 65536;  // calls with max_visible up to this use it
 
 struct TopkWorkspace {

@@ -40,11 +40,11 @@ constexpr int IDX_BLOCK = 16 * IDX_GROUPS;  // positions per wave iteration
 // same test, so each row is scored exactly once.
 //
 // One 512-thread workgroup scores a shared block (32 rows x 32 heads = 1024
-// MFMA rows) against 64-position key tiles: each tile is loaded once into LDS
+// MFMA rows) against 128-position key tiles: each tile is loaded once into LDS
 // (256 B per position, rows padded to 272 B so the 16 rows an operand read
 // touches sit in distinct banks), and each wave multiplies its 4 rows' queries
-// (128 heads, kept in registers) by the tile: 128 MFMAs per 16 KB of keys and
-// one barrier.  The causal triangle is skipped: a block only visits positions
+// (128 heads, kept in registers) by the tile: 256 MFMAs per wave per 32 KB of
+// keys and one barrier.  The causal triangle is skipped: a block only visits positions
 // below its longest row, and scores past a row's own length are not stored.
 // Workgroups of one block take every CX-th tile, for load balance across
 // blocks of different lengths.
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     const uint16_t* kb = kc + base[r0] * 128;
 
     // Staging roles: thread t moves 16 bytes (chunk t & 15) of positions
-    // (t >> 4) and (t >> 4) + 32 of a 64-position tile.  Positions past nmax
-    // are clamped onto nmax - 1.
+    // (t >> 4) + 32 h, h < NH, of a tile.  Positions past nmax are clamped
+    // onto nmax - 1.
     const int sp_pos = threadIdx.x >> 4, sp_chunk = threadIdx.x & 15;
     constexpr int NH = IDX_TILE_POS / 32;  // staging loads per thread per tile
     auto load_tile = [&](int tt, u32x4 (&dst)[NH]) {
@@ -303,7 +303,7 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
     const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
     if (nblk > 0) {
         // Workgroups per shared block: enough for ~2 per CU overall, never
-        // more than the block's 64-position tiles.
+        // more than the block's key tiles.
         const int tiles = (max_visible + IDX_TILE_POS - 1) / IDX_TILE_POS;
         int cx = (512 + nblk - 1) / nblk;
         if (cx > 8) cx = 8;

@@ -66,12 +66,13 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
 
 // Finds, in a histogram h[0..B) (larger bin = larger key), the bin b holding
 // the need-th largest element (need >= 1, need <= sum of h): the number of
-// elements in bins above b is < need and including b is >= need.  Returns b
-// and the count strictly above it via shared outputs.  NT threads, B a
-// multiple of NT.
+// elements in bins above b is < need and including b is >= need.  Returns b,
+// the count strictly above it and (if out_count is set) the count in b via
+// shared outputs.  NT threads, B a multiple of NT.
 template <int NT, int B>
 __device__ __forceinline__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* out_bin,
-                                                   uint32_t* out_above, uint32_t* sh)
+                                                   uint32_t* out_above, uint32_t* sh,
+                                                   uint32_t* out_count = nullptr)
 {
     constexpr int PER = B / NT;
     const int t = threadIdx.x;
@@ -88,6 +89,7 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* h, uint32_t n
             if (acc + h[b] >= need) {
                 *out_bin = (uint32_t)b;
                 *out_above = acc;
+                if (out_count) *out_count = h[b];
                 break;
             }
             acc += h[b];
@@ -385,59 +387,81 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(const int32_t* _
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per row, for rows of at most TR_MAXN positions.
+// One workgroup per row, for rows of at most TR_ROW_PATH_MAXN positions.  The
+// row is read from memory once, into registers: thread t holds the scores of
+// positions 4 (t + TR_THREADS u) + q, q < 4, for every group u the row
+// reaches.  A workgroup of 16 waves shares one CU, so the per-element work is
+// kept to a few VALU operations: the full pass compares raw floats (exact:
+// fp32 denormals are kept, -0.0 == +0.0 and NaN compares false, the same
+// order as the keys), and only sampled elements and candidates are turned
+// into keys.
 //
 // Fast path (sampled bound):
-//   1. A strided sample of about 4096 scores gives a conservative lower bound
-//      theta_lo on the k-th largest key: the lower edge of the 12-bit key bin
-//      holding the sample's rho-th largest, rho about 1.5x the rank the k-th
-//      largest has in the sample plus a margin.
-//   2. One streaming pass appends every element with key >= theta_lo
-//      (key, position) to its wave's private segment of an LDS candidate list
-//      (a wave-uniform counter: no atomics).
-//   3. If at least k candidates were found and no segment overflowed, the k-th
+//   1. The keys at positions 4 (t + TR_THREADS u) of every su-th group (about
+//      4096 samples) give a conservative lower bound theta_lo on the k-th
+//      largest key: the lower edge of the 12-bit key bin holding the sample's
+//      rho-th largest, rho about 1.5x the rank the k-th largest has in the
+//      sample plus a margin.
+//   2. Every element whose key is >= theta_lo (a float compare against the
+//      bound's float) is a candidate; lanes count their own, the wave and
+//      block prefix sums place them densely in an LDS list.  NaN (and any
+//      position past the row, loaded as NaN) is never a candidate; when that
+//      matters, fewer than k candidates remain and the fallback runs.
+//   3. If there are at least k candidates and they fit the list, the k-th
 //      largest key lies among them, and a radix select over the candidates
-//      alone is exact.  Its bins are taken relative to the candidates' own key
-//      range (12 bits per round, at most three rounds), which spreads them
-//      over the histogram instead of piling onto a few hot bins.
+//      alone (held in registers, 12 bits per round relative to their own key
+//      range, at most three rounds) is exact.
 // Fallback (exact for any input, e.g. huge tie groups or a misleading
 // sample): an LDS histogram of the top 12 key bits of the whole row gives the
-// threshold bin b0; elements above b0 go straight to the result bitmap and
-// those inside b0 become the candidates (if they overflow, the radix rounds
-// rescan the row instead of the list).
-// Finally candidates above theta join a position bitmap, theta-valued ones go
-// to a tie bitmap, and an ordered pass over the bitmaps (one block scan for
-// ties, one for output offsets) keeps the first need_eq ties in position
-// order and writes the selected positions in ascending order.
+// threshold bin b0; elements above b0 are marked selected at once, and the
+// elements inside b0 become the candidates (if they overflow the list, the
+// radix rounds histogram the row again, from memory).
+// Finally candidates above theta are marked in a position bitmap and
+// theta-valued ones in a tie bitmap, and an ordered pass over the bitmaps
+// writes the selected positions in ascending order.  When every theta-valued
+// element is kept (the usual case) one block scan gives the output offsets;
+// otherwise a first scan ranks the ties so that the first need_eq of them in
+// position order are kept.
 constexpr int TR_THREADS = 1024;
 constexpr int TR_WAVES = TR_THREADS / 64;
-constexpr int TR_SEG = 512;                    // candidate slots per wave
-constexpr int TR_CAP = TR_SEG * TR_WAVES;      // 8192
-constexpr int TR_BATCH = 8;  // 16-byte loads in flight per thread in row passes
+constexpr int TR_CAP = 8192;                                       // candidate list slots
+constexpr int TR_CPT = TR_CAP / TR_THREADS;                        // candidate slots per thread
+constexpr int TR_GROUPS = TR_ROW_PATH_MAXN / (4 * TR_THREADS);     // 16 float4 groups per thread
+constexpr int TR_WORDS = TR_ROW_PATH_MAXN / 32;
 
-// Appends (key, t) to the calling wave's segment; `count` is the wave's
-// (uniform) fill level.  Must be called by every lane of the wave.
-__device__ __forceinline__ void append_candidate(bool want, uint32_t key, int t, uint32_t& count,
-                                                 unsigned long long* seg)
+// The order-preserving key of a score, branch-free (see score_key).
+__device__ __forceinline__ uint32_t key_of(float f)
 {
-    const unsigned long long m = __ballot(want);
-    if (m == 0) return;
-    const int lane = threadIdx.x & 63;
-    if (want) {
-        const uint32_t slot = count + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        if (slot < (uint32_t)TR_SEG) seg[slot] = ((unsigned long long)key << 32) | (uint32_t)t;
-    }
-    count += (uint32_t)__popcll(m);
+    const uint32_t b = __float_as_uint(f), a = b & 0x7fffffffu;
+    return a > 0x7f800000u ? 0u : (a == 0u ? 0x80000000u : ((b >> 31) ? ~b : (b | 0x80000000u)));
 }
 
-// Visits every candidate: wave segments are dense prefixes of length segn[w].
-template <class F>
-__device__ __forceinline__ void for_each_candidate(const unsigned long long* cand, const uint32_t* segn, F f)
+// The float whose key is k, for keys of non-NaN scores (k in
+// [key(-inf), key(+inf)]); key(-0.0) maps back to -0.0, which compares like
+// +0.0.
+__device__ __forceinline__ float float_of_key(uint32_t k)
 {
-    for (int i = threadIdx.x; i < TR_CAP; i += TR_THREADS) {
-        const int w = i / TR_SEG;
-        if ((uint32_t)(i - w * TR_SEG) < segn[w]) f(cand[i]);
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Maximum over the wave, valid in lane 63 (DPP row shifts and broadcasts);
+// NaN is ignored.
+__device__ __forceinline__ float wave_max_lane63(float x)
+{
+    const int ninf = __float_as_int(-__builtin_inff());
+#define TR_MAX_STEP(ctrl, rm)                                                                   \
+    {                                                                                           \
+        const float y = __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), ctrl, rm, 0xF, false)); \
+        x = y > x ? y : x;                                                                      \
     }
+    TR_MAX_STEP(0x111, 0xF)  // row_shr:1
+    TR_MAX_STEP(0x112, 0xF)  // row_shr:2
+    TR_MAX_STEP(0x114, 0xF)  // row_shr:4
+    TR_MAX_STEP(0x118, 0xF)  // row_shr:8
+    TR_MAX_STEP(0x142, 0xA)  // row_bcast:15
+    TR_MAX_STEP(0x143, 0xC)  // row_bcast:31
+#undef TR_MAX_STEP
+    return x;
 }
 
 __device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0; }
@@ -456,185 +480,267 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
         for (int t = tid; t < k; t += TR_THREADS) out[t] = t < n ? t : -1;
         return;
     }
-    __shared__ uint32_t hist[TK_BINS];
-    __shared__ uint32_t gtbits[TR_MAXN / 32];
-    __shared__ uint32_t eqbits[TR_MAXN / 32];
-    __shared__ unsigned long long cand[TR_CAP];
-    __shared__ uint32_t segn[TR_WAVES];
+    __shared__ uint32_t hs[TK_BINS];      // sample, then fallback histogram
+    __shared__ uint32_t hr[2][TK_BINS];   // radix rounds, alternating
+    __shared__ uint32_t gtbits[TR_WORDS];
+    __shared__ uint32_t eqbits[TR_WORDS];
+    __shared__ unsigned long long cand[TR_CAP];  // (score bits, position)
+    __shared__ uint32_t wcnt[TR_WAVES];
+    __shared__ float wmax[TR_WAVES];
     __shared__ uint32_t sh[TR_THREADS / 64];
-    __shared__ uint32_t s_bin, s_above, s_max;
+    __shared__ uint32_t s_bin, s_above, s_cnt;
 
-    const int nwords = (n + 31) >> 5;
+    // ---- the row, into registers ---------------------------------------------
     const float* row = scores + (int64_t)r * ld;
-    unsigned long long* seg = cand + wave * TR_SEG;
-    for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
+    const int nu = (n + 4 * TR_THREADS - 1) / (4 * TR_THREADS);  // groups the row reaches
+    float x[TR_GROUPS][4];
+#pragma unroll
+    for (int u = 0; u < TR_GROUPS; u++) {
+        if (u < nu) {
+            // A 4-aligned group starting below n lies inside the row allocation
+            // (ld is a multiple of 4 and n <= ld); lanes past the row re-read
+            // its last group and turn it into NaN below.
+            const int p = min(4 * (tid + TR_THREADS * u), (n - 1) & ~3);
+            const float4 v = *reinterpret_cast<const float4*>(row + p);
+            x[u][0] = v.x;
+            x[u][1] = v.y;
+            x[u][2] = v.z;
+            x[u][3] = v.w;
+        }
+    }
+    const int nwords = (n + 31) >> 5;
+    for (int i = tid; i < TK_BINS; i += TR_THREADS) {
+        hs[i] = 0u;
+        hr[0][i] = 0u;
+        hr[1][i] = 0u;
+    }
     for (int i = tid; i < nwords; i += TR_THREADS) {
         gtbits[i] = 0u;
         eqbits[i] = 0u;
     }
-    if (tid == 0) s_max = 0u;
-    __syncthreads();
-
-    // ---- 1. sampled lower bound -------------------------------------------
-    const int stride = max(1, n >> 12);
-    const int msamp = (n + stride - 1) / stride;
-    const uint32_t rho = (uint32_t)min((int64_t)msamp, ((int64_t)3 * k * msamp) / (2 * (int64_t)n) + 32);
-#pragma unroll 4
-    for (int i = tid; i < msamp; i += TR_THREADS) atomicAdd(&hist[score_key(row[(int64_t)i * stride]) >> 20], 1u);
-    __syncthreads();
-    find_threshold_bin<TR_THREADS, TK_BINS>(hist, rho, &s_bin, &s_above, sh);
-    const uint32_t theta_lo = (rho >= (uint32_t)msamp) ? 0u : (s_bin << 20);
-
-    // ---- 2. filter pass ------------------------------------------------------
-    // TR_BATCH independent 16-byte loads per thread are issued before any is
-    // used, so each wave keeps several KB in flight.
-    uint32_t count = 0;  // wave-uniform
-    for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
-        float4 v[TR_BATCH];
+    // Only the last group can run past the row.
 #pragma unroll
-        for (int u = 0; u < TR_BATCH; u++) {
-            const int b = bb + 4 * (tid + TR_THREADS * u);
-            // A 4-aligned group starting below n lies inside the row
-            // allocation because ld is a multiple of 4 and n <= ld.
-            v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < TR_GROUPS; u++) {
+        if (u == nu - 1 && 4 * TR_THREADS * nu > n) {
+            const int p = 4 * (tid + TR_THREADS * u);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                if (p + q >= n) x[u][q] = __uint_as_float(0xffffffffu);
         }
+    }
+    __syncthreads();  // histograms and bitmaps cleared
+
+    // ---- 1. sampled lower bound ------------------------------------------------
+    // Samples past the row are NaN, key 0, bin 0: below the rho-th largest of
+    // the real samples, so they change nothing.
+    const int su = nu <= 4 ? 1 : (nu <= 8 ? 2 : 4);  // sample every su-th group
+    int msamp = 0;
+    for (int u = 0; u < nu; u += su) msamp += min(TR_THREADS, (n - 4 * TR_THREADS * u + 3) >> 2);
 #pragma unroll
-        for (int u = 0; u < TR_BATCH; u++) {
-            const int b = bb + 4 * (tid + TR_THREADS * u);
-            const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    for (int u = 0; u < TR_GROUPS; u++)
+        if (u < nu && (u & (su - 1)) == 0) atomicAdd(&hs[key_of(x[u][0]) >> 20], 1u);
+    __syncthreads();
+    const uint32_t rho = (uint32_t)min((int64_t)msamp, ((int64_t)3 * k * msamp) / (2 * (int64_t)n) + 32);
+    find_threshold_bin<TR_THREADS, TK_BINS>(hs, rho, &s_bin, &s_above, sh);
+    // Candidates: keys >= lo0, i.e. scores >= flo (key(-inf) is the lowest
+    // key of a non-NaN score).
+    const uint32_t lo0 = max((rho >= (uint32_t)msamp) ? 0u : (s_bin << 20), 0x007fffffu);
+    const float flo = float_of_key(lo0);
+
+    // ---- 2. candidates ----------------------------------------------------------
+    uint32_t c = 0;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < TR_GROUPS; u++) {
+        if (u < nu) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const uint32_t key = score_key(e[q]);
-                append_candidate(b + q < n && key >= theta_lo, key, b + q, count, seg);
+                c += x[u][q] >= flo ? 1u : 0u;
+                mx = x[u][q] > mx ? x[u][q] : mx;
             }
         }
     }
-    if (lane == 0) segn[wave] = count;
+    const uint32_t incl = wave_inclusive_scan(c);
+    mx = wave_max_lane63(mx);
+    if (lane == 63) {
+        wcnt[wave] = incl;
+        wmax[wave] = mx;
+    }
     __syncthreads();
-    uint32_t total = 0;
-    bool seg_over = false;
+    uint32_t total = 0, base = 0;
+    float row_max = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < TR_WAVES; w++) {
-        total += segn[w];
-        seg_over |= segn[w] > (uint32_t)TR_SEG;
+        const uint32_t t = wcnt[w];
+        base += w < wave ? t : 0u;
+        total += t;
+        row_max = wmax[w] > row_max ? wmax[w] : row_max;
     }
-    const bool fast = total >= (uint32_t)k && !seg_over;
+    const bool fast = total >= (uint32_t)k && total <= (uint32_t)TR_CAP;
+    if (fast) {
+        uint32_t slot = base + incl - c;
+#pragma unroll
+        for (int u = 0; u < TR_GROUPS; u++) {
+            if (u < nu) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    if (x[u][q] >= flo) {
+                        cand[slot] = ((unsigned long long)__float_as_uint(x[u][q]) << 32) |
+                                     (uint32_t)(4 * (tid + TR_THREADS * u) + q);
+                        slot++;
+                    }
+                }
+            }
+        }
+    }
 
     uint32_t need = (uint32_t)k;
-    uint32_t lo, hi;            // every key still in play lies in [lo, hi]
-    bool from_row = false;      // candidates overflowed: rescan the row
+    uint32_t lo, hi;          // every key still in play lies in [lo, hi]
+    bool from_regs = false;   // fallback candidates overflowed: rescan the row
+    uint32_t ncand = total;
     if (fast) {
-        lo = theta_lo;
-        uint32_t mx = 0;
-        for_each_candidate(cand, segn, [&](unsigned long long c) { mx = max(mx, (uint32_t)(c >> 32)); });
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
-        if (lane == 0) atomicMax(&s_max, mx);
-        __syncthreads();
-        hi = s_max;
+        lo = lo0;
+        hi = key_of(row_max);  // >= lo0, since some candidate exists
     } else {
-        // ---- fallback: whole-row histogram --------------------------------
-        for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
+        // ---- fallback: whole-row histogram -----------------------------------
+        // (every thread read wcnt above; the barriers below order its reuse)
+        for (int i = tid; i < TK_BINS; i += TR_THREADS) hs[i] = 0u;
         __syncthreads();
-        for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
-            float4 v[TR_BATCH];
 #pragma unroll
-            for (int u = 0; u < TR_BATCH; u++) {
-                const int b = bb + 4 * (tid + TR_THREADS * u);
-                v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < TR_BATCH; u++) {
-                const int b = bb + 4 * (tid + TR_THREADS * u);
-                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < TR_GROUPS; u++) {
+            if (u < nu) {
+                const int p = 4 * (tid + TR_THREADS * u);
 #pragma unroll
                 for (int q = 0; q < 4; q++)
-                    if (b + q < n) atomicAdd(&hist[score_key(e[q]) >> 20], 1u);
+                    if (p + q < n) atomicAdd(&hs[key_of(x[u][q]) >> 20], 1u);
             }
         }
         __syncthreads();
-        find_threshold_bin<TR_THREADS, TK_BINS>(hist, need, &s_bin, &s_above, sh);
+        find_threshold_bin<TR_THREADS, TK_BINS>(hs, need, &s_bin, &s_above, sh);
         const uint32_t b0 = s_bin;
         need -= s_above;
         lo = b0 << 20;
         hi = lo | 0xfffffu;
-        count = 0;
-        for (int bb = 0; bb < n; bb += 4 * TR_THREADS * TR_BATCH) {
-            float4 v[TR_BATCH];
+        // Elements above b0 are selected; those inside b0 are the candidates.
+        uint32_t cb = 0;
 #pragma unroll
-            for (int u = 0; u < TR_BATCH; u++) {
-                const int b = bb + 4 * (tid + TR_THREADS * u);
-                v[u] = b < n ? *reinterpret_cast<const float4*>(row + b) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < TR_BATCH; u++) {
-                const int b = bb + 4 * (tid + TR_THREADS * u);
-                const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < TR_GROUPS; u++) {
+            if (u < nu) {
+                const int p = 4 * (tid + TR_THREADS * u);
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const int t = b + q;
-                    const uint32_t key = score_key(e[q]);
-                    const uint32_t bin = key >> 20;
-                    if (t < n && bin > b0) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
-                    append_candidate(t < n && bin == b0, key, t, count, seg);
+                    const uint32_t kk = key_of(x[u][q]);
+                    if (p + q < n && (kk >> 20) > b0) atomicOr(&gtbits[(p + q) >> 5], 1u << ((p + q) & 31));
+                    cb += (p + q < n && (kk >> 20) == b0) ? 1u : 0u;
                 }
             }
         }
-        __syncthreads();  // every wave has read segn (above) before it changes
-        if (lane == 0) segn[wave] = count;
+        const uint32_t incl_b = wave_inclusive_scan(cb);
+        if (lane == 63) wcnt[wave] = incl_b;
         __syncthreads();
+        uint32_t base_b = 0;
+        ncand = 0;
 #pragma unroll
-        for (int w = 0; w < TR_WAVES; w++) from_row |= segn[w] > (uint32_t)TR_SEG;
+        for (int w = 0; w < TR_WAVES; w++) {
+            const uint32_t t = wcnt[w];
+            base_b += w < wave ? t : 0u;
+            ncand += t;
+        }
+        from_regs = ncand > (uint32_t)TR_CAP;
+        if (!from_regs) {
+            uint32_t slot = base_b + incl_b - cb;
+#pragma unroll
+            for (int u = 0; u < TR_GROUPS; u++) {
+                if (u < nu) {
+                    const int p = 4 * (tid + TR_THREADS * u);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        if (p + q < n && (key_of(x[u][q]) >> 20) == b0) {
+                            cand[slot] = ((unsigned long long)__float_as_uint(x[u][q]) << 32) | (uint32_t)(p + q);
+                            slot++;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // candidate list written
+
+    // Candidate i lives in thread i % TR_THREADS, slot i / TR_THREADS.
+    uint32_t ck[TR_CPT], cp[TR_CPT];
+#pragma unroll
+    for (int j = 0; j < TR_CPT; j++) {
+        const uint32_t i = (uint32_t)(tid + TR_THREADS * j);
+        ck[j] = 0u;
+        cp[j] = 0u;
+        if (!from_regs && i < ncand) {
+            const unsigned long long cv = cand[i];
+            ck[j] = key_of(__uint_as_float((uint32_t)(cv >> 32)));
+            cp[j] = (uint32_t)cv;
+        }
     }
 
     // ---- 3. radix rounds on [lo, hi], 12 bits at a time --------------------
     // Each round histograms (key - lo) >> shift over the keys in [lo, hi]
-    // and narrows [lo, hi] to the bin holding the need-th largest.
-    while (true) {
+    // and narrows [lo, hi] to the bin holding the need-th largest.  Rounds
+    // alternate between two histograms, each cleared for the round after next.
+    uint32_t eq_total = 0;  // theta-valued elements in play, from the last round
+    for (int round = 0;; round++) {
+        uint32_t* h = hr[round & 1];
         const uint32_t span = hi - lo;
         const int shift = max(0, bitlen(span) - 12);
-        for (int i = tid; i < TK_BINS; i += TR_THREADS) hist[i] = 0u;
-        __syncthreads();
-        if (!from_row) {
-            for_each_candidate(cand, segn, [&](unsigned long long c) {
-                const uint32_t key = (uint32_t)(c >> 32);
-                if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
-            });
+        if (!from_regs) {
+#pragma unroll
+            for (int j = 0; j < TR_CPT; j++) {
+                const uint32_t kk = ck[j];
+                if ((uint32_t)(tid + TR_THREADS * j) < ncand && kk >= lo && kk <= hi)
+                    atomicAdd(&h[(kk - lo) >> shift], 1u);
+            }
         } else {
+            // (rare) the row again, from memory, so the registers above can go
             for (int t = tid; t < n; t += TR_THREADS) {
-                const uint32_t key = score_key(row[t]);
-                if (key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+                const uint32_t kk = key_of(row[t]);
+                if (kk >= lo && kk <= hi) atomicAdd(&h[(kk - lo) >> shift], 1u);
             }
         }
         __syncthreads();
-        find_threshold_bin<TR_THREADS, TK_BINS>(hist, need, &s_bin, &s_above, sh);
+        find_threshold_bin<TR_THREADS, TK_BINS>(h, need, &s_bin, &s_above, sh, &s_cnt);
+        const uint32_t bin = s_bin;
         need -= s_above;
-        const uint32_t nlo = lo + (s_bin << shift);
+        for (int i = tid; i < TK_BINS; i += TR_THREADS) h[i] = 0u;  // for round + 2
+        const uint32_t nlo = lo + (bin << shift);
         const uint32_t nhi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
         lo = nlo;
         hi = nhi;
-        if (shift == 0) break;
+        if (shift == 0) {
+            eq_total = s_cnt;
+            break;
+        }
     }
     const uint32_t theta = lo;
     const uint32_t need_eq = need;
+    // When every theta-valued element is kept, ties go straight to the result.
+    const bool keep_all_ties = need_eq == eq_total;
 
-    // Candidates above theta join the result; theta ties are marked.  (In the
-    // fallback, elements above the top-12-bit bin are already in gtbits and
-    // only elements of that bin are candidates.)
-    if (!from_row) {
-        for_each_candidate(cand, segn, [&](unsigned long long c) {
-            const uint32_t key = (uint32_t)(c >> 32);
-            const int t = (int)(uint32_t)c;
-            if (key > theta) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
-            else if (key == theta) atomicOr(&eqbits[t >> 5], 1u << (t & 31));
-        });
+    // ---- bitmaps ----------------------------------------------------------------
+    // Candidates hold every element at or above theta except, in the
+    // fallback, those above b0, which are marked already.
+    if (!from_regs) {
+#pragma unroll
+        for (int j = 0; j < TR_CPT; j++) {
+            const uint32_t kk = ck[j], t = cp[j];
+            if ((uint32_t)(tid + TR_THREADS * j) < ncand && kk >= theta) {
+                if (kk > theta || keep_all_ties) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
+                else atomicOr(&eqbits[t >> 5], 1u << (t & 31));
+            }
+        }
     } else {
-        const uint32_t b0 = theta >> 20;
         for (int t = tid; t < n; t += TR_THREADS) {
-            const uint32_t key = score_key(row[t]);
-            if ((key >> 20) != b0) continue;
-            if (key > theta) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
-            else if (key == theta) atomicOr(&eqbits[t >> 5], 1u << (t & 31));
+            const uint32_t kk = key_of(row[t]);
+            if (kk >= theta) {
+                if (kk > theta || keep_all_ties) atomicOr(&gtbits[t >> 5], 1u << (t & 31));
+                else atomicOr(&eqbits[t >> 5], 1u << (t & 31));
+            }
         }
     }
     __syncthreads();
@@ -642,24 +748,25 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
     // ---- ordered output.  Thread tid owns the contiguous words [w0, w1). ----
     const int per = (nwords + TR_THREADS - 1) / TR_THREADS;
     const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-    uint32_t my_eq = 0;
-    for (int w = w0; w < w1; w++) my_eq += __popc(eqbits[w]);
     uint32_t tot;
-    uint32_t eq_before = block_exclusive_scan<TR_THREADS>(my_eq, &tot, sh);
-    uint32_t my_sel = 0;
-    for (int w = w0; w < w1; w++) {
-        uint32_t e = eqbits[w];
-        uint32_t keep = 0;
-        while (e && eq_before < need_eq) {
-            const uint32_t low = e & (0u - e);
-            keep |= low;
-            e ^= low;
-            eq_before++;
+    if (!keep_all_ties) {
+        uint32_t my_eq = 0;
+        for (int w = w0; w < w1; w++) my_eq += __popc(eqbits[w]);
+        uint32_t eq_before = block_exclusive_scan<TR_THREADS>(my_eq, &tot, sh);
+        for (int w = w0; w < w1; w++) {
+            uint32_t e = eqbits[w];
+            uint32_t keep = 0;
+            while (e && eq_before < need_eq) {
+                const uint32_t low = e & (0u - e);
+                keep |= low;
+                e ^= low;
+                eq_before++;
+            }
+            gtbits[w] |= keep;  // only this thread touches word w from here on
         }
-        const uint32_t selw = gtbits[w] | keep;
-        gtbits[w] = selw;  // only this thread touches word w from here on
-        my_sel += __popc(selw);
     }
+    uint32_t my_sel = 0;
+    for (int w = w0; w < w1; w++) my_sel += __popc(gtbits[w]);
     uint32_t pos = block_exclusive_scan<TR_THREADS>(my_sel, &tot, sh);
     for (int w = w0; w < w1; w++) {
         uint32_t selw = gtbits[w];

@@ -195,7 +195,7 @@ def config(name):
 
 def random_scores(seed, R, n, ld=None, kind="normal"):
     """Synthetic fp32 score rows for exercising the top-k alone.
-    kind: normal | ties (8 distinct values) | zeros | signed_zeros | coarse"""
+    kind: normal | ties (8 distinct values) | zeros | signed_zeros | coarse | tiny"""
     ld = n if ld is None else ld
     g = rng(seed, 100, 0)
     if kind == "normal":
@@ -209,6 +209,11 @@ def random_scores(seed, R, n, ld=None, kind="normal"):
         s[:, ::7] = np.float32(1.0)
     elif kind == "coarse":
         s = np.round(g.standard_normal((R, ld), dtype=np.float32) * 4).astype(np.float32)
+    elif kind == "tiny":
+        # fp32 denormals (multiples of 2^-149, both signs) and signed zeros
+        v = g.integers(-40, 41, size=(R, ld))
+        s = (v.astype(np.float32) * np.float32(2.0 ** -149)).astype(np.float32)
+        s[(v == 0) & (g.integers(0, 2, size=(R, ld)) == 0)] = np.float32(-0.0)
     else:
         raise KeyError(kind)
     return np.ascontiguousarray(s)

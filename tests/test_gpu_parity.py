@@ -208,7 +208,7 @@ def test_indexer_sampled_rows(dsa, oracle_mod, name, rows):
 
 # ----------------------------------------------------------------------------- top-k
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "signed_zeros", "coarse"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "signed_zeros", "coarse", "tiny"])
 @pytest.mark.parametrize("k", [2048, 1, 7, 300])
 def test_topk_bitexact_synthetic(dsa, oracle_mod, kind, k):
     lens = np.array([1, 5, 300, 2047, 2048, 2049, 4095, 4096, 4097, 9000, 20000], np.int32)
@@ -224,12 +224,13 @@ def test_topk_bitexact_synthetic(dsa, oracle_mod, kind, k):
 def test_topk_bitexact_long_rows_and_overflow(dsa, oracle_mod):
     # 65,536-position rows (one workgroup per row): normal scores (sampled
     # fast path), 8-valued ties and all-equal rows (candidate overflow, exact
-    # whole-row fallback), coarse values; and 202,752-position rows (multi-
-    # workgroup path).
+    # whole-row fallback), coarse values, fp32 denormals with signed zeros;
+    # and 202,752-position rows (multi-workgroup path).
     for n in (65536, 202752):
-        lens = np.array([n, n, n, n - 1000], np.int32)
+        lens = np.array([n, n, n, n - 1000, n - 7], np.int32)
         s = np.concatenate([wl.random_scores(1, 1, n, kind="normal"), wl.random_scores(2, 1, n, kind="ties"),
-                            wl.random_scores(3, 1, n, kind="zeros"), wl.random_scores(4, 1, n, kind="coarse")])
+                            wl.random_scores(3, 1, n, kind="zeros"), wl.random_scores(4, 1, n, kind="coarse"),
+                            wl.random_scores(5, 1, n, kind="tiny")])
         got = run_topk(dsa, lens, s, 2048)
         ref = oracle_mod.topk(lens, s, 2048)
         assert np.array_equal(got, ref), n
