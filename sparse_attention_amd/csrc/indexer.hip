@@ -203,8 +203,9 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
 // wave wr of the row scores 64-position blocks wr, wr + NW, wr + 2 NW, ...
 // (NW = waves per row), so the waves in flight read one compact, advancing
 // window of the key cache per row instead of thousands of scattered streams,
-// which keeps DRAM pages open.  Each wave loads its next block before
-// scoring the current one.
+// which keeps DRAM pages open.  Each wave loads each 16-position group of its
+// next block as soon as the same group of the current block has gone
+// through the matrix cores.
 __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
     const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
@@ -241,21 +242,20 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     float* srow = scores + (int64_t)r * ld;
 
     bf16x8 kv[IDX_GROUPS][4];
-    auto load = [&](int p0) {
+    auto load = [&](int p0, int u) {
+        // Reads past the row's visible range are clamped onto its last
+        // position; their results are never stored.
+        const int pc = min(p0 + 16 * u + j, n - 1);
+        const uint16_t* kp = kb + (int64_t)pc * 128 + 8 * g;
 #pragma unroll
-        for (int u = 0; u < IDX_GROUPS; u++) {
-            // Reads past the row's visible range are clamped onto its last
-            // position; their results are never stored.
-            const int pc = min(p0 + 16 * u + j, n - 1);
-            const uint16_t* kp = kb + (int64_t)pc * 128 + 8 * g;
-#pragma unroll
-            for (int s = 0; s < 4; s++) kv[u][s] = load_bf16x8(kp + 32 * s);
-        }
+        for (int s = 0; s < 4; s++) kv[u][s] = load_bf16x8(kp + 32 * s);
     };
 
-    load(wr * IDX_BLOCK);
+#pragma unroll
+    for (int u = 0; u < IDX_GROUPS; u++) load(wr * IDX_BLOCK, u);
     for (int b = wr; b * IDX_BLOCK < n; b += nw) {
         const int p0 = b * IDX_BLOCK;
+        const bool more = (b + nw) * IDX_BLOCK < n;  // wave-uniform
         float part[IDX_GROUPS];
 #pragma unroll
         for (int u = 0; u < IDX_GROUPS; u++) {
@@ -266,6 +266,9 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
                 a0 = mfma_16x16x32(qa[0][s], kv[u][s], a0);
                 a1 = mfma_16x16x32(qa[1][s], kv[u][s], a1);
             }
+            // The group's registers are free once its MFMAs have issued: the
+            // next block's group goes out now, not after the whole block.
+            if (more) load((b + nw) * IDX_BLOCK, u);
             float acc = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; v++) acc += w0[v] * relu_bits(a0[v]);
@@ -273,7 +276,6 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
             for (int v = 0; v < 4; v++) acc += w1[v] * relu_bits(a1[v]);
             part[u] = acc;  // this lane's 8 heads
         }
-        if ((b + nw) * IDX_BLOCK < n) load((b + nw) * IDX_BLOCK);
         // Lane group g takes group u == g, summed over all 32 heads: 64
         // consecutive scores per store.
         const float mine = xrow_reduce_scatter4(part);

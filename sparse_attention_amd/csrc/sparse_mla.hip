@@ -27,11 +27,13 @@
 //    operand (16 bytes per lane).
 //  - Output waves (w = 4..7) own latent columns 128(w-4)..+127 for all 64
 //    heads: O[64 x 128] += P[64 x 32] . V[32 x 128] one tile behind the score
-//    waves, reading each V element once (transposing ds_read_b64_tr_b16) and P
-//    as four plain 16-byte reads.  They also issue the gathers.
+//    waves, reading each V element once (transposing ds_read_b64_tr_b16, into
+//    registers during the tile's QK step, so its ring slot is free one step
+//    later and three tiles stay in flight) and P as four plain 16-byte reads.
+//    They also issue the gathers.
 //  - One barrier per tile: score waves hand over P(t) while output waves
 //    finish PV(t-1); P, the rescale factors and the selected indices live in
-//    small double / quadruple buffers.
+//    small double / octuple buffers.
 //  - Splits write unnormalized partials (O, running max, running sum); a
 //    combine kernel merges them in split order, so results do not depend on
 //    scheduling.  A single split normalizes in place.
@@ -46,7 +48,9 @@ constexpr int AT_TILE = 32;        // selected positions per tile
 constexpr int AT_CHUNKS = 72;      // 16-byte chunks per latent row
 constexpr int AT_TILE_BYTES = AT_TILE * AT_CHUNKS * 16;  // 36,864
 constexpr int AT_STAGES = 4;       // ring slots
+constexpr int AT_SID = 8;          // index ring slots
 constexpr int AT_MAX_SPLIT = 2048; // largest split (slots)
+constexpr int AT_OPAD = 132;       // padded row of an output block staged in LDS (floats)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
 constexpr float LN2 = 0.6931471805599453f;
@@ -91,6 +95,12 @@ __device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_ba
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
+
+// The same for 4 bytes per lane (lane L's word lands at lds_base + 4 L).
+__device__ __forceinline__ void load4_to_lds(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
@@ -121,41 +131,55 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
     __shared__ __attribute__((aligned(16))) u32x4 plds[2][4][64];  // P of tile t: [t & 1][head block][lane]
     __shared__ __attribute__((aligned(16))) float alpha_l[2][64];  // per-head rescale factor of tile t
     __shared__ __attribute__((aligned(16))) int flag_l[2][4];      // head block rescaled in tile t
-    __shared__ __attribute__((aligned(16))) int32_t sid[AT_STAGES][AT_TILE];  // indices of tile t: [t % 4]
+    __shared__ __attribute__((aligned(16))) int32_t sid[AT_SID][AT_TILE];  // indices of tile t: [t % 8]
     __shared__ __attribute__((aligned(16))) float lfin[64];
-    __shared__ int s_last;
+    __shared__ int s_wlast[8];
 
-    // Last valid slot of the split: tiles past it hold no position and are skipped.
-    if (threadIdx.x == 0) s_last = -1;
-    __syncthreads();
+    // Prologue, one memory round trip before the first gathers: every thread
+    // reads its slots of the split (at most four), posting the first tiles'
+    // indices to the index ring and the last valid slot (tiles past it hold no
+    // position and are skipped) as a per-wave maximum.
+    static_assert(AT_MAX_SPLIT <= 4 * 512, "four slots per thread");
+    int32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) v[u] = irow[min((int)threadIdx.x + 512 * u, nslots - 1)];  // nslots >= 1
     {
         int last = -1;
-        for (int i = threadIdx.x; i < nslots; i += 512)
-            if (irow[i] >= 0) last = i;
-        if (last >= 0) atomicMax(&s_last, last);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int i = threadIdx.x + 512 * u;
+            if (i >= nslots) v[u] = -1;
+            last = v[u] >= 0 ? i : last;
+        }
+        if (threadIdx.x < AT_STAGES * AT_TILE) sid[threadIdx.x / AT_TILE][threadIdx.x % AT_TILE] = v[0];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d));
+        if (lane == 0) s_wlast[wave] = last;
+    }
+    // The queries go out after the indices have been used (so that waiting
+    // for the indices does not mean waiting for them): they still land before
+    // the first tile, which needs a second round trip.
+    bf16x8 qreg[18];  // score waves: B operands of QK, Q[r][16 wr + j][32 s + 8 g .. +8]
+    if (scorer) {
+        const uint16_t* qrow = qa + ((int64_t)r * 64 + wr * 16 + j) * 576 + 8 * g;
+#pragma unroll
+        for (int s = 0; s < 18; s++) qreg[s] = load_bf16x8(qrow + 32 * s);
     }
     __syncthreads();
+    int s_last = -1;
+#pragma unroll
+    for (int w = 0; w < 8; w++) s_last = max(s_last, s_wlast[w]);
     const int ntiles = (s_last + AT_TILE) / AT_TILE;
-    // Indices of a tile (padding slots past the split read as -1).
-    auto tile_index = [&](int t, int p) -> int32_t {
-        const int i = t * AT_TILE + p;
-        return (t < ntiles && i < nslots) ? irow[i] : -1;
-    };
-    if (threadIdx.x < (AT_STAGES - 1) * AT_TILE)
-        sid[threadIdx.x / AT_TILE][threadIdx.x % AT_TILE] = tile_index(threadIdx.x / AT_TILE, threadIdx.x % AT_TILE);
 
     if (scorer) {
         // ------------------------------------------------------------ score waves
         const int h0 = wr * 16;
-        // B operands of QK: Q[r][h0 + j][32 s + 8 g .. +8].
-        bf16x8 qreg[18];
-        {
-            const uint16_t* qrow = qa + ((int64_t)r * 64 + h0 + j) * 576 + 8 * g;
+        // Complete the query loads here: otherwise the compiler's wait counts
+        // at the loop head assume they may still be in flight and make every
+        // step wait for the index prefetches below as well.
 #pragma unroll
-            for (int s = 0; s < 18; s++) qreg[s] = load_bf16x8(qrow + 32 * s);
-        }
-        __syncthreads();  // indices of tiles 0..2 visible
-        lds_barrier();    // tile 0 landed (the output waves waited for it)
+        for (int s = 0; s < 18; s++) asm volatile("" ::"v"(qreg[s]));
+        lds_barrier();  // tile 0 landed (the output waves waited for it)
 
         // QK A-operand bases: rows j and 16 + j, logical chunk 4 s + g =
         // 8 (s >> 1) + (4 (s & 1) + g) -> two bases per row plus immediate 128 (s >> 1).
@@ -163,12 +187,21 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         const int qa10 = tile_chunk_offset(16 + j, g), qa11 = tile_chunk_offset(16 + j, 4 + g);
         float m_run = -INFINITY, l_run = 0.f;  // head h0 + j; l_run: this lane's positions
 
-        for (int t = 0; t < ntiles; t++) {
-            // Indices of tile t + 3 (one score wave loads them; they are
-            // stored at the end of this step, into the slot of tile t - 1).
-            int32_t next_id = -1;
-            if (wr == 0) next_id = tile_index(t + AT_STAGES - 1, lane & 31);
-
+        // The index ring is refilled by direct loads into LDS (wave 0, lanes
+        // 0..31), two steps ahead: the indices of tile t + 5 go out at the
+        // start of step t and are waited for at the end of step t + 1, before
+        // the barrier after which the output waves issue that tile's gathers.
+        // Slots past the split read its last slot and are masked as invalid.
+        auto fetch_ids = [&](int tt) {
+            if (lane < AT_TILE) {
+                const int i = min(tt * AT_TILE + lane, nslots - 1);
+                load4_to_lds(irow + i, (uint32_t)(uintptr_t)&sid[tt % AT_SID][0]);
+            }
+        };
+        if (wr == 0 && AT_STAGES < ntiles) fetch_ids(AT_STAGES);
+        auto score_step = [&](int t) {
+            const bool fetch = wr == 0 && t + AT_STAGES + 1 < ntiles;  // wave-uniform
+            if (fetch) fetch_ids(t + AT_STAGES + 1);
             const uint8_t* tl = ring[t % AT_STAGES];
             // QK: s0 -> tile positions 0..15, s1 -> 16..31 (rows of S^T);
             // lane (j, g) ends with S[head h0 + j][position 16 mb + 4 g + v] in s_mb[v].
@@ -193,7 +226,8 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
             }
 
             // Validity of the tile's 32 slots (bit p: slot p holds a position).
-            const uint32_t vbits = (uint32_t)__ballot(sid[t % AT_STAGES][lane & 31] >= 0);
+            const uint32_t vbits =
+                (uint32_t)__ballot(sid[t % AT_SID][lane & 31] >= 0 && t * AT_TILE + (lane & 31) < nslots);
             float z[8];
 #pragma unroll
             for (int v = 0; v < 4; v++) {
@@ -235,9 +269,14 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
             if (g == 0) alpha_l[t & 1][h0 + j] = alpha;
             const bool any_need = __ballot(need) != 0ull;
             if (lane == 0) flag_l[t & 1][wr] = any_need ? 1 : 0;
-            if (wr == 0 && lane < AT_TILE) sid[(t + AT_STAGES - 1) % AT_STAGES][lane] = next_id;
+            // Indices of tile t + 4 landed (those of t + 5 may be in flight).
+            if (wr == 0) {
+                if (fetch) wait_vm<1>();
+                else wait_vm<0>();
+            }
             lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
-        }
+        };
+        for (int t = 0; t < ntiles; t++) score_step(t);
 
         // Row sums (the four lanes of a head), log-sum-exp, split statistics.
         const float l_tot = xrow_sum(l_run);
@@ -269,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         int gid[9];
         auto gather_ids = [&](int t) {
 #pragma unroll
-            for (int i = 0; i < 9; i++) gid[i] = sid[t % AT_STAGES][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
+            for (int i = 0; i < 9; i++) gid[i] = sid[t % AT_SID][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
         };
         auto gather_one = [&](int t, int i) {
             const uint32_t dst = __builtin_amdgcn_readfirstlane(
@@ -302,90 +341,129 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
 #pragma unroll
             for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-        // PV of tile t: rescale the O rows of head blocks whose reference
-        // moved, then O[64 x 128] += P[64 x 32] . V[32 x 128].  With refill
-        // >= 0 the loads of tile `refill` go out between the MFMAs.
-        auto pv = [&](int t, int refill) {
+        // V operands of the current tile, read from the ring one step before
+        // their PV, so that a slot is free as soon as both roles have read it
+        // (the step after its QK) and three tiles stay in flight.
+        bf16x8 vb[8];
+        // Step body of the output waves at step t: rescale the O rows of head
+        // blocks whose reference moved in tile t - 1 and accumulate
+        // O[64 x 128] += P(t-1)[64 x 32] . V(t-1)[32 x 128] (if t > 0), then
+        // read V(t) into vb.  With refill >= 0 the loads of tile `refill` go
+        // out between the MFMAs.
+        auto step = [&](int t, int refill) {
             const uint8_t* tl = ring[t % AT_STAGES];
+            if (t > 0) {
+                const int tp = (t - 1) & 1;
+                bf16x8 pa[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[tp][mb][lane]);
+                const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[tp]);
+#pragma unroll
+                for (int mb = 0; mb < 4; mb++) {
+                    if (__builtin_amdgcn_readfirstlane(fl[mb])) {
+                        const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[tp][16 * mb + 4 * g]);
+#pragma unroll
+                        for (int cb = 0; cb < 8; cb++)
+#pragma unroll
+                            for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
+                    }
+                }
+#pragma unroll
+                for (int cb = 0; cb < 8; cb++) {
+#pragma unroll
+                    for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
+                    const int off = 128 * (cb >> 2);
+                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off),
+                                              (const uint16_t*)(tl + vhi[cb & 3] + off));
+                    if (refill >= 0) gather_one(refill, cb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < 8; cb++) {
+                    const int off = 128 * (cb >> 2);
+                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off),
+                                              (const uint16_t*)(tl + vhi[cb & 3] + off));
+                    if (refill >= 0) gather_one(refill, cb);
+                }
+            }
+            if (refill >= 0) gather_one(refill, 8);
+        };
+        // PV of the last tile, after the final hand-over.
+        auto pv_last = [&](int t) {
+            const int tp = t & 1;
             bf16x8 pa[4];
 #pragma unroll
-            for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[t & 1][mb][lane]);
-            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[t & 1]);
+            for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[tp][mb][lane]);
+            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[tp]);
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
                 if (__builtin_amdgcn_readfirstlane(fl[mb])) {
-                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[t & 1][16 * mb + 4 * g]);
+                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[tp][16 * mb + 4 * g]);
 #pragma unroll
                     for (int cb = 0; cb < 8; cb++)
 #pragma unroll
                         for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
                 }
             }
-            constexpr int PV_AHEAD = 2;
-            bf16x8 vb[8];
-            auto rdv = [&](int cb) {
-                const int off = 128 * (cb >> 2);
-                vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off), (const uint16_t*)(tl + vhi[cb & 3] + off));
-            };
 #pragma unroll
-            for (int cb = 0; cb < PV_AHEAD; cb++) rdv(cb);
-#pragma unroll
-            for (int cb = 0; cb < 8; cb++) {
-                if (cb + PV_AHEAD < 8) rdv(cb + PV_AHEAD);
+            for (int cb = 0; cb < 8; cb++)
 #pragma unroll
                 for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
-                if (refill >= 0) gather_one(refill, cb);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (refill >= 0) gather_one(refill, 8);
         };
 
-        __syncthreads();  // indices of tiles 0..2 visible
         // Pipeline: at step t the score waves work on tile t and the output
-        // waves on tile t - 1; tiles t + 1 (landed) and t + 2 (in flight) fill
-        // the other two slots.  Loads in flight per output wave after the
-        // issue of step t: tiles t + 1, t + 2.
+        // waves on tiles t - 1 (PV) and t (V reads); tiles t + 1 (landed),
+        // t + 2 and t + 3 (in flight) fill the other slots.  The refill of
+        // step t goes into the slot of tile t - 1, which both roles finished
+        // reading in step t - 1.
         if (ntiles > 0) issue(0);
         if (ntiles > 1) issue(1);
-        if (ntiles > 1) wait_vm<9>();
+        if (ntiles > 2) issue(2);
+        if (ntiles > 2) wait_vm<18>();
+        else if (ntiles > 1) wait_vm<9>();
         else wait_vm<0>();
         lds_barrier();  // tile 0 landed
         for (int t = 0; t < ntiles; t++) {
-            // Refill: tile t + 2 into the slot of tile t - 2 (finished at step t - 1).
-            const int refill = t + 2 < ntiles ? t + 2 : -1;  // wave-uniform
+            const int refill = t + 3 < ntiles ? t + 3 : -1;  // wave-uniform
             if (refill >= 0) gather_ids(refill);
-            if (t > 0) pv(t - 1, refill);
-            else if (refill >= 0)
-#pragma unroll
-                for (int i = 0; i < 9; i++) gather_one(refill, i);
+            step(t, refill);
             if (t + 1 < ntiles) {
-                if (t + 2 < ntiles) wait_vm<9>();
+                // Tile t + 1 must have landed; tiles issued after it may not.
+                const int after = min(ntiles - 1, t + 3) - (t + 1);
+                if (after >= 2) wait_vm<18>();
+                else if (after == 1) wait_vm<9>();
                 else wait_vm<0>();
             }
             lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
         }
-        if (ntiles > 0) pv(ntiles - 1, -1);
+        if (ntiles > 0) pv_last(ntiles - 1);
         __syncthreads();  // lfin visible
 
-        // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j].
+        // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j]; the
+        // block goes through this wave's own region of the (now idle) ring,
+        // rows padded to 132 floats, so that the stores leave as 16-byte
+        // pieces of 512-byte row segments.
+        float* ot = reinterpret_cast<float*>(&ring[0][0]) + wr * (64 * AT_OPAD);
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const int h = 16 * mb + 4 * g + v;
-                float* orow;
-                float scl;
-                if (nsplit == 1) {
-                    orow = out + ((int64_t)r * 64 + h) * 512 + c0;
-                    scl = lv[v] > 0.f ? 1.f / lv[v] : 0.f;
-                } else {
-                    orow = part_o + (((int64_t)r * nsplit + sp) * 64 + h) * 512 + c0;
-                    scl = 1.f;
-                }
+                const float scl = nsplit == 1 ? (lv[v] > 0.f ? 1.f / lv[v] : 0.f) : 1.f;
+                float* orow = ot + (16 * mb + 4 * g + v) * AT_OPAD + j;
 #pragma unroll
-                for (int cb = 0; cb < 8; cb++) orow[16 * cb + j] = o[mb][cb][v] * scl;
+                for (int cb = 0; cb < 8; cb++) orow[16 * cb] = o[mb][cb][v] * scl;
             }
+        }
+        // Only this wave touches its region: LDS keeps its accesses in order.
+        float* dst = nsplit == 1 ? out + (int64_t)r * 64 * 512 + c0
+                                 : part_o + ((int64_t)r * nsplit + sp) * 64 * 512 + c0;
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const int h = 2 * i + (lane >> 5), c = 4 * (lane & 31);
+            const floatx4 val = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
+            *reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c) = val;
         }
     }
 }
