@@ -14,7 +14,7 @@
 // round trips for the softmax), so the workgroup is split into two kinds of
 // waves that work on consecutive tiles at the same time:
 //  - One workgroup = one row x one contiguous split of its index list;
-//    8 waves, one "score" wave and one "output" wave per SIMD.
+//    12 waves: per SIMD one "score" wave and two "output" waves.
 //  - Tiles of 32 selected positions: the 32 latent rows (1152 B each) are
 //    gathered into a 4-slot LDS ring with direct global->LDS loads.
 //  - Score waves (w = 0..3) own heads 16w..16w+15.  QK computes
@@ -25,12 +25,13 @@
 //    needs in-lane work plus two cross-row swaps.  P is rounded to bf16
 //    (round-to-nearest-even) and stored in the exact layout of the PV A
 //    operand (16 bytes per lane).
-//  - Output waves (w = 4..7) own latent columns 128(w-4)..+127 for all 64
-//    heads: O[64 x 128] += P[64 x 32] . V[32 x 128] one tile behind the score
+//  - Output waves (w = 4..11) own latent columns 64(w-4)..+63 for all 64
+//    heads: O[64 x 64] += P[64 x 32] . V[32 x 64] one tile behind the score
 //    waves, reading each V element once (transposing ds_read_b64_tr_b16, into
 //    registers during the tile's QK step, so its ring slot is free one step
 //    later and three tiles stay in flight) and P as four plain 16-byte reads.
-//    They also issue the gathers.
+//    They also issue the gathers; with two of them per SIMD, one waiting for
+//    the address unit leaves the matrix core to the other.
 //  - One barrier per tile: score waves hand over P(t) while output waves
 //    finish PV(t-1); P, the rescale factors and the selected indices live in
 //    small double / octuple buffers.
@@ -50,7 +51,12 @@ constexpr int AT_TILE_BYTES = AT_TILE * AT_CHUNKS * 16;  // 36,864
 constexpr int AT_STAGES = 4;       // ring slots
 constexpr int AT_SID = 8;          // index ring slots
 constexpr int AT_MAX_SPLIT = 2048; // largest split (slots)
-constexpr int AT_OPAD = 132;       // padded row of an output block staged in LDS (floats)
+constexpr int AT_OWAVES = 8;       // output waves
+constexpr int AT_OCOLS = 512 / AT_OWAVES;  // latent columns per output wave (64)
+constexpr int AT_OCB = AT_OCOLS / 16;      // 16-column blocks per output wave
+constexpr int AT_GQ = AT_TILE_BYTES / 1024;  // gather instructions per tile (36)
+constexpr int AT_THREADS = 64 * (4 + AT_OWAVES);  // 4 score waves + output waves
+constexpr int AT_OPAD = AT_OCOLS + 4;  // padded row of an output block staged in LDS (floats)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
 constexpr float LN2 = 0.6931471805599453f;
@@ -103,7 +109,7 @@ __device__ __forceinline__ void load4_to_lds(const void* src, uint32_t lds_base)
 }
 #pragma clang diagnostic pop
 
-__global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
+__global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
                                                            const int32_t* __restrict__ idx, int k,
@@ -133,21 +139,21 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
     __shared__ __attribute__((aligned(16))) int flag_l[2][4];      // head block rescaled in tile t
     __shared__ __attribute__((aligned(16))) int32_t sid[AT_SID][AT_TILE];  // indices of tile t: [t % 8]
     __shared__ __attribute__((aligned(16))) float lfin[64];
-    __shared__ int s_wlast[8];
+    __shared__ int s_wlast[AT_THREADS / 64];
 
     // Prologue, one memory round trip before the first gathers: every thread
-    // reads its slots of the split (at most four), posting the first tiles'
+    // reads its slots of the split (at most three), posting the first tiles'
     // indices to the index ring and the last valid slot (tiles past it hold no
     // position and are skipped) as a per-wave maximum.
-    static_assert(AT_MAX_SPLIT <= 4 * 512, "four slots per thread");
-    int32_t v[4];
+    static_assert(AT_MAX_SPLIT <= 3 * AT_THREADS, "three slots per thread");
+    int32_t v[3];
 #pragma unroll
-    for (int u = 0; u < 4; u++) v[u] = irow[min((int)threadIdx.x + 512 * u, nslots - 1)];  // nslots >= 1
+    for (int u = 0; u < 3; u++) v[u] = irow[min((int)threadIdx.x + AT_THREADS * u, nslots - 1)];  // nslots >= 1
     {
         int last = -1;
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int i = threadIdx.x + 512 * u;
+        for (int u = 0; u < 3; u++) {
+            const int i = threadIdx.x + AT_THREADS * u;
             if (i >= nslots) v[u] = -1;
             last = v[u] >= 0 ? i : last;
         }
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
     __syncthreads();
     int s_last = -1;
 #pragma unroll
-    for (int w = 0; w < 8; w++) s_last = max(s_last, s_wlast[w]);
+    for (int w = 0; w < AT_THREADS / 64; w++) s_last = max(s_last, s_wlast[w]);
     const int ntiles = (s_last + AT_TILE) / AT_TILE;
 
     if (scorer) {
@@ -291,29 +297,32 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         __syncthreads();  // lfin visible to the output waves
     } else {
         // ----------------------------------------------------------- output waves
-        const int c0 = wr * 128;
-        const int tc = lane & 3;  // transposed-read roles inside a 16-lane group
+        const int ob = wave - 4;    // output wave 0..7
+        const int c0 = ob * AT_OCOLS;
+        const int tc = lane & 3;    // transposed-read roles inside a 16-lane group
         const int tk = (lane >> 2) & 3;
         const uint16_t* kvrow = kv + base[r] * 576;
 
-        // Gather roles.  Output wave b fills tile rows 8b..8b+7 (LDS chunks
-        // [576 b, 576 b + 576)): its i-th load instruction writes 64
-        // consecutive 16-byte LDS chunks (lane order), and lane L fetches
-        // whichever logical chunk belongs at LDS chunk 576 b + 64 i + L under
-        // the swizzle.  Padding slots fetch the sequence's first latent row
-        // (always present); their softmax weight is zero.
-        // The address unit takes ~30 clocks per such instruction, so the nine
-        // loads of a refill are spread over the PV MFMAs (gather_one) rather
-        // than issued back to back, which would stall this wave meanwhile.
-        int gid[9];
+        // Gather roles.  A tile is 36 load instructions, each writing 64
+        // consecutive 16-byte LDS chunks (lane order); output wave ob issues
+        // instructions q = ob + 8 i (five for ob < 4, four otherwise), and lane
+        // L fetches whichever logical chunk belongs at LDS chunk 64 q + L
+        // under the swizzle.  Padding slots fetch the sequence's first latent
+        // row (always present); their softmax weight is zero.  The loads are
+        // spread over the PV MFMAs: a wave waiting for the address unit leaves
+        // the matrix core to the other output wave of its SIMD.
+        const bool five = ob < AT_GQ - 4 * AT_OWAVES;  // wave-uniform
+        int gid[5];
         auto gather_ids = [&](int t) {
 #pragma unroll
-            for (int i = 0; i < 9; i++) gid[i] = sid[t % AT_SID][((wr * 9 + i) * 64 + lane) / AT_CHUNKS];
+            for (int i = 0; i < 5; i++)
+                gid[i] = sid[t % AT_SID][min((ob + AT_OWAVES * i) * 64 + lane, AT_TILE * AT_CHUNKS - 1) / AT_CHUNKS];
         };
         auto gather_one = [&](int t, int i) {
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(ring[t % AT_STAGES] + wr * 9 * 1024 + i * 1024));
-            const int p = (wr * 9 + i) * 64 + lane;
+            const int q = ob + AT_OWAVES * i;
+            const uint32_t dst =
+                __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ring[t % AT_STAGES] + q * 1024));
+            const int p = q * 64 + lane;
             const int row = p / AT_CHUNKS;
             const int part = (p - row * AT_CHUNKS) ^ (row & 7);
             gather16_to_lds(kvrow + (int64_t)max(gid[i], 0) * 576 + part * 8, dst);
@@ -321,33 +330,59 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         auto issue = [&](int t) {
             gather_ids(t);
 #pragma unroll
-            for (int i = 0; i < 9; i++) gather_one(t, i);
+            for (int i = 0; i < 4; i++) gather_one(t, i);
+            if (five) gather_one(t, 4);
+        };
+        // Tile t + 1 landed, `after` tiles issued later possibly not.
+        auto wait_tiles = [&](int after) {
+            if (five) {
+                if (after >= 2) wait_vm<10>();
+                else if (after == 1) wait_vm<5>();
+                else wait_vm<0>();
+            } else {
+                if (after >= 2) wait_vm<8>();
+                else if (after == 1) wait_vm<4>();
+                else wait_vm<0>();
+            }
         };
 
-        // Transposed-read bases (tile rows 4g + tk and 16 + 4g + tk, columns
-        // c0 + 16 cb + 4 tc .. +3 = logical chunk 16 b + 2 cb + (tc >> 1),
-        // byte 8 (tc & 1)); cb = 4 m + e -> immediate 128 m on top of base e.
+        // Transposed-read bases: tile rows 4g + tk and 16 + 4g + tk, columns
+        // c0 + 16 cb + 4 tc .. +3 = logical chunk 8 ob + 2 cb + (tc >> 1),
+        // byte 8 (tc & 1).
         const int vrlo = 4 * g + tk, vrhi = 16 + 4 * g + tk;
-        int vlo[4], vhi[4];
+        int vlo[AT_OCB], vhi[AT_OCB];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            vlo[e] = tile_chunk_offset(vrlo, 16 * wr + 2 * e + (tc >> 1)) + 8 * (tc & 1);
-            vhi[e] = tile_chunk_offset(vrhi, 16 * wr + 2 * e + (tc >> 1)) + 8 * (tc & 1);
+        for (int cb = 0; cb < AT_OCB; cb++) {
+            vlo[cb] = tile_chunk_offset(vrlo, 8 * ob + 2 * cb + (tc >> 1)) + 8 * (tc & 1);
+            vhi[cb] = tile_chunk_offset(vrhi, 8 * ob + 2 * cb + (tc >> 1)) + 8 * (tc & 1);
         }
         // O[16 mb + 4 g + v][c0 + 16 cb + j] = o[mb][cb][v].
-        floatx4 o[4][8];
+        floatx4 o[4][AT_OCB];
 #pragma unroll
         for (int mb = 0; mb < 4; mb++)
 #pragma unroll
-            for (int cb = 0; cb < 8; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < AT_OCB; cb++) o[mb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
         // V operands of the current tile, read from the ring one step before
         // their PV, so that a slot is free as soon as both roles have read it
         // (the step after its QK) and three tiles stay in flight.
-        bf16x8 vb[8];
+        bf16x8 vb[AT_OCB];
+        auto rescale = [&](int tp) {
+            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[tp]);
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+                if (__builtin_amdgcn_readfirstlane(fl[mb])) {
+                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[tp][16 * mb + 4 * g]);
+#pragma unroll
+                    for (int cb = 0; cb < AT_OCB; cb++)
+#pragma unroll
+                        for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
+                }
+            }
+        };
         // Step body of the output waves at step t: rescale the O rows of head
         // blocks whose reference moved in tile t - 1 and accumulate
-        // O[64 x 128] += P(t-1)[64 x 32] . V(t-1)[32 x 128] (if t > 0), then
+        // O[64 x 64] += P(t-1)[64 x 32] . V(t-1)[32 x 64] (if t > 0), then
         // read V(t) into vb.  With refill >= 0 the loads of tile `refill` go
         // out between the MFMAs.
         auto step = [&](int t, int refill) {
@@ -357,37 +392,23 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
                 bf16x8 pa[4];
 #pragma unroll
                 for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[tp][mb][lane]);
-                const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[tp]);
+                rescale(tp);
 #pragma unroll
-                for (int mb = 0; mb < 4; mb++) {
-                    if (__builtin_amdgcn_readfirstlane(fl[mb])) {
-                        const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[tp][16 * mb + 4 * g]);
-#pragma unroll
-                        for (int cb = 0; cb < 8; cb++)
-#pragma unroll
-                            for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
-                    }
-                }
-#pragma unroll
-                for (int cb = 0; cb < 8; cb++) {
+                for (int cb = 0; cb < AT_OCB; cb++) {
 #pragma unroll
                     for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
-                    const int off = 128 * (cb >> 2);
-                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off),
-                                              (const uint16_t*)(tl + vhi[cb & 3] + off));
+                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb]), (const uint16_t*)(tl + vhi[cb]));
                     if (refill >= 0) gather_one(refill, cb);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
 #pragma unroll
-                for (int cb = 0; cb < 8; cb++) {
-                    const int off = 128 * (cb >> 2);
-                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb & 3] + off),
-                                              (const uint16_t*)(tl + vhi[cb & 3] + off));
+                for (int cb = 0; cb < AT_OCB; cb++) {
+                    vb[cb] = lds_read_tr_pair((const uint16_t*)(tl + vlo[cb]), (const uint16_t*)(tl + vhi[cb]));
                     if (refill >= 0) gather_one(refill, cb);
                 }
             }
-            if (refill >= 0) gather_one(refill, 8);
+            if (refill >= 0 && five) gather_one(refill, 4);
         };
         // PV of the last tile, after the final hand-over.
         auto pv_last = [&](int t) {
@@ -395,19 +416,9 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
             bf16x8 pa[4];
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) pa[mb] = __builtin_bit_cast(bf16x8, plds[tp][mb][lane]);
-            const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_l[tp]);
+            rescale(tp);
 #pragma unroll
-            for (int mb = 0; mb < 4; mb++) {
-                if (__builtin_amdgcn_readfirstlane(fl[mb])) {
-                    const floatx4 al = *reinterpret_cast<const floatx4*>(&alpha_l[tp][16 * mb + 4 * g]);
-#pragma unroll
-                    for (int cb = 0; cb < 8; cb++)
-#pragma unroll
-                        for (int v = 0; v < 4; v++) o[mb][cb][v] *= al[v];
-                }
-            }
-#pragma unroll
-            for (int cb = 0; cb < 8; cb++)
+            for (int cb = 0; cb < AT_OCB; cb++)
 #pragma unroll
                 for (int mb = 0; mb < 4; mb++) o[mb][cb] = mfma_16x16x32(pa[mb], vb[cb], o[mb][cb]);
         };
@@ -420,21 +431,13 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
         if (ntiles > 0) issue(0);
         if (ntiles > 1) issue(1);
         if (ntiles > 2) issue(2);
-        if (ntiles > 2) wait_vm<18>();
-        else if (ntiles > 1) wait_vm<9>();
-        else wait_vm<0>();
+        wait_tiles(min(ntiles, 3) - 1);
         lds_barrier();  // tile 0 landed
         for (int t = 0; t < ntiles; t++) {
             const int refill = t + 3 < ntiles ? t + 3 : -1;  // wave-uniform
             if (refill >= 0) gather_ids(refill);
             step(t, refill);
-            if (t + 1 < ntiles) {
-                // Tile t + 1 must have landed; tiles issued after it may not.
-                const int after = min(ntiles - 1, t + 3) - (t + 1);
-                if (after >= 2) wait_vm<18>();
-                else if (after == 1) wait_vm<9>();
-                else wait_vm<0>();
-            }
+            if (t + 1 < ntiles) wait_tiles(min(ntiles - 1, t + 3) - (t + 1));
             lds_barrier();  // step t: P(t) handed over; tile t + 1 landed
         }
         if (ntiles > 0) pv_last(ntiles - 1);
@@ -442,9 +445,9 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
 
         // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j]; the
         // block goes through this wave's own region of the (now idle) ring,
-        // rows padded to 132 floats, so that the stores leave as 16-byte
-        // pieces of 512-byte row segments.
-        float* ot = reinterpret_cast<float*>(&ring[0][0]) + wr * (64 * AT_OPAD);
+        // rows padded to AT_OPAD floats, so that the stores leave as 16-byte
+        // pieces of 256-byte row segments.
+        float* ot = reinterpret_cast<float*>(&ring[0][0]) + ob * (64 * AT_OPAD);
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
@@ -453,15 +456,15 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(const int64_t* __res
                 const float scl = nsplit == 1 ? (lv[v] > 0.f ? 1.f / lv[v] : 0.f) : 1.f;
                 float* orow = ot + (16 * mb + 4 * g + v) * AT_OPAD + j;
 #pragma unroll
-                for (int cb = 0; cb < 8; cb++) orow[16 * cb] = o[mb][cb][v] * scl;
+                for (int cb = 0; cb < AT_OCB; cb++) orow[16 * cb] = o[mb][cb][v] * scl;
             }
         }
         // Only this wave touches its region: LDS keeps its accesses in order.
         float* dst = nsplit == 1 ? out + (int64_t)r * 64 * 512 + c0
                                  : part_o + ((int64_t)r * nsplit + sp) * 64 * 512 + c0;
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            const int h = 2 * i + (lane >> 5), c = 4 * (lane & 31);
+        for (int i = 0; i < 16; i++) {
+            const int h = 4 * i + (lane >> 4), c = 4 * (lane & 15);
             const floatx4 val = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
             *reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c) = val;
         }
@@ -552,7 +555,7 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
         part_o = (float*)ws;
         part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
     }
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(512), 0, stream, base, qa, kv, idx, k,
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k,
                        softmax_scale * LOG2E, split_len, out, lse, part_o, part_ml);
     if (s > 1)
         hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(64, num_rows), dim3(128), 0, stream, part_o, part_ml, s,

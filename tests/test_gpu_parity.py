@@ -391,6 +391,32 @@ def test_prefill_rows_up_to_k_equal_dense(dsa, oracle_mod):
     assert recall_check(idx[rows], idx_ref, s64, y["visible_len"]) >= 0.999
 
 
+@pytest.mark.parametrize("R", [64, 100, 128, 16])
+def test_decode_step_attention_matches_standalone_call(dsa, R):
+    """The attention inside dsa_decode_step equals dsa_sparse_mla_attn on the
+    same index lists bit for bit, for 4, 3, 2 and 16 splits per row, also when
+    the workspace starts out full of garbage and is reused by a second call
+    (the split partials and their merge leave nothing behind)."""
+    w, x = inputs("c3")
+    y = sub(x, [i % 64 for i in range(R)])
+    d = device_inputs(y)
+    vis, base = y["visible_len"], y["row_cache_base"]
+    rows = make_rows(dsa, vis, base)
+    k = 2048
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, int(vis.max()), k), DEV)
+    ws.fill_(255)
+    for rep in range(2):
+        idx = torch.empty((R, k), dtype=torch.int32, device=DEV)
+        out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+        dsa.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], wl.INDEX_SCALE, d["q_abs"], d["kv_latent"],
+                            wl.SOFTMAX_SCALE, k, idx, out, lse, ws)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = run_attn(dsa, y, idx.cpu().numpy(), k, d=d)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref_out.view(np.uint32)), rep
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref_lse.view(np.uint32)), rep
+
+
 def test_decode_step_deterministic(dsa):
     w, x = inputs("c3")
     d = device_inputs(x)
