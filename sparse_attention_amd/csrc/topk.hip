@@ -68,31 +68,53 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
 // the need-th largest element (need >= 1, need <= sum of h): the number of
 // elements in bins above b is < need and including b is >= need.  Returns b,
 // the count strictly above it and (if out_count is set) the count in b via
-// shared outputs.  NT threads, B a multiple of NT.
+// shared outputs.  NT threads, B a multiple of NT; two barriers: thread t
+// holds bins [B - PER (t+1), B - PER t) in registers, a wave prefix sum plus
+// the per-wave totals in sh[] give its offset from the top, and the one
+// thread whose range holds the answer scans its own registers.
 template <int NT, int B>
 __device__ __forceinline__ void find_threshold_bin(const uint32_t* h, uint32_t need, uint32_t* out_bin,
                                                    uint32_t* out_above, uint32_t* sh,
                                                    uint32_t* out_count = nullptr)
 {
     constexpr int PER = B / NT;
-    const int t = threadIdx.x;
-    // Thread t owns bins [B - PER (t+1), B - PER t), scanned from the top.
+    static_assert(PER >= 1 && PER * NT == B, "bins split evenly over the threads");
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int lo = B - PER * (t + 1);
+    uint32_t c[PER];
+    if constexpr (PER % 4 == 0) {  // 16-byte reads (the histograms are 16-byte aligned)
+#pragma unroll
+        for (int i = 0; i < PER; i += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(h + lo + i);
+            c[i] = v.x;
+            c[i + 1] = v.y;
+            c[i + 2] = v.z;
+            c[i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; i++) c[i] = h[lo + i];
+    }
     uint32_t mine = 0;
 #pragma unroll
-    for (int i = 0; i < PER; i++) mine += h[B - 1 - (PER * t + i)];
-    uint32_t total;
-    uint32_t pre = block_exclusive_scan<NT>(mine, &total, sh);
+    for (int i = 0; i < PER; i++) mine += c[i];
+    const uint32_t incl = wave_inclusive_scan(mine);
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) before += (w < wave) ? sh[w] : 0u;
+    const uint32_t pre = before + incl - mine;  // elements in bins above this thread's range
     if (pre < need && pre + mine >= need) {
         uint32_t acc = pre;
-        for (int i = 0; i < PER; i++) {
-            const int b = B - 1 - (PER * t + i);
-            if (acc + h[b] >= need) {
-                *out_bin = (uint32_t)b;
+#pragma unroll
+        for (int i = PER - 1; i >= 0; i--) {
+            if (acc < need && acc + c[i] >= need) {
+                *out_bin = (uint32_t)(lo + i);
                 *out_above = acc;
-                if (out_count) *out_count = h[b];
-                break;
+                if (out_count) *out_count = c[i];
             }
-            acc += h[b];
+            acc += c[i];
         }
     }
     __syncthreads();
@@ -140,7 +162,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const int32_t* __
     const int start = blockIdx.x * TK_CHUNK;
     if (n <= k || n <= min_n || start >= n) return;
     const int end = min(n, start + TK_CHUNK);
-    __shared__ uint32_t h[TK_BINS];
+    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
     for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
     uint32_t key[TK_PER_THREAD], present;
@@ -167,7 +189,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(const int32_t* 
     const int start = c * TK_CHUNK;
     if (n <= k || n <= min_n || start >= n) return;
     const int end = min(n, start + TK_CHUNK);
-    __shared__ uint32_t h[TK_BINS];
+    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
     __shared__ uint32_t sh[TK_THREADS / 64];
     __shared__ uint32_t s_b0, s_gt0, s_base;
     const uint32_t* gh = hist + (int64_t)r * TK_BINS;
@@ -221,7 +243,7 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
     const int n = vis[r];
     if (n <= k || n <= min_n) return;
     __shared__ unsigned long long cl[TK_CAP];
-    __shared__ uint32_t h[TK_BINS];
+    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
     __shared__ uint32_t cgt[TK_MAX_CHUNKS / 2];  // per-chunk counts, see note below
     __shared__ uint32_t ceq[TK_MAX_CHUNKS / 2];
     __shared__ uint32_t sh[RS_THREADS / 64];
@@ -480,8 +502,8 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
         for (int t = tid; t < k; t += TR_THREADS) out[t] = t < n ? t : -1;
         return;
     }
-    __shared__ uint32_t hs[TK_BINS];      // sample, then fallback histogram
-    __shared__ uint32_t hr[2][TK_BINS];   // radix rounds, alternating
+    __shared__ __attribute__((aligned(16))) uint32_t hs[TK_BINS];     // sample, then fallback histogram
+    __shared__ __attribute__((aligned(16))) uint32_t hr[2][TK_BINS];  // radix rounds, alternating
     __shared__ uint32_t gtbits[TR_WORDS];
     __shared__ uint32_t eqbits[TR_WORDS];
     __shared__ unsigned long long cand[TR_CAP];  // (score bits, position)
