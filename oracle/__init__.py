@@ -32,6 +32,8 @@ def _lib():
         lib.oracle_round_to_f32.argtypes = [i64, P, P]
         lib.oracle_topk.argtypes = [i32, P, P, i64, i32, P]
         lib.oracle_sparse_mla.argtypes = [i32, P, P, P, P, i32, f64, P, P]
+        lib.oracle_absorb_queries.argtypes = [i32, P, P, P, P]
+        lib.oracle_v_up_proj.argtypes = [i32, P, P, P]
         lib.oracle_version.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -93,6 +95,28 @@ def sparse_mla(row_cache_base, q_abs, kv_latent, indices, softmax_scale):
     lse = np.empty((R, 64), np.float64)
     _lib().oracle_sparse_mla(R, _p(base), _p(qa), _p(kv), _p(idx), k, float(softmax_scale), _p(out), _p(lse))
     return out, lse
+
+
+def absorb_queries(q_nope, q_pe, kv_b):
+    """q_abs [R,64,576] fp64 = [W_UK^T q_nope || q_pe] per head (bf16-bit inputs;
+    kv_b is the kv_b_proj weight [64,448,512])."""
+    qn = _c(q_nope, np.uint16).reshape(-1, 64, 192)
+    R = qn.shape[0]
+    qp = _c(q_pe, np.uint16).reshape(R, 64, 64)
+    w = _c(kv_b, np.uint16).reshape(64, 448, 512)
+    out = np.empty((R, 64, 576), np.float64)
+    _lib().oracle_absorb_queries(R, _p(qn), _p(qp), _p(w), _p(out))
+    return out
+
+
+def v_up_proj(o, kv_b):
+    """out [R,64,256] fp64 = W_UV o per head (o taken as given, in fp64)."""
+    oo = _c(o, np.float64).reshape(-1, 64, 512)
+    R = oo.shape[0]
+    w = _c(kv_b, np.uint16).reshape(64, 448, 512)
+    out = np.empty((R, 64, 256), np.float64)
+    _lib().oracle_v_up_proj(R, _p(oo), _p(w), _p(out))
+    return out
 
 
 def decode_step(visible_len, row_cache_base, q_idx, w, k_idx, q_abs, kv_latent, k, index_scale, softmax_scale):

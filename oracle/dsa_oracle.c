@@ -206,3 +206,69 @@ void oracle_sparse_mla(int32_t R, const int64_t* base, const uint16_t* qa, const
         free(z);
     }
 }
+
+/* Per-head kv_b_proj geometry ([P1] CH4 §4.1: kv_b_proj expands the 512-d
+ * latent into 64 heads x (192 non-RoPE key dims + 256 value dims); §4.5 step 2
+ * splits each head's 448 outputs as [k_nope (192) || value (256)];
+ * [P5] Q1.1: qk_nope_head_dim 192, v_head_dim 256). */
+#define OR_NOPE 192
+#define OR_VDIM 256
+#define OR_KVB_ROWS (OR_NOPE + OR_VDIM)
+#define OR_ROPE 64
+
+/*
+ * Query absorption (the step before the path).  kv_b_proj is linear, so for
+ * the non-RoPE part of head h, with W_UK,h the first 192 rows of its 448 output
+ * rows ([P1] §4.1, §4.5 step 2):
+ *     q_nope . k_nope = q_nope . (W_UK,h c) = (W_UK,h^T q_nope) . c
+ * and the absorbed query is the 576-wide [W_UK,h^T q_nope || q_pe]:
+ *     q_abs[r,h,c]       = sum_{d<192} W[h,d,c] * q_nope[r,h,d]    (c < 512)
+ *     q_abs[r,h,512 + i] = q_pe[r,h,i]                              (i < 64)
+ * q_nope: [R,64,192] bf16 bits; q_pe: [R,64,64] bf16 bits; kvb: kv_b_proj
+ * weight [64,448,512] bf16 bits; q_abs: [R,64,576] fp64.
+ */
+void oracle_absorb_queries(int32_t R, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* kvb,
+                           double* q_abs)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < R; r++) {
+        for (int h = 0; h < OR_HEADS; h++) {
+            const uint16_t* qn = q_nope + ((int64_t)r * OR_HEADS + h) * OR_NOPE;
+            const uint16_t* qp = q_pe + ((int64_t)r * OR_HEADS + h) * OR_ROPE;
+            const uint16_t* W = kvb + (int64_t)h * OR_KVB_ROWS * OR_LATENT;
+            double* o = q_abs + ((int64_t)r * OR_HEADS + h) * OR_ROW;
+            for (int c = 0; c < OR_LATENT; c++) {
+                double acc = 0.0;
+                for (int d = 0; d < OR_NOPE; d++) acc += bf16_to_f64(W[(int64_t)d * OR_LATENT + c]) * bf16_to_f64(qn[d]);
+                o[c] = acc;
+            }
+            for (int i = 0; i < OR_ROPE; i++) o[OR_LATENT + i] = bf16_to_f64(qp[i]);
+        }
+    }
+}
+
+/*
+ * V up-projection (the step after the path): the values are W_UV,h c with
+ * W_UV,h the last 256 of head h's 448 kv_b_proj rows ([P1] §4.1, §4.5 step 2),
+ * and attention weights sum linearly, so the head output is W_UV,h applied to
+ * the latent output o[r,h,:]:
+ *     out[r,h,v] = sum_{c<512} W[h, 192 + v, c] * o[r,h,c]           (v < 256)
+ * o: [R,64,512] fp64 (given as the caller hands it); kvb: [64,448,512] bf16
+ * bits; out: [R,64,256] fp64.
+ */
+void oracle_v_up_proj(int32_t R, const double* o, const uint16_t* kvb, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < R; r++) {
+        for (int h = 0; h < OR_HEADS; h++) {
+            const double* oh = o + ((int64_t)r * OR_HEADS + h) * OR_LATENT;
+            const uint16_t* W = kvb + ((int64_t)h * OR_KVB_ROWS + OR_NOPE) * OR_LATENT;
+            double* y = out + ((int64_t)r * OR_HEADS + h) * OR_VDIM;
+            for (int v = 0; v < OR_VDIM; v++) {
+                double acc = 0.0;
+                for (int c = 0; c < OR_LATENT; c++) acc += bf16_to_f64(W[(int64_t)v * OR_LATENT + c]) * oh[c];
+                y[v] = acc;
+            }
+        }
+    }
+}

@@ -258,32 +258,40 @@ def test_attention_one_and_two_position_closed_forms(oracle_mod):
 
 
 def test_attention_absorbed_equals_expanded_mla_via_torch_sdpa(oracle_mod):
-    """Absorbed form (576-wide rows, 512-wide latent output) against the
-    expanded form the teardown's §4.5 describes (k = [W_UK c || k_pe],
-    v = W_UV c, 256-wide QK heads, scale 1/sqrt(256)), run through torch's
-    scaled_dot_product_attention in fp64 on the CPU."""
+    """The absorbed path -- query absorption, 576-wide attention with a
+    512-wide latent output, V up-projection, all three oracle functions --
+    against the expanded form the teardown's §4.1/§4.5 describes (kv_b_proj
+    rows [W_UK (192) || W_UV (256)] per head, k = [W_UK c || k_pe], v = W_UV c,
+    256-wide QK heads, scale 1/sqrt(256)), run through torch's
+    scaled_dot_product_attention in fp64 on the CPU.  A transposed weight, a
+    wrong row offset between W_UK and W_UV, or a dropped q_pe fails it."""
     g = np.random.default_rng(12)
     T, H = 40, 64
     kv = bf16((T, 576), 13)                       # [c_kv (512) || k_pe (64)]
     c = f(kv[:, :512])
     k_pe = f(kv[:, 512:])
-    # W_UK [H, 192, 512] with 3 nonzeros (+-1) per latent column keeps
-    # q_abs = W_UK^T q_nope exact in bf16 for small-integer q_nope.
+    # kv_b_proj weight [H, 448, 512]: W_UK rows with 3 nonzeros (+-1) per
+    # latent column keep q_abs = W_UK^T q_nope exact in bf16 for small-integer
+    # q_nope; W_UV rows are bf16 values.
     W_UK = np.zeros((H, 192, 512))
     for h in range(H):
         for col in range(512):
             rows = g.choice(192, 3, replace=False)
             W_UK[h, rows, col] = g.choice([-1.0, 1.0], 3)
-    W_UV = g.standard_normal((H, 256, 512)) / 16
+    W_UV_bits = bf16((H, 256, 512), 15, scale=1 / 16)
+    W_UV = f(W_UV_bits)
+    kvb = np.concatenate([wl.f32_to_bf16_bits(W_UK.astype(np.float32)), W_UV_bits], axis=1)
     q_nope = g.integers(-2, 3, size=(H, 192)).astype(np.float64)
-    q_pe = f(bf16((H, 64), 14))
-    q_abs = np.concatenate([np.einsum("hdc,hd->hc", W_UK, q_nope), q_pe], axis=1)
+    q_nope_bits = wl.f32_to_bf16_bits(q_nope.astype(np.float32))
+    q_pe_bits = bf16((H, 64), 14)
+    q_pe = f(q_pe_bits)
+    q_abs = oracle_mod.absorb_queries(q_nope_bits[None], q_pe_bits[None], kvb)[0]
     q_abs_bits = wl.f32_to_bf16_bits(q_abs.astype(np.float32))
     assert np.array_equal(f(q_abs_bits), q_abs)   # exactly representable
     idx = np.array([[1, 5, 6, 17, 22, 31, 39, -1]], np.int32)
     sel = idx[0][idx[0] >= 0]
     out, lse = oracle_mod.sparse_mla(np.zeros(1, np.int64), q_abs_bits[None], kv, idx, 1 / 16)
-    absorbed = np.einsum("hvc,hc->hv", W_UV, out[0])        # per-head V up-projection
+    absorbed = oracle_mod.v_up_proj(out, kvb)[0]          # per-head V up-projection
     k_nope = np.einsum("hdc,tc->htd", W_UK, c[sel])          # [H, m, 192]
     k_full = np.concatenate([k_nope, np.broadcast_to(k_pe[sel], (H, len(sel), 64))], axis=2)
     v_full = np.einsum("hvc,tc->htv", W_UV, c[sel])          # [H, m, 256]
@@ -292,6 +300,33 @@ def test_attention_absorbed_equals_expanded_mla_via_torch_sdpa(oracle_mod):
         torch.from_numpy(q_full), torch.from_numpy(np.ascontiguousarray(k_full)),
         torch.from_numpy(np.ascontiguousarray(v_full)), scale=1 / 16)[:, 0].numpy()
     np.testing.assert_allclose(absorbed, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_absorption_and_up_projection_one_hot_weights(oracle_mod):
+    """With one-hot kv_b_proj rows both projections reduce to gathers: W_UK,h
+    with W[h, d, pi(d)] = 1 puts q_nope[d] at latent column pi(d) (the other
+    columns 0) and appends q_pe; W_UV,h with W[h, 192 + v, sigma(v)] = 1 picks
+    o[sigma(v)].  The head index must match on both sides."""
+    g = np.random.default_rng(21)
+    R, H = 2, 64
+    kvb = np.zeros((H, 448, 512), np.uint16)
+    one = wl.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    pi = np.stack([g.permutation(512)[:192] for _ in range(H)])
+    sigma = np.stack([g.permutation(512)[:256] for _ in range(H)])
+    for h in range(H):
+        kvb[h, np.arange(192), pi[h]] = one
+        kvb[h, 192 + np.arange(256), sigma[h]] = one
+    q_nope = bf16((R, H, 192), 22)
+    q_pe = bf16((R, H, 64), 23)
+    q_abs = oracle_mod.absorb_queries(q_nope, q_pe, kvb)
+    expect = np.zeros((R, H, 576))
+    for h in range(H):
+        expect[:, h, pi[h]] = f(q_nope[:, h])
+    expect[:, :, 512:] = f(q_pe)
+    assert np.array_equal(q_abs, expect)
+    o = g.standard_normal((R, H, 512))
+    y = oracle_mod.v_up_proj(o, kvb)
+    assert np.array_equal(y, np.stack([o[:, h, sigma[h]] for h in range(H)], axis=1))
 
 
 def test_dsa_equals_dense_causal_attention_when_at_most_k_visible(oracle_mod):
