@@ -186,6 +186,42 @@ DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, 
                              int32_t* indices, float* out_latent, float* out_lse, void* ws,
                              size_t ws_bytes, void* hip_stream);
 
+/* ---- Projections on either side of the path ----------------------------
+ *
+ * kv_b_proj expands the 512-d latent into 64 heads x (192 non-RoPE key dims
+ * + 256 value dims) ("GLM-5.1 架构深度拆解" CH4 §4.1; §4.5 step 2 splits each
+ * head's 448 output rows as [k_nope || value]).  Both calls take that weight
+ * as the model holds it:
+ *   kv_b_weight  [64, 448, 512] bf16: head h's rows 0..191 are W_UK,h, rows
+ *                192..447 are W_UV,h; each row is 512 latent columns.
+ * Because kv_b_proj is linear, q_nope . (W_UK,h c) = (W_UK,h^T q_nope) . c
+ * and the values W_UV,h c can be up-projected after the attention sum, which
+ * is what lets the attention run on the 576-wide latent rows.
+ */
+
+/* Query absorption: for each row r < num_rows and head h < 64,
+ *   q_abs[r,h,c]       = sum_{d<192} W_UK,h[d,c] * q_nope[r,h,d]   (c < 512)
+ *   q_abs[r,h,512 + i] = q_pe[r,h,i]                                (i < 64)
+ * computed on bf16 matrix cores with fp32 accumulation and rounded to bf16
+ * (round-to-nearest-even): the q_abs layout dsa_sparse_mla_attn and
+ * dsa_decode_step take.
+ *   q_nope [R,64,192] bf16, q_pe [R,64,64] bf16 (RoPE already applied),
+ *   kv_b_weight as above, q_abs [R,64,576] bf16 (written).
+ * Errors: num_rows outside [1, 2^24]; a NULL or not 16-byte-aligned pointer;
+ * no gfx950 device.  No workspace. */
+DSA_API dsa_status_t dsa_absorb_queries(int32_t num_rows, const void* q_nope, const void* q_pe,
+                                        const void* kv_b_weight, void* q_abs, void* hip_stream);
+
+/* V up-projection: for each row r < num_rows and head h < 64,
+ *   out[r,h,v] = sum_{c<512} W_UV,h[v,c] * bf16(o_latent[r,h,c])   (v < 256)
+ * where bf16() rounds to nearest even (the precision of the bf16 matrix-core
+ * operand); fp32 accumulation.  o_latent is the attention output
+ * (out_latent of dsa_sparse_mla_attn / dsa_decode_step).
+ *   o_latent [R,64,512] fp32, kv_b_weight as above, out [R,64,256] fp32.
+ * Errors: as for dsa_absorb_queries. */
+DSA_API dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* kv_b_weight,
+                                   float* out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,6 +84,8 @@ def load_library():
         "dsa_sparse_mla_attn": ([rows_p, P, P, P, i32, f32, P, P, P, sz, P], ctypes.c_int),
         "dsa_decode_step_workspace_size": ([i32, i32, i32], sz),
         "dsa_decode_step": ([rows_p, P, P, P, f32, P, P, f32, i32, P, P, P, P, sz, P], ctypes.c_int),
+        "dsa_absorb_queries": ([i32, P, P, P, P, P], ctypes.c_int),
+        "dsa_v_up_proj": ([i32, P, P, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sigs.items():
         fn = getattr(lib, name)
@@ -98,7 +100,8 @@ def exported_symbols():
     return [
         "dsa_version", "dsa_status_string", "dsa_last_error_detail", "dsa_indexer_scores",
         "dsa_topk_workspace_size", "dsa_topk_select", "dsa_sparse_mla_workspace_size",
-        "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step",
+        "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step", "dsa_absorb_queries",
+        "dsa_v_up_proj",
     ]
 
 
@@ -218,3 +221,21 @@ def dsa_decode_step(rows, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softma
                                _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
                                ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream, out_latent)))
+
+
+def dsa_absorb_queries(q_nope, q_pe, kv_b_weight, q_abs, stream=None):
+    """q_abs [R,64,576] bf16 = [W_UK^T q_nope || q_pe] per head."""
+    lib = load_library()
+    R = int(q_nope.shape[0])
+    _check(lib.dsa_absorb_queries(R, _ptr(q_nope, "q_nope", _BF16), _ptr(q_pe, "q_pe", _BF16),
+                                  _ptr(kv_b_weight, "kv_b_weight", _BF16), _ptr(q_abs, "q_abs", _BF16),
+                                  _stream(stream, q_abs)))
+
+
+def dsa_v_up_proj(o_latent, kv_b_weight, out, stream=None):
+    """out [R,64,256] fp32 = W_UV bf16(o_latent) per head."""
+    lib = load_library()
+    R = int(o_latent.shape[0])
+    _check(lib.dsa_v_up_proj(R, _ptr(o_latent, "o_latent", (torch.float32,)),
+                             _ptr(kv_b_weight, "kv_b_weight", _BF16), _ptr(out, "out", (torch.float32,)),
+                             _stream(stream, out)))

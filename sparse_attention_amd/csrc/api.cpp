@@ -289,4 +289,36 @@ dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const fl
     return after_launch(st, "decode_step/sparse_mla");
 }
 
+dsa_status_t dsa_absorb_queries(int32_t num_rows, const void* q_nope, const void* q_pe, const void* kv_b_weight,
+                                void* q_abs, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    if (num_rows < 1 || num_rows > kMaxRows)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows=%d outside [1, %d]", num_rows, kMaxRows);
+    DSA_TRY(check_ptr16(q_nope, "q_nope"));
+    DSA_TRY(check_ptr16(q_pe, "q_pe"));
+    DSA_TRY(check_ptr16(kv_b_weight, "kv_b_weight"));
+    DSA_TRY(check_ptr16(q_abs, "q_abs"));
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::launch_absorb_queries(num_rows, (const uint16_t*)q_nope, (const uint16_t*)q_pe,
+                               (const uint16_t*)kv_b_weight, (uint16_t*)q_abs, st);
+    return after_launch(st, "absorb_queries");
+}
+
+dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* kv_b_weight, float* out,
+                           void* hip_stream)
+{
+    g_detail[0] = '\0';
+    if (num_rows < 1 || num_rows > kMaxRows)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "num_rows=%d outside [1, %d]", num_rows, kMaxRows);
+    DSA_TRY(check_ptr16(o_latent, "o_latent"));
+    DSA_TRY(check_ptr16(kv_b_weight, "kv_b_weight"));
+    DSA_TRY(check_ptr16(out, "out"));
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::launch_v_up_proj(num_rows, o_latent, (const uint16_t*)kv_b_weight, out, st);
+    return after_launch(st, "v_up_proj");
+}
+
 }  // extern "C"

@@ -47,6 +47,11 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
                        const uint16_t* kv, const int32_t* idx, int32_t k, float softmax_scale,
                        float* out, float* lse, void* ws, hipStream_t stream);
 
+// ---- projections on either side of the attention -------------------------
+void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* kvb,
+                           uint16_t* q_abs, hipStream_t stream);
+void launch_v_up_proj(int32_t num_rows, const float* o, const uint16_t* kvb, float* out, hipStream_t stream);
+
 // Debug aid: when DSA_SYNC_DEBUG=1, synchronize after every launch.
 bool sync_debug();
 

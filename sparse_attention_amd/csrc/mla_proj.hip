@@ -1,0 +1,190 @@
+// mla_proj.hip -- the two per-head projections on either side of the
+// absorbed sparse attention, on gfx950 matrix cores.
+//
+// kv_b_proj expands the 512-d latent into 64 heads x (192 non-RoPE key dims +
+// 256 value dims) ("GLM-5.1 架构深度拆解" CH4 §4.1; §4.5 step 2 splits each
+// head's 448 output rows as [k_nope || value]).  Being linear, it can move
+// off the cache side:
+//  - query absorption: q_abs[r,h] = [W_UK,h^T q_nope[r,h] (512) || q_pe[r,h] (64)],
+//    W_UK,h = head h's first 192 rows, so that q_abs . [c_kv || k_pe] equals
+//    the expanded q_nope . k_nope + q_pe . k_pe;
+//  - V up-projection: out[r,h] = W_UV,h o[r,h], W_UV,h = head h's last 256
+//    rows, applied once to the attention's 512-wide latent output instead of
+//    to every selected value row.
+// Both are per-head GEMMs, C_h[R x N] = A_h[R x K] B_h[K x N], run on
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulate):
+//   absorption:     A = q_nope (K = 192), B = W_UK,h (N = 512 latent columns)
+//   up-projection:  A = bf16(o) (K = 512), B = W_UV,h^T (N = 256 value dims)
+// A workgroup (4 waves) owns one head and one 64-column tile of N, stages that
+// tile of the weight in LDS once, and walks the 64-row tiles of R (wave w:
+// rows 16w..16w+15, all four 16-column blocks).  At decode batch sizes the
+// weights (12.6 + 16.8 MB) are the traffic; at prefill sizes the MFMAs.
+//  - W_UK rows are 512 latent values each, so its K (= row) direction is
+//    strided; the staged tile is read with transposing LDS reads
+//    (ds_read_b64_tr_b16), which deliver 4 consecutive rows of one column per
+//    lane, so two reads give the 8 consecutive K values of a B operand.
+//  - W_UV rows are already K-contiguous: plain 16-byte LDS reads.
+//  - o arrives as fp32 and is rounded to bf16 (round-to-nearest-even) as it
+//    is loaded, the precision of the MFMA operand.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int PJ_NOPE = 192;   // qk_nope_head_dim
+constexpr int PJ_VDIM = 256;   // v_head_dim
+constexpr int PJ_LAT = 512;    // kv_lora_rank
+constexpr int PJ_ROPE = 64;    // qk_rope_head_dim
+constexpr int PJ_ROW = PJ_LAT + PJ_ROPE;
+constexpr int PJ_KVB = PJ_NOPE + PJ_VDIM;  // kv_b_proj rows per head
+constexpr int PJ_TM = 64;      // rows of R per tile
+constexpr int PJ_TN = 64;      // columns of N per workgroup
+constexpr int AB_PITCH = 160;  // bytes per staged W_UK row (64 bf16 + 32; spreads the 16 rows a read touches)
+constexpr int VU_PITCH = 1040; // bytes per staged W_UV row (512 bf16 + 16)
+
+__device__ __forceinline__ uint16_t to_bf16(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);  // round-to-nearest-even
+}
+
+__global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __restrict__ qn,
+                                                     const uint16_t* __restrict__ qp,
+                                                     const uint16_t* __restrict__ kvb, uint16_t* __restrict__ qa)
+{
+    const int nt = blockIdx.x;  // 64-column tile of the 512 latent columns
+    const int h = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
+    __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_NOPE * AB_PITCH];
+
+    // Stage W_UK,h[0:192][64 nt .. +64]: 192 rows x 8 chunks of 16 bytes.
+    const uint16_t* W = kvb + (int64_t)h * PJ_KVB * PJ_LAT + PJ_TN * nt;
+    for (int i = threadIdx.x; i < PJ_NOPE * 8; i += 256) {
+        const int row = i >> 3, ch = i & 7;
+        *reinterpret_cast<u32x4*>(wt + row * AB_PITCH + 16 * ch) = load_u32x4(W + (int64_t)row * PJ_LAT + 8 * ch);
+    }
+    __syncthreads();
+
+    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
+    for (int mt = blockIdx.y; mt < mtiles; mt += gridDim.y) {
+        // A operand rows (clamped inside R; their results are not stored).
+        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
+        const uint16_t* arow = qn + ((int64_t)ra * 64 + h) * PJ_NOPE + 8 * g;
+        bf16x8 a[PJ_NOPE / 32];
+#pragma unroll
+        for (int s = 0; s < PJ_NOPE / 32; s++) a[s] = load_bf16x8(arow + 32 * s);
+        floatx4 acc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < PJ_NOPE / 32; s++) {
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                // Lane (j, g): rows 32 s + 8 g + (j >> 2) (+4), columns
+                // 16 nb + 4 (j & 3) .. +3; it receives column 16 nb + j of
+                // rows 32 s + 8 g .. +7, the same K order as its A operand.
+                const uint8_t* lo = wt + (32 * s + 8 * g + (j >> 2)) * AB_PITCH + 2 * (16 * nb + 4 * (j & 3));
+                const bf16x8 b = lds_read_tr_pair((const uint16_t*)lo, (const uint16_t*)(lo + 4 * AB_PITCH));
+                acc[nb] = mfma_16x16x32(a[s], b, acc[nb]);
+            }
+        }
+        // Lane (j, g) holds C[16 wave + 4 g + v][16 nb + j].
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int r = mt * PJ_TM + 16 * wave + 4 * g + v;
+            if (r < R) {
+                uint16_t* orow = qa + ((int64_t)r * 64 + h) * PJ_ROW + PJ_TN * nt + j;
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) orow[16 * nb] = to_bf16(acc[nb][v]);
+            }
+        }
+        if (nt == 0) {
+            // q_pe passes through: 64 rows x 8 chunks of 16 bytes.
+            for (int i = threadIdx.x; i < PJ_TM * 8; i += 256) {
+                const int r = mt * PJ_TM + (i >> 3), ch = i & 7;
+                if (r < R)
+                    *reinterpret_cast<u32x4*>(qa + ((int64_t)r * 64 + h) * PJ_ROW + PJ_LAT + 8 * ch) =
+                        load_u32x4(qp + ((int64_t)r * 64 + h) * PJ_ROPE + 8 * ch);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict__ o,
+                                                  const uint16_t* __restrict__ kvb, float* __restrict__ out)
+{
+    const int nt = blockIdx.x;  // 64-column tile of the 256 value dims
+    const int h = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
+    __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_TN * VU_PITCH];
+
+    // Stage W_UV,h rows 64 nt .. +64 (all 512 columns): 64 rows x 64 chunks.
+    const uint16_t* W = kvb + ((int64_t)h * PJ_KVB + PJ_NOPE + PJ_TN * nt) * PJ_LAT;
+    for (int i = threadIdx.x; i < PJ_TN * 64; i += 256) {
+        const int row = i >> 6, ch = i & 63;
+        *reinterpret_cast<u32x4*>(wt + row * VU_PITCH + 16 * ch) = load_u32x4(W + (int64_t)row * PJ_LAT + 8 * ch);
+    }
+    __syncthreads();
+
+    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
+    for (int mt = blockIdx.y; mt < mtiles; mt += gridDim.y) {
+        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
+        const float* arow = o + ((int64_t)ra * 64 + h) * PJ_LAT + 8 * g;
+        floatx4 acc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < PJ_LAT / 32; s++) {
+            const float4 x0 = *reinterpret_cast<const float4*>(arow + 32 * s);
+            const float4 x1 = *reinterpret_cast<const float4*>(arow + 32 * s + 4);
+            const bf16x8 a = {(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                              (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                // Lane (j, g): value dim 16 nb + j, latent columns 32 s + 8 g .. +7.
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(wt + (16 * nb + j) * VU_PITCH + 2 * (32 * s + 8 * g)));
+                acc[nb] = mfma_16x16x32(a, b, acc[nb]);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int r = mt * PJ_TM + 16 * wave + 4 * g + v;
+            if (r < R) {
+                float* orow = out + ((int64_t)r * 64 + h) * PJ_VDIM + PJ_TN * nt + j;
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) orow[16 * nb] = acc[nb][v];
+            }
+        }
+    }
+}
+
+// Row-tile groups per (column tile, head): about 2048 workgroups in all, each
+// walking the row tiles of its group (its weight tile is staged once).
+int proj_row_groups(int32_t num_rows, int col_tiles)
+{
+    const int mtiles = (num_rows + PJ_TM - 1) / PJ_TM;
+    int groups = 2048 / (col_tiles * 64);
+    if (groups < 1) groups = 1;
+    return mtiles < groups ? mtiles : groups;
+}
+
+}  // namespace
+
+void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* kvb,
+                           uint16_t* q_abs, hipStream_t stream)
+{
+    const int ct = PJ_LAT / PJ_TN;
+    hipLaunchKernelGGL(absorb_kernel, dim3(ct, proj_row_groups(num_rows, ct), 64), dim3(256), 0, stream, num_rows,
+                       q_nope, q_pe, kvb, q_abs);
+}
+
+void launch_v_up_proj(int32_t num_rows, const float* o, const uint16_t* kvb, float* out, hipStream_t stream)
+{
+    const int ct = PJ_VDIM / PJ_TN;
+    hipLaunchKernelGGL(vup_kernel, dim3(ct, proj_row_groups(num_rows, ct), 64), dim3(256), 0, stream, num_rows, o,
+                       kvb, out);
+}
+
+}  // namespace dsa

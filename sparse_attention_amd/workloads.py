@@ -40,7 +40,8 @@ SOFTMAX_SCALE = float(np.float32(1.0 / math.sqrt(256.0)))
 INDEX_SCALE = 1.0
 W_SCALE = np.float32(32.0 ** -0.5)
 
-T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN = range(8)
+T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN, T_Q_NOPE, T_Q_PE, T_KVB, T_O = range(12)
+KVB_SCALE = np.float32(512.0 ** -0.5)   # kv_b_proj rows ~ N(0, 1/512): unit-variance outputs
 
 
 def rng(seed, tensor_id, seq_id):
@@ -191,6 +192,19 @@ def config(name):
     if name == "c5":
         return ragged(seed=4, name="c5")
     raise KeyError(name)
+
+
+def projection_inputs(R, seed=5):
+    """Synthetic inputs of the two projections around the path, shaped like the
+    model's: q_nope [R,64,192] and q_pe [R,64,64] bf16 N(0,1); the kv_b_proj
+    weight [64,448,512] bf16 N(0,1/512) (rows 0..191 of a head: W_UK, rows
+    192..447: W_UV); an attention latent output o [R,64,512] fp32 N(0,1/4)."""
+    kvb = f32_to_bf16_bits(rng(seed, T_KVB, 0).standard_normal((HEADS, 448, 512), dtype=np.float32) * KVB_SCALE)
+    q_nope = np.stack([normal_bf16(seed, T_Q_NOPE, r, (HEADS, 192)) for r in range(R)])
+    q_pe = np.stack([normal_bf16(seed, T_Q_PE, r, (HEADS, 64)) for r in range(R)])
+    o = np.stack([rng(seed, T_O, r).standard_normal((HEADS, 512), dtype=np.float32) * np.float32(0.5)
+                  for r in range(R)])
+    return dict(q_nope=q_nope, q_pe=q_pe, kv_b=kvb, o=o)
 
 
 def random_scores(seed, R, n, ld=None, kind="normal"):

@@ -158,3 +158,24 @@ def test_attention_and_decode_step_validation(lib):
     assert g(ws_bytes=need - 256) == WS_SMALL
     if not HAS_GPU:
         assert g() == NO_DEVICE
+
+
+def test_projection_validation(lib):
+    f = lambda **kw: lib.dsa_absorb_queries(kw.get("R", 4), kw.get("qn", 0x1000), kw.get("qp", 0x2000),
+                                            kw.get("w", 0x3000), kw.get("qa", 0x4000), None)
+    assert f(R=0) == INVALID
+    assert f(R=(1 << 24) + 1) == INVALID
+    assert f(qn=0) == INVALID
+    assert f(qp=0x2008) == MISALIGNED
+    assert f(w=0) == INVALID
+    assert f(qa=0x4002) == MISALIGNED
+    if not HAS_GPU:
+        assert f() == NO_DEVICE
+    g = lambda **kw: lib.dsa_v_up_proj(kw.get("R", 4), kw.get("o", 0x1000), kw.get("w", 0x3000),
+                                       kw.get("out", 0x4000), None)
+    assert g(R=-1) == INVALID
+    assert g(o=0x1004) == MISALIGNED
+    assert g(w=0x3008) == MISALIGNED
+    assert g(out=0) == INVALID
+    if not HAS_GPU:
+        assert g() == NO_DEVICE

@@ -424,3 +424,49 @@ def test_decode_step_deterministic(dsa):
     b = run_decode_step(dsa, x, d=d)
     for u, v in zip(a, b):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+# ----------------------------------------------------------------------------- projections
+
+U32 = 2.0 ** -24  # fp32 unit roundoff
+
+
+@pytest.mark.parametrize("R", [1, 5, 64, 130, 1024])
+def test_absorb_queries_against_oracle(dsa, oracle_mod, R):
+    """q_abs = [W_UK^T q_nope || q_pe]: the 512 absorbed columns within the
+    error of fp32 accumulation over 192 products plus one bf16 rounding
+    (at most 2^-8 |ref|: half an ulp of an 8-bit significand); the RoPE
+    part copied bit for bit.  R = 5, 130 leave ragged row tiles; R = 1024 makes
+    each workgroup walk several row tiles."""
+    x = wl.projection_inputs(R, seed=5 + R)
+    qa = torch.empty((R, 64, 576), dtype=torch.bfloat16, device=DEV)
+    dsa.dsa_absorb_queries(dev_bf16(x["q_nope"]), dev_bf16(x["q_pe"]), dev_bf16(x["kv_b"]), qa)
+    torch.cuda.synchronize()
+    got_bits = qa.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle_mod.absorb_queries(x["q_nope"], x["q_pe"], x["kv_b"])
+    got = wl.bf16_bits_to_f32(got_bits).astype(np.float64)
+    W = np.abs(wl.bf16_bits_to_f32(x["kv_b"][:, :192, :]).astype(np.float64))          # [64,192,512]
+    qn = np.abs(wl.bf16_bits_to_f32(x["q_nope"]).astype(np.float64))                   # [R,64,192]
+    mag = np.matmul(qn.transpose(1, 0, 2), W).transpose(1, 0, 2)                        # sum of |terms|
+    bound = 2.0 ** -8 * np.abs(ref[:, :, :512]) + 192 * U32 * mag * 1.01
+    assert np.all(np.abs(got[:, :, :512] - ref[:, :, :512]) <= bound)
+    assert np.array_equal(got_bits[:, :, 512:], x["q_pe"])
+    # and (up to accumulation-order flips at rounding ties) the bf16 rounding of the fp64 result
+    same = got_bits[:, :, :512] == wl.f32_to_bf16_bits(ref[:, :, :512].astype(np.float32))
+    assert same.mean() >= 0.999
+
+
+@pytest.mark.parametrize("R", [1, 5, 64, 130, 1024])
+def test_v_up_proj_against_oracle(dsa, oracle_mod, R):
+    """out = W_UV bf16(o): within the fp32 accumulation bound over 512
+    products, element by element (o rounded to bf16 the same way on both
+    sides: round-to-nearest-even)."""
+    x = wl.projection_inputs(R, seed=50 + R)
+    out = torch.empty((R, 64, 256), dtype=torch.float32, device=DEV)
+    dsa.dsa_v_up_proj(dev(x["o"]), dev_bf16(x["kv_b"]), out)
+    torch.cuda.synchronize()
+    ob = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(x["o"])).astype(np.float64)
+    ref = oracle_mod.v_up_proj(ob, x["kv_b"])
+    W = np.abs(wl.bf16_bits_to_f32(x["kv_b"][:, 192:, :]).astype(np.float64))          # [64,256,512]
+    mag = np.matmul(np.abs(ob).transpose(1, 0, 2), W.transpose(0, 2, 1)).transpose(1, 0, 2)
+    assert np.all(np.abs(out.cpu().numpy() - ref) <= 512 * U32 * mag * 1.01 + 1e-30)
