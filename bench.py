@@ -28,6 +28,7 @@ sys.path.insert(0, REPO)
 
 METRIC = "DSA decode tokens/s (indexer+top2048+sparse MLA) & % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 matrix-core peak, TFLOP/s
 K_TOP = 2048
 
 
@@ -201,6 +202,45 @@ def main():
     achieved = alg_bytes / (ms_idx * 1e-3) / 1e9
     log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
 
+    # The projections on either side of the path (query absorption before it,
+    # V up-projection after it), timed alone at this workload's row count
+    # (at most 8192 rows), with synthetic kv_b_proj weights.
+    Rp = min(R, 8192)
+    px = wl.projection_inputs(Rp)
+    qn, qp, kvb = bf(px["q_nope"]), bf(px["q_pe"]), bf(px["kv_b"])
+    o_lat = torch.from_numpy(px["o"]).to(dev)
+    qa_p = torch.empty((Rp, 64, 576), dtype=torch.bfloat16, device=dev)
+    up = torch.empty((Rp, 64, 256), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_ab = timed(lambda: dsa.dsa_absorb_queries(qn, qp, kvb, qa_p, stream=stream))
+    ms_up = timed(lambda: dsa.dsa_v_up_proj(o_lat, kvb, up, stream=stream))
+    ab_bytes = 64 * 192 * 512 * 2 + Rp * 64 * (192 + 64 + 576) * 2
+    up_bytes = 64 * 256 * 512 * 2 + Rp * 64 * (512 * 4 + 256 * 4)
+    ab_flops = 2 * Rp * 64 * 192 * 512
+    up_flops = 2 * Rp * 64 * 512 * 256
+
+    def proj_entry(ms, nbytes, flops):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tfs = flops / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "gbs": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "tflops": round(tfs, 2),
+                "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+
+    projections = {"rows": Rp, "absorb_queries": proj_entry(ms_ab, ab_bytes, ab_flops),
+                   "v_up_proj": proj_entry(ms_up, up_bytes, up_flops)}
+    log(f"[bench] absorb_queries: {ms_ab * 1e3:.1f} us, v_up_proj: {ms_up * 1e3:.1f} us ({Rp} rows)")
+
     # Step-level algorithmic bytes (whole path) for context.
     step_bytes = int(np.sum(256 * n + 1152 * np.minimum(n, K_TOP) + 82048 + 139264))
     traffic = traffic_from_profiles("indexer", w.name, src_hash(["indexer.hip", "dsa_device.h"]))
@@ -232,6 +272,7 @@ def main():
                      "kernel": "indexer_rows_kernel", "kernel_us": round(ms_idx * 1e3, 2),
                      "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
+        "projections": projections,
         "step_alg_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }

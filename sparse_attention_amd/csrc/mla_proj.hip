@@ -49,36 +49,72 @@ __device__ __forceinline__ uint16_t to_bf16(float x)
     return __builtin_bit_cast(uint16_t, (__bf16)x);  // round-to-nearest-even
 }
 
+// Workgroup -> (column tile, head, row group).  Workgroups are handed to the
+// 8 XCDs round-robin, and the NT column tiles of one (head, row group) read
+// the same A rows: numbering them 8 apart puts them on one XCD, where its L2
+// serves A to all of them (only locality depends on this, not correctness).
+struct ProjTile {
+    int nt, h, grp;
+};
+template <int NT>
+__device__ __forceinline__ ProjTile proj_tile()
+{
+    const int L = blockIdx.x;
+    const int c = L & 7, b = (L >> 3) % NT, a = L / (8 * NT);
+    const int p = 8 * a + c;  // (head, row group) pair
+    return ProjTile{b, p & 63, p >> 6};
+}
+
 __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __restrict__ qn,
                                                      const uint16_t* __restrict__ qp,
                                                      const uint16_t* __restrict__ kvb, uint16_t* __restrict__ qa)
 {
-    const int nt = blockIdx.x;  // 64-column tile of the 512 latent columns
-    const int h = blockIdx.z;
+    const ProjTile tile = proj_tile<PJ_LAT / PJ_TN>();
+    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_LAT / PJ_TN));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
     __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_NOPE * AB_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t ct[4][16][PJ_TN + 8];  // output staging, per wave
+    constexpr int KS = PJ_NOPE / 32;  // k-steps
 
-    // Stage W_UK,h[0:192][64 nt .. +64]: 192 rows x 8 chunks of 16 bytes.
+    // A operand of row tile mt: lane (j, g) holds q_nope[row][32 s + 8 g .. +8]
+    // (rows clamped inside R; their results are not stored).
+    auto load_a = [&](int mt, bf16x8 (&a)[KS]) {
+        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
+        const uint16_t* arow = qn + ((int64_t)ra * 64 + h) * PJ_NOPE + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; s++) a[s] = load_bf16x8(arow + 32 * s);
+    };
+
+    // Every global load of the prologue goes out before the one barrier:
+    // W_UK,h[0:192][64 nt .. +64] (192 rows x 8 chunks of 16 bytes) and the
+    // first row tile's A operand.
     const uint16_t* W = kvb + (int64_t)h * PJ_KVB * PJ_LAT + PJ_TN * nt;
-    for (int i = threadIdx.x; i < PJ_NOPE * 8; i += 256) {
-        const int row = i >> 3, ch = i & 7;
-        *reinterpret_cast<u32x4*>(wt + row * AB_PITCH + 16 * ch) = load_u32x4(W + (int64_t)row * PJ_LAT + 8 * ch);
+    u32x4 wreg[PJ_NOPE * 8 / 256];
+#pragma unroll
+    for (int i = 0; i < PJ_NOPE * 8 / 256; i++) {
+        const int c = threadIdx.x + 256 * i;
+        wreg[i] = load_u32x4(W + (int64_t)(c >> 3) * PJ_LAT + 8 * (c & 7));
+    }
+    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
+    bf16x8 a[KS];
+    load_a(grp, a);
+#pragma unroll
+    for (int i = 0; i < PJ_NOPE * 8 / 256; i++) {
+        const int c = threadIdx.x + 256 * i;
+        *reinterpret_cast<u32x4*>(wt + (c >> 3) * AB_PITCH + 16 * (c & 7)) = wreg[i];
     }
     __syncthreads();
 
-    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
-    for (int mt = blockIdx.y; mt < mtiles; mt += gridDim.y) {
-        // A operand rows (clamped inside R; their results are not stored).
-        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
-        const uint16_t* arow = qn + ((int64_t)ra * 64 + h) * PJ_NOPE + 8 * g;
-        bf16x8 a[PJ_NOPE / 32];
-#pragma unroll
-        for (int s = 0; s < PJ_NOPE / 32; s++) a[s] = load_bf16x8(arow + 32 * s);
+    for (int mt = grp; mt < mtiles; mt += ngrp) {
+        // The next row tile's A goes out before this tile's MFMAs.
+        const bool more = mt + ngrp < mtiles;  // uniform
+        bf16x8 an[KS];
+        if (more) load_a(mt + ngrp, an);
         floatx4 acc[4];
 #pragma unroll
         for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < PJ_NOPE / 32; s++) {
+        for (int s = 0; s < KS; s++) {
 #pragma unroll
             for (int nb = 0; nb < 4; nb++) {
                 // Lane (j, g): rows 32 s + 8 g + (j >> 2) (+4), columns
@@ -89,15 +125,19 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
                 acc[nb] = mfma_16x16x32(a[s], b, acc[nb]);
             }
         }
-        // Lane (j, g) holds C[16 wave + 4 g + v][16 nb + j].
+        // Lane (j, g) holds C[16 wave + 4 g + v][16 nb + j]; the wave's 16 rows
+        // go through its own staging rows (only this wave touches them, and
+        // LDS keeps one wave's accesses in order) and leave as 16-byte stores.
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int r = mt * PJ_TM + 16 * wave + 4 * g + v;
-            if (r < R) {
-                uint16_t* orow = qa + ((int64_t)r * 64 + h) * PJ_ROW + PJ_TN * nt + j;
+        for (int v = 0; v < 4; v++)
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) orow[16 * nb] = to_bf16(acc[nb][v]);
-            }
+            for (int nb = 0; nb < 4; nb++) ct[wave][4 * g + v][16 * nb + j] = to_bf16(acc[nb][v]);
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int rr = 8 * i + (lane >> 3), ch = lane & 7;  // row of the wave's 16, 16-byte chunk
+            const int r = mt * PJ_TM + 16 * wave + rr;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(&ct[wave][rr][8 * ch]);
+            if (r < R) *reinterpret_cast<u32x4*>(qa + ((int64_t)r * 64 + h) * PJ_ROW + PJ_TN * nt + 8 * ch) = val;
         }
         if (nt == 0) {
             // q_pe passes through: 64 rows x 8 chunks of 16 bytes.
@@ -108,46 +148,77 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
                         load_u32x4(qp + ((int64_t)r * 64 + h) * PJ_ROPE + 8 * ch);
             }
         }
+        if (more) {
+#pragma unroll
+            for (int s = 0; s < KS; s++) a[s] = an[s];
+        }
     }
 }
 
 __global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict__ o,
                                                   const uint16_t* __restrict__ kvb, float* __restrict__ out)
 {
-    const int nt = blockIdx.x;  // 64-column tile of the 256 value dims
-    const int h = blockIdx.z;
+    const ProjTile tile = proj_tile<PJ_VDIM / PJ_TN>();
+    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_VDIM / PJ_TN));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
     __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_TN * VU_PITCH];
+    constexpr int KS = PJ_LAT / 32;  // k-steps
 
-    // Stage W_UV,h rows 64 nt .. +64 (all 512 columns): 64 rows x 64 chunks.
+    // A operand of row tile mt, rounded to bf16 as it arrives: lane (j, g)
+    // holds bf16(o[row][32 s + 8 g .. +8]).
+    auto load_a = [&](int mt, bf16x8 (&a)[KS]) {
+        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
+        const float* arow = o + ((int64_t)ra * 64 + h) * PJ_LAT + 8 * g;
+        float4 x[2 * KS];
+#pragma unroll
+        for (int s = 0; s < KS; s++) {
+            x[2 * s] = *reinterpret_cast<const float4*>(arow + 32 * s);
+            x[2 * s + 1] = *reinterpret_cast<const float4*>(arow + 32 * s + 4);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; s++) {
+            const float4 x0 = x[2 * s], x1 = x[2 * s + 1];
+            a[s] = bf16x8{(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                          (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+        }
+    };
+
+    // Prologue loads before the one barrier: W_UV,h rows 64 nt .. +64 (all
+    // 512 columns, 64 rows x 64 chunks of 16 bytes), then the first row tile.
     const uint16_t* W = kvb + ((int64_t)h * PJ_KVB + PJ_NOPE + PJ_TN * nt) * PJ_LAT;
-    for (int i = threadIdx.x; i < PJ_TN * 64; i += 256) {
-        const int row = i >> 6, ch = i & 63;
-        *reinterpret_cast<u32x4*>(wt + row * VU_PITCH + 16 * ch) = load_u32x4(W + (int64_t)row * PJ_LAT + 8 * ch);
+    u32x4 wreg[PJ_TN * 64 / 256];
+#pragma unroll
+    for (int i = 0; i < PJ_TN * 64 / 256; i++) {
+        const int c = threadIdx.x + 256 * i;
+        wreg[i] = load_u32x4(W + (int64_t)(c >> 6) * PJ_LAT + 8 * (c & 63));
+    }
+    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
+    bf16x8 a[KS];
+    load_a(grp, a);
+#pragma unroll
+    for (int i = 0; i < PJ_TN * 64 / 256; i++) {
+        const int c = threadIdx.x + 256 * i;
+        *reinterpret_cast<u32x4*>(wt + (c >> 6) * VU_PITCH + 16 * (c & 63)) = wreg[i];
     }
     __syncthreads();
 
-    const int mtiles = (R + PJ_TM - 1) / PJ_TM;
-    for (int mt = blockIdx.y; mt < mtiles; mt += gridDim.y) {
-        const int ra = min(mt * PJ_TM + 16 * wave + j, R - 1);
-        const float* arow = o + ((int64_t)ra * 64 + h) * PJ_LAT + 8 * g;
+    for (int mt = grp; mt < mtiles; mt += ngrp) {
+        const bool more = mt + ngrp < mtiles;  // uniform
         floatx4 acc[4];
 #pragma unroll
         for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < PJ_LAT / 32; s++) {
-            const float4 x0 = *reinterpret_cast<const float4*>(arow + 32 * s);
-            const float4 x1 = *reinterpret_cast<const float4*>(arow + 32 * s + 4);
-            const bf16x8 a = {(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
-                              (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+        for (int s = 0; s < KS; s++) {
 #pragma unroll
             for (int nb = 0; nb < 4; nb++) {
                 // Lane (j, g): value dim 16 nb + j, latent columns 32 s + 8 g .. +7.
                 const bf16x8 b = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(wt + (16 * nb + j) * VU_PITCH + 2 * (32 * s + 8 * g)));
-                acc[nb] = mfma_16x16x32(a, b, acc[nb]);
+                acc[nb] = mfma_16x16x32(a[s], b, acc[nb]);
             }
         }
+        // The next row tile's A goes out once this tile's MFMAs have read theirs.
+        if (more) load_a(mt + ngrp, a);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
             const int r = mt * PJ_TM + 16 * wave + 4 * g + v;
@@ -176,14 +247,14 @@ void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint1
                            uint16_t* q_abs, hipStream_t stream)
 {
     const int ct = PJ_LAT / PJ_TN;
-    hipLaunchKernelGGL(absorb_kernel, dim3(ct, proj_row_groups(num_rows, ct), 64), dim3(256), 0, stream, num_rows,
+    hipLaunchKernelGGL(absorb_kernel, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream, num_rows,
                        q_nope, q_pe, kvb, q_abs);
 }
 
 void launch_v_up_proj(int32_t num_rows, const float* o, const uint16_t* kvb, float* out, hipStream_t stream)
 {
     const int ct = PJ_VDIM / PJ_TN;
-    hipLaunchKernelGGL(vup_kernel, dim3(ct, proj_row_groups(num_rows, ct), 64), dim3(256), 0, stream, num_rows, o,
+    hipLaunchKernelGGL(vup_kernel, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream, num_rows, o,
                        kvb, out);
 }
 
