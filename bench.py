@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--config", default="c3", help="workload: c1 | c3 | c4 | c5")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (oracle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-index-share", dest="index_share", action="store_false",
+                   help="skip timing a 4-layer IndexShare group (1 full + 3 shared layers)")
     p.add_argument("--mode", default="decode", choices=["decode", "copy"],
                    help="copy: a plain device-to-device copy of --copy-mib MiB, repeated --steps times, to "
                         "calibrate HBM byte counters against a kernel of known traffic")
@@ -202,6 +204,45 @@ def main():
     achieved = alg_bytes / (ms_idx * 1e-3) / 1e9
     log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
 
+    # IndexShare: a 4-layer group in which one "full" layer runs the whole path
+    # and three "shared" layers reuse its top-2048 list for their attention
+    # (each with its own absorbed queries and latent cache).  Decode configs only.
+    share = None
+    if args.index_share and R <= 1024:
+        n_shared = 3
+        # Each shared layer's queries and latent cache: N(0,1) in bf16, drawn on
+        # the device (only timed here; parity of this composition is a test).
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1000)
+        extra = [(torch.randn(q_abs.shape, generator=gen, device=dev).to(torch.bfloat16),
+                  torch.randn(kv.shape, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(n_shared)]
+        ws_a = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, K_TOP), dev)
+        out_s = torch.empty_like(out)
+        lse_s = torch.empty_like(lse)
+
+        def group():
+            step()
+            for qa_l, kv_l in extra:
+                dsa.dsa_sparse_mla_attn(rows, qa_l, kv_l, idx, K_TOP, wl.SOFTMAX_SCALE, out_s, lse_s, ws_a,
+                                        stream=stream)
+
+        for _ in range(args.warmup):
+            group()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            group()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_group = e0.elapsed_time(e1) / args.steps
+        share = {"layers_per_group": 1 + n_shared, "us_per_group": round(ms_group * 1e3, 2),
+                 "tokens_per_s_per_group": round(R / (ms_group * 1e-3), 1),
+                 "us_per_layer": round(ms_group * 1e3 / (1 + n_shared), 2),
+                 "us_if_every_layer_ran_the_indexer": round(ms_step * 1e3 * (1 + n_shared), 2)}
+        log(f"[bench] IndexShare group (1 full + {n_shared} shared layers): {ms_group * 1e3:.1f} us, "
+            f"{R / (ms_group * 1e-3):.0f} tokens/s per group")
+        del extra
+
     # The projections on either side of the path (query absorption before it,
     # V up-projection after it), timed alone at this workload's row count
     # (at most 8192 rows), with synthetic kv_b_proj weights.
@@ -273,6 +314,7 @@ def main():
                      "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "projections": projections,
+        "index_share": share,
         "step_alg_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }

@@ -222,6 +222,30 @@ DSA_API dsa_status_t dsa_absorb_queries(int32_t num_rows, const void* q_nope, co
 DSA_API dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* kv_b_weight,
                                    float* out, void* hip_stream);
 
+/* ---- IndexShare: one selection serving several layers ------------------
+ *
+ * Only "full" layers run the indexer and the top-k; a "shared" layer has no
+ * indexer (and no index-key cache) and attends over the index list of the
+ * latest full layer below it ("GLM-5.2 架构 QA" CH2 Q2.1 and Q2.2; the layer
+ * pattern is CH1 Q1.2 and CH2 Q2.4).  With this library a full layer calls
+ * dsa_decode_step, which writes `indices`; each shared layer after it calls
+ * dsa_sparse_mla_attn with its own q_abs and kv_latent and that same
+ * `indices` buffer, which nothing in between may overwrite.  Attention reads
+ * the indices only, so the buffer is the model's shared top-k cache as is.
+ */
+
+/* The layer whose selection `layer` attends over: `layer` itself when it is
+ * a full layer, else the latest full layer below it.  The first
+ * `leading_full` layers are full; above them the layers repeat with period
+ * `freq`, each period being freq - 1 shared layers followed by one full
+ * layer.  num_layers = 78, leading_full = 3, freq = 4 gives the GLM-5.2
+ * pattern: layers 0, 1, 2, 6, 10, ..., 74 full (21 of 78), layers 3..5
+ * reuse layer 2, layers 75..77 reuse layer 74.  freq = 1 makes every layer
+ * full.  Host arithmetic only (no device needed).  Returns -1 when
+ * num_layers < 1, layer is outside [0, num_layers), leading_full < 1 or
+ * freq < 1. */
+DSA_API int32_t dsa_index_share_source(int32_t layer, int32_t num_layers, int32_t leading_full, int32_t freq);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,5 +128,34 @@ def decode_step(visible_len, row_cache_base, q_idx, w, k_idx, q_abs, kv_latent, 
     return s64, s32, idx, out, lse
 
 
+# The 78-entry indexer_types array of GLM-5.2 as "GLM-5.2 架构 QA" CH1 Q1.2
+# spells it out: a cold-start block of 3 full then 3 shared layers, then 18
+# periods of one full layer followed by 3 shared ones.
+GLM52_INDEXER_TYPES = ["full"] * 3 + ["shared"] * 3 + (["full"] + ["shared"] * 3) * 18
+
+
+def index_share_layers(types, layers, visible_len, row_cache_base, k, index_scale, softmax_scale):
+    """IndexShare over consecutive layers ("GLM-5.2 架构 QA" CH2 Q2.1, Q2.2):
+    a "full" layer runs the whole path on its own indexer inputs and its list
+    becomes the shared one; a "shared" layer runs attention alone over the
+    latest full layer's list.  `layers[i]` holds layer i's q_abs and kv_latent
+    (and q_idx, w, k_idx for a full layer).  Returns, per layer, (idx, out,
+    lse) with idx the list the layer attended over."""
+    shared_idx = None
+    res = []
+    for kind, x in zip(types, layers):
+        if kind == "full":
+            _, _, shared_idx, out, lse = decode_step(visible_len, row_cache_base, x["q_idx"], x["w"], x["k_idx"],
+                                                     x["q_abs"], x["kv_latent"], k, index_scale, softmax_scale)
+        elif kind == "shared":
+            if shared_idx is None:
+                raise ValueError("a shared layer needs a full layer before it")
+            out, lse = sparse_mla(row_cache_base, x["q_abs"], x["kv_latent"], shared_idx, softmax_scale)
+        else:
+            raise ValueError(kind)
+        res.append((shared_idx, out, lse))
+    return res
+
+
 def version():
     return _lib().oracle_version().decode()

@@ -18,7 +18,8 @@ __all__ = [
     "DsaError", "Rows", "library_path", "load_library", "dsa_version", "exported_symbols",
     "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk_select",
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn",
-    "dsa_decode_step_workspace_size", "dsa_decode_step", "workspace",
+    "dsa_decode_step_workspace_size", "dsa_decode_step", "workspace", "dsa_absorb_queries", "dsa_v_up_proj",
+    "dsa_index_share_source",
     "INDEX_HEADS", "INDEX_DIM", "HEADS", "LATENT_DIM", "ROPE_DIM", "ROW_DIM", "TOPK_MAX",
     "ROWS_DISTINCT_SEQUENCES",
 ]
@@ -86,6 +87,7 @@ def load_library():
         "dsa_decode_step": ([rows_p, P, P, P, f32, P, P, f32, i32, P, P, P, P, sz, P], ctypes.c_int),
         "dsa_absorb_queries": ([i32, P, P, P, P, P], ctypes.c_int),
         "dsa_v_up_proj": ([i32, P, P, P, P], ctypes.c_int),
+        "dsa_index_share_source": ([i32, i32, i32, i32], i32),
     }
     for name, (argtypes, restype) in sigs.items():
         fn = getattr(lib, name)
@@ -101,7 +103,7 @@ def exported_symbols():
         "dsa_version", "dsa_status_string", "dsa_last_error_detail", "dsa_indexer_scores",
         "dsa_topk_workspace_size", "dsa_topk_select", "dsa_sparse_mla_workspace_size",
         "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step", "dsa_absorb_queries",
-        "dsa_v_up_proj",
+        "dsa_v_up_proj", "dsa_index_share_source",
     ]
 
 
@@ -239,3 +241,12 @@ def dsa_v_up_proj(o_latent, kv_b_weight, out, stream=None):
     _check(lib.dsa_v_up_proj(R, _ptr(o_latent, "o_latent", (torch.float32,)),
                              _ptr(kv_b_weight, "kv_b_weight", _BF16), _ptr(out, "out", (torch.float32,)),
                              _stream(stream, out)))
+
+
+def dsa_index_share_source(layer, num_layers=78, leading_full=3, freq=4):
+    """The layer whose top-k selection `layer` attends over (itself for a full
+    layer); raises on arguments the C call rejects."""
+    src = load_library().dsa_index_share_source(int(layer), int(num_layers), int(leading_full), int(freq))
+    if src < 0:
+        raise DsaError(1, f"dsa_index_share_source({layer}, {num_layers}, {leading_full}, {freq}): bad arguments")
+    return int(src)

@@ -321,4 +321,12 @@ dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* 
     return after_launch(st, "v_up_proj");
 }
 
+int32_t dsa_index_share_source(int32_t layer, int32_t num_layers, int32_t leading_full, int32_t freq)
+{
+    if (num_layers < 1 || layer < 0 || layer >= num_layers || leading_full < 1 || freq < 1) return -1;
+    if (layer < leading_full) return layer;
+    const int32_t pos = (layer - leading_full) % freq;  // 0 .. freq-2 shared, freq-1 full
+    return pos == freq - 1 ? layer : layer - pos - 1;
+}
+
 }  // extern "C"

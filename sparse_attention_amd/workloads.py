@@ -40,7 +40,7 @@ SOFTMAX_SCALE = float(np.float32(1.0 / math.sqrt(256.0)))
 INDEX_SCALE = 1.0
 W_SCALE = np.float32(32.0 ** -0.5)
 
-T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN, T_Q_NOPE, T_Q_PE, T_KVB, T_O = range(12)
+T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN, T_Q_NOPE, T_Q_PE, T_KVB, T_O, T_LAYER = range(13)
 KVB_SCALE = np.float32(512.0 ** -0.5)   # kv_b_proj rows ~ N(0, 1/512): unit-variance outputs
 
 
@@ -192,6 +192,18 @@ def config(name):
     if name == "c5":
         return ragged(seed=4, name="c5")
     raise KeyError(name)
+
+
+def layer_stack(lengths, num_layers, seed=6):
+    """Inputs of `num_layers` consecutive layers over the same decode batch
+    (one row per sequence of the given lengths): layer l is a decode workload
+    whose seed is drawn from SeedSequence(seed, spawn_key=(T_LAYER, l)), so
+    every layer has its own queries, index keys and latent cache."""
+    out = []
+    for l in range(num_layers):
+        s_l = int(np.random.SeedSequence(seed, spawn_key=(T_LAYER, l)).generate_state(1)[0])
+        out.append(_decode(f"layer{l}", s_l, lengths, f"layer {l}").generate())
+    return out
 
 
 def projection_inputs(R, seed=5):

@@ -179,3 +179,40 @@ def test_projection_validation(lib):
     assert g(out=0) == INVALID
     if not HAS_GPU:
         assert g() == NO_DEVICE
+
+
+def test_index_share_source_matches_printed_layer_pattern(lib, oracle_mod):
+    """The native layer schedule against the pattern the pages print
+    (tests/golden/index_share_layers.json) and against the oracle's spelled-out
+    indexer_types array, for all 78 layers."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "index_share_layers.json")) as fh:
+        g = json.load(fh)
+    L, freq = g["num_layers"], g["index_topk_freq"]
+    src = [lib.dsa_index_share_source(l, L, 3, freq) for l in range(L)]
+    for a, b, kind, source in g["rows"]:
+        for l in range(a, b + 1):
+            assert src[l] == source, l
+            assert (src[l] == l) == (kind == "full"), l
+    assert sum(s == l for l, s in enumerate(src)) == g["full_layers"]
+    assert sum(s != l for l, s in enumerate(src)) == g["shared_layers"]
+    types = ["full" if s == l else "shared" for l, s in enumerate(src)]
+    assert types == oracle_mod.GLM52_INDEXER_TYPES
+    # every shared layer points at the latest full layer below it
+    for l in range(L):
+        fulls = [j for j in range(l + 1) if types[j] == "full"]
+        assert src[l] == fulls[-1]
+    assert m.dsa_index_share_source(77) == 74
+
+
+def test_index_share_source_validation_and_other_periods(lib):
+    f = lib.dsa_index_share_source
+    assert f(-1, 78, 3, 4) == -1
+    assert f(78, 78, 3, 4) == -1
+    assert f(0, 0, 3, 4) == -1
+    assert f(5, 78, 0, 4) == -1
+    assert f(5, 78, 3, 0) == -1
+    assert [f(l, 10, 1, 1) for l in range(10)] == list(range(10))        # freq 1: no sharing
+    assert [f(l, 8, 1, 2) for l in range(8)] == [0, 0, 2, 2, 4, 4, 6, 6]  # one full, one shared
+    with pytest.raises(m.DsaError):
+        m.dsa_index_share_source(78)

@@ -426,6 +426,59 @@ def test_decode_step_deterministic(dsa):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+# ----------------------------------------------------------------------------- IndexShare
+
+def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):
+    """Layers 0..9 of the GLM-5.2 pattern (3 full, 3 shared, 1 full, 3 shared;
+    the schedule comes from dsa_index_share_source) over a decode batch with
+    rows longer than, equal to and shorter than k.  Full layers run
+    dsa_decode_step into one shared index buffer; shared layers run
+    dsa_sparse_mla_attn on that buffer with their own queries and cache.
+    Checks: the buffer is untouched by shared layers; each full layer's list
+    against the oracle's selection (recall, near-threshold swaps only); every
+    layer's attention against the oracle on the list it used, and against the
+    oracle's whole IndexShare composition for rows whose lists agree."""
+    lengths = [5000, 2048, 3001, 700]
+    L = 10
+    layers = wl.layer_stack(lengths, L, seed=6)
+    vis, base = layers[0]["visible_len"], layers[0]["row_cache_base"]
+    R, k = len(vis), 2048
+    types = ["full" if dsa.dsa_index_share_source(l) == l else "shared" for l in range(L)]
+    assert types == oracle_mod.GLM52_INDEXER_TYPES[:L]
+    rows = make_rows(dsa, vis, base)
+    idx = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, int(vis.max()), k), DEV)
+    ws_a = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, k), DEV)
+    got = []
+    for l, x in enumerate(layers):
+        d = device_inputs(x)
+        out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+        if types[l] == "full":
+            dsa.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], wl.INDEX_SCALE, d["q_abs"], d["kv_latent"],
+                                wl.SOFTMAX_SCALE, k, idx, out, lse, ws)
+            torch.cuda.synchronize()
+            snap = idx.clone()
+        else:
+            dsa.dsa_sparse_mla_attn(rows, d["q_abs"], d["kv_latent"], idx, k, wl.SOFTMAX_SCALE, out, lse, ws_a)
+            torch.cuda.synchronize()
+            assert torch.equal(idx, snap), l
+        got.append((snap.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()))
+    ref = oracle_mod.index_share_layers(types, layers, vis, base, k, wl.INDEX_SCALE, wl.SOFTMAX_SCALE)
+    for l in range(L):
+        idx_g, out_g, lse_g = got[l]
+        idx_r, out_r, lse_r = ref[l]
+        x = layers[l]
+        if types[l] == "full":
+            s64 = oracle_mod.indexer_scores(vis, base, x["q_idx"], x["w"], x["k_idx"], wl.INDEX_SCALE)
+            assert recall_check(idx_g, idx_r, s64, vis) >= 0.999, l
+        on_own = oracle_mod.sparse_mla(base, x["q_abs"], x["kv_latent"], idx_g, wl.SOFTMAX_SCALE)
+        check_attention(out_g, lse_g, on_own[0], on_own[1], f"layer {l} ({types[l]})")
+        same = [r for r in range(R) if np.array_equal(idx_g[r], idx_r[r])]
+        assert len(same) >= R - 1, (l, same)
+        check_attention(out_g[same], lse_g[same], out_r[same], lse_r[same], f"layer {l} vs oracle composition")
+
+
 # ----------------------------------------------------------------------------- projections
 
 U32 = 2.0 ** -24  # fp32 unit roundoff

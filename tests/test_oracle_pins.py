@@ -346,6 +346,63 @@ def test_dsa_equals_dense_causal_attention_when_at_most_k_visible(oracle_mod):
     np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- IndexShare
+
+def test_index_share_types_match_printed_layer_pattern(oracle_mod):
+    with open(os.path.join(os.path.dirname(__file__), "golden", "index_share_layers.json")) as fh:
+        g = json.load(fh)
+    t = oracle_mod.GLM52_INDEXER_TYPES
+    assert len(t) == g["num_layers"]
+    assert t.count("full") == g["full_layers"] and t.count("shared") == g["shared_layers"]
+    for a, b, kind, _ in g["rows"]:
+        assert t[a:b + 1] == [kind] * (b - a + 1)
+    # after the cold-start block, exactly one full layer in every index_topk_freq layers
+    freq = g["index_topk_freq"]
+    for p in range(3, g["num_layers"] - freq + 1, freq):
+        assert t[p:p + freq].count("full") == 1
+
+
+def test_index_share_shared_layers_use_latest_full_list(oracle_mod):
+    """Five layers full, shared, shared, full, shared over one row of 64
+    positions with k = 8.  Index key column 0 is chosen per layer so that the
+    first full layer's indexer picks positions 56..63, the second 0..7, and a
+    (wrongly consulted) shared layer's own indexer inputs 28..35.  Queries are
+    zero, so attention averages the selected latent rows, whose column 0 holds
+    the position: out[..., 0] is the mean position of the list a layer used
+    (59.5, 3.5, 31.5) and every other column is 0.  Reusing the previous
+    layer's list happens to agree here, but reusing the first list throughout,
+    or selecting afresh in a shared layer, fails."""
+    T, k = 64, 8
+    t = np.arange(T, dtype=np.float32)
+    one = wl.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+
+    def layer(order):
+        q_idx = np.zeros((1, 32, 128), np.uint16)
+        q_idx[0, 0, 0] = one
+        w = np.zeros((1, 32), np.float32)
+        w[0, 0] = 1.0
+        k_idx = np.zeros((T, 128), np.uint16)
+        k_idx[:, 0] = wl.f32_to_bf16_bits(order)
+        kv = np.zeros((T, 576), np.uint16)
+        kv[:, 0] = wl.f32_to_bf16_bits(t)
+        return dict(q_idx=q_idx, w=w, k_idx=k_idx, q_abs=np.zeros((1, 64, 576), np.uint16), kv_latent=kv)
+
+    top, bottom, middle = t + 1, T - t, T - np.abs(t - 32)
+    layers = [layer(top), layer(middle), layer(middle), layer(bottom), layer(middle)]
+    types = ["full", "shared", "shared", "full", "shared"]
+    res = oracle_mod.index_share_layers(types, layers, np.array([T], np.int32), np.zeros(1, np.int64), k, 1.0,
+                                        1 / 16)
+    for (idx, out, lse), mean, first in zip(res, [59.5, 59.5, 59.5, 3.5, 3.5], [56, 56, 56, 0, 0]):
+        assert np.array_equal(idx[0], np.arange(first, first + k))
+        assert np.all(out[0, :, 0] == mean) and not np.any(out[0, :, 1:])
+        np.testing.assert_allclose(lse[0], np.log(k), rtol=1e-15)
+    assert oracle_mod.topk(np.array([T], np.int32), middle[None].astype(np.float32), k)[0].tolist() == \
+        list(range(28, 36))
+    with pytest.raises(ValueError):
+        oracle_mod.index_share_layers(["shared"], layers[:1], np.array([T], np.int32), np.zeros(1, np.int64), k,
+                                      1.0, 1 / 16)
+
+
 # --------------------------------------------------------------------------- printed sizes
 
 def test_printed_cache_and_flop_numbers():
