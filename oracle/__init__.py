@@ -34,6 +34,7 @@ def _lib():
         lib.oracle_sparse_mla.argtypes = [i32, P, P, P, P, i32, f64, P, P]
         lib.oracle_absorb_queries.argtypes = [i32, P, P, P, P]
         lib.oracle_v_up_proj.argtypes = [i32, P, P, P]
+        lib.oracle_cache_rows.argtypes = [i32, P, P, P, P, f64, P, P, f64, P, f64, P, P]
         lib.oracle_version.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -126,6 +127,25 @@ def decode_step(visible_len, row_cache_base, q_idx, w, k_idx, q_abs, kv_latent, 
     idx = topk(visible_len, s32, k)
     out, lse = sparse_mla(row_cache_base, q_abs, kv_latent, idx, softmax_scale)
     return s64, s32, idx, out, lse
+
+
+def cache_rows(hidden, wk, k_norm_weight, k_norm_bias, k_norm_eps, kv_a, kv_norm_weight, kv_norm_eps, positions,
+               rope_theta):
+    """(key [N,128], latent [N,576]) in fp64: the indexer-cache and latent-cache
+    rows of N new tokens (bf16-bit hidden and weights, fp32 norm parameters)."""
+    x = _c(hidden, np.uint16).reshape(-1, 6144)
+    N = x.shape[0]
+    wk_ = _c(wk, np.uint16).reshape(128, 6144)
+    kva = _c(kv_a, np.uint16).reshape(576, 6144)
+    kg, kb = _c(k_norm_weight, np.float32), _c(k_norm_bias, np.float32)
+    kvg = _c(kv_norm_weight, np.float32)
+    pos = _c(positions, np.int64)
+    assert kg.shape == (128,) and kb.shape == (128,) and kvg.shape == (512,) and pos.shape == (N,)
+    key = np.empty((N, 128), np.float64)
+    lat = np.empty((N, 576), np.float64)
+    _lib().oracle_cache_rows(N, _p(x), _p(wk_), _p(kg), _p(kb), ctypes.c_double(k_norm_eps), _p(kva), _p(kvg),
+                             ctypes.c_double(kv_norm_eps), _p(pos), ctypes.c_double(rope_theta), _p(key), _p(lat))
+    return key, lat
 
 
 # The 78-entry indexer_types array of GLM-5.2 as "GLM-5.2 架构 QA" CH1 Q1.2

@@ -272,3 +272,76 @@ void oracle_v_up_proj(int32_t R, const double* o, const uint16_t* kvb, double* o
         }
     }
 }
+
+/* ---- cache rows written per new token ------------------------------------
+ *
+ * [P1] CH3 §3.6 step 2: the indexer key is LayerNorm(128) of wk(hidden),
+ * whose first 64 dims then get RoPE and whose last 64 pass through:
+ *     k = [RoPE(LN(wk x)[0:64]) || LN(wk x)[64:128]].
+ * [P1] CH4 §4.1 / §4.5 steps 2-3: kv_a_proj_with_mqa maps the hidden state to
+ * 576 = 512 (compressed kv) + 64 (single-head k_pe); the 512 part goes
+ * through kv_a_layernorm (RMSNorm over 512) and k_pe through RoPE:
+ *     latent = [RMSNorm(c_kv) || RoPE(k_pe)].
+ * RoPE ([P5] Q1.4): the pair (i, i + 32) of a 64-dim block is rotated by the
+ * angle m * base^(-2i/64), m the token position, base = rope_theta.  The pages
+ * use HF's apply_rotary_pos_emb, which pairs dimension i with i + 32 (the two
+ * halves), and which this follows:
+ *     y[i]      = x[i] cos(a_i) - x[i + 32] sin(a_i)
+ *     y[i + 32] = x[i + 32] cos(a_i) + x[i] sin(a_i)          (i < 32)
+ * LayerNorm: (v - mean) / sqrt(var + eps) * g + b with the population
+ * variance; RMSNorm: v / sqrt(mean(v^2) + eps) * g.
+ * hidden [N, 6144] bf16 bits; wk [128, 6144] and kv_a [576, 6144] bf16 bits
+ * (nn.Linear layout: one output per row); k_g, k_b [128], kv_g [512] fp32;
+ * pos [N]; outputs key [N, 128] and latent [N, 576] in fp64.
+ */
+#define OR_HIDDEN 6144
+
+static void or_rope64(double* v, int64_t m, double base)
+{
+    for (int i = 0; i < 32; i++) {
+        const double a = (double)m * pow(base, -2.0 * i / 64.0);
+        const double c = cos(a), s = sin(a);
+        const double x0 = v[i], x1 = v[i + 32];
+        v[i] = x0 * c - x1 * s;
+        v[i + 32] = x1 * c + x0 * s;
+    }
+}
+
+void oracle_cache_rows(int32_t N, const uint16_t* hidden, const uint16_t* wk, const float* k_g, const float* k_b,
+                       double k_eps, const uint16_t* kv_a, const float* kv_g, double kv_eps, const int64_t* pos,
+                       double rope_theta, double* key, double* latent)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < N; t++) {
+        const uint16_t* x = hidden + (int64_t)t * OR_HIDDEN;
+        double kx[OR_IDX_DIM], lx[OR_ROW];
+        for (int c = 0; c < OR_IDX_DIM; c++) {
+            double acc = 0.0;
+            for (int d = 0; d < OR_HIDDEN; d++) acc += bf16_to_f64(wk[(int64_t)c * OR_HIDDEN + d]) * bf16_to_f64(x[d]);
+            kx[c] = acc;
+        }
+        for (int c = 0; c < OR_ROW; c++) {
+            double acc = 0.0;
+            for (int d = 0; d < OR_HIDDEN; d++) acc += bf16_to_f64(kv_a[(int64_t)c * OR_HIDDEN + d]) * bf16_to_f64(x[d]);
+            lx[c] = acc;
+        }
+        /* indexer key: LayerNorm(128), then RoPE on dims 0..63 */
+        double mean = 0.0, var = 0.0;
+        for (int c = 0; c < OR_IDX_DIM; c++) mean += kx[c];
+        mean /= OR_IDX_DIM;
+        for (int c = 0; c < OR_IDX_DIM; c++) var += (kx[c] - mean) * (kx[c] - mean);
+        var /= OR_IDX_DIM;
+        const double inv = 1.0 / sqrt(var + k_eps);
+        for (int c = 0; c < OR_IDX_DIM; c++) kx[c] = (kx[c] - mean) * inv * (double)k_g[c] + (double)k_b[c];
+        or_rope64(kx, pos[t], rope_theta);
+        /* latent row: RMSNorm over c_kv, RoPE on k_pe */
+        double ms = 0.0;
+        for (int c = 0; c < OR_LATENT; c++) ms += lx[c] * lx[c];
+        ms /= OR_LATENT;
+        const double rinv = 1.0 / sqrt(ms + kv_eps);
+        for (int c = 0; c < OR_LATENT; c++) lx[c] = lx[c] * rinv * (double)kv_g[c];
+        or_rope64(lx + OR_LATENT, pos[t], rope_theta);
+        memcpy(key + (int64_t)t * OR_IDX_DIM, kx, sizeof kx);
+        memcpy(latent + (int64_t)t * OR_ROW, lx, sizeof lx);
+    }
+}

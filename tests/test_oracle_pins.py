@@ -346,6 +346,98 @@ def test_dsa_equals_dense_causal_attention_when_at_most_k_visible(oracle_mod):
     np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
 
 
+# --------------------------------------------------------------------------- cache writers
+
+def cache_inputs(N, seed, theta_key="rope_theta_glm52"):
+    g = np.random.default_rng(seed)
+    H = golden("hidden_size")
+    x = wl.f32_to_bf16_bits(g.standard_normal((N, H)).astype(np.float32))
+    wk = wl.f32_to_bf16_bits((g.standard_normal((128, H)) / np.sqrt(H)).astype(np.float32))
+    kva = wl.f32_to_bf16_bits((g.standard_normal((576, H)) / np.sqrt(H)).astype(np.float32))
+    kg = (1 + 0.1 * g.standard_normal(128)).astype(np.float32)
+    kb = (0.1 * g.standard_normal(128)).astype(np.float32)
+    kvg = (1 + 0.1 * g.standard_normal(512)).astype(np.float32)
+    return dict(hidden=x, wk=wk, k_norm_weight=kg, k_norm_bias=kb, k_norm_eps=1e-6, kv_a=kva, kv_norm_weight=kvg,
+                kv_norm_eps=1e-5, rope_theta=float(golden(theta_key)))
+
+
+def test_cache_rows_at_position_zero_are_torch_layer_norm_and_rms_norm(oracle_mod):
+    """RoPE at position 0 is the identity, so the rows reduce to library
+    routines: numpy matmul for both projections, torch layer_norm (with weight
+    and bias) on the 128-d key and torch rms_norm (with weight) on the 512-d
+    c_kv, all in fp64; k_pe passes through unchanged."""
+    c = cache_inputs(5, 31)
+    key, lat = oracle_mod.cache_rows(positions=np.zeros(5, np.int64), **c)
+    xf = f(c["hidden"])
+    yk = xf @ f(c["wk"]).T
+    yl = xf @ f(c["kv_a"]).T
+    ln = torch.nn.functional.layer_norm(torch.from_numpy(yk), (128,), torch.from_numpy(c["k_norm_weight"].astype(np.float64)),
+                                        torch.from_numpy(c["k_norm_bias"].astype(np.float64)), eps=c["k_norm_eps"]).numpy()
+    rms = torch.nn.functional.rms_norm(torch.from_numpy(yl[:, :512]), (512,),
+                                       torch.from_numpy(c["kv_norm_weight"].astype(np.float64)),
+                                       eps=c["kv_norm_eps"]).numpy()
+    np.testing.assert_allclose(key, ln, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lat[:, :512], rms, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lat[:, 512:], yl[:, 512:], rtol=1e-12, atol=1e-13)
+
+
+def test_cache_rows_rope_closed_forms(oracle_mod):
+    """A one-hot hidden state and a k_pe weight block that yields the 64-d
+    vector (1 x 32, 0 x 32) make RoPE's output readable: dims i and i + 32
+    become cos and sin of m * theta^(-2i/64) (GLM-5.2 QA Q1.4), the
+    half-split pairing of apply_rotary_pos_emb.  Pair 0 turns by exactly m
+    radians, pair 16 by m / sqrt(theta).  Swapped halves, interleaved pairs, a
+    wrong sign or a wrong frequency exponent fail."""
+    c = cache_inputs(1, 32)
+    x = np.zeros((3, 6144), np.uint16)
+    x[:, 7] = wl.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    kva = c["kv_a"].copy()
+    kva[512:, 7] = 0
+    kva[512:544, 7] = wl.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    c.update(hidden=x, kv_a=kva)
+    m = np.array([1, 2, 1000003], np.int64)
+    _, lat = oracle_mod.cache_rows(positions=m, **c)
+    pe = lat[:, 512:]
+    theta = c["rope_theta"]
+    assert theta == 8e6
+    for t in range(3):
+        np.testing.assert_allclose(pe[t, 0], np.cos(float(m[t])), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(pe[t, 32], np.sin(float(m[t])), rtol=0, atol=1e-12)
+        a16 = m[t] / np.sqrt(theta)
+        np.testing.assert_allclose(pe[t, [16, 48]], [np.cos(a16), np.sin(a16)], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(pe[t, :32] ** 2 + pe[t, 32:] ** 2, 1.0, rtol=0, atol=1e-12)
+    # angles fall with i: the last pair turns by m * theta^(-62/64)
+    a31 = 2 * theta ** (-62 / 64)
+    np.testing.assert_allclose(pe[1, [31, 63]], [np.cos(a31), np.sin(a31)], rtol=0, atol=1e-12)
+
+
+def test_cache_rows_norm_invariants(oracle_mod):
+    """With eps = 0 both norms are scale-invariant (doubling the hidden state,
+    exact in bf16, changes nothing); a hidden state whose pre-norm key is
+    constant across the 128 dims gives LayerNorm output = bias (then RoPE on
+    the first 64 dims); RoPE keeps each pair's length and, being a rotation,
+    the dot product of two keys depends only on their position difference."""
+    c = cache_inputs(4, 33)
+    c.update(k_norm_eps=0.0, kv_norm_eps=0.0)
+    pos = np.array([3, 70, 5000, 123456], np.int64)
+    k1, l1 = oracle_mod.cache_rows(positions=pos, **c)
+    c2 = dict(c, hidden=wl.f32_to_bf16_bits(2 * f(c["hidden"]).astype(np.float32)))
+    k2, l2 = oracle_mod.cache_rows(positions=pos, **c2)
+    np.testing.assert_allclose(k2, k1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2[:, :512], l1[:, :512], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2[:, 512:], 2 * l1[:, 512:], rtol=1e-12, atol=1e-12)
+    # constant pre-norm key: every wk row identical
+    wk = np.repeat(c["wk"][:1], 128, axis=0)
+    k3, _ = oracle_mod.cache_rows(positions=np.zeros(4, np.int64), **dict(c, wk=wk, k_norm_eps=1e-6))
+    np.testing.assert_allclose(k3, np.broadcast_to(c["k_norm_bias"].astype(np.float64), (4, 128)), atol=1e-12)
+    # relative positions: same hidden at positions (m, n) and (m + d, n + d)
+    cc = dict(c, hidden=np.repeat(c["hidden"][:1], 4, axis=0))
+    kk, ll = oracle_mod.cache_rows(positions=np.array([10, 17, 10 + 900, 17 + 900], np.int64), **cc)
+    np.testing.assert_allclose(kk[0, :64] @ kk[1, :64], kk[2, :64] @ kk[3, :64], rtol=1e-10)
+    np.testing.assert_allclose(ll[0, 512:] @ ll[1, 512:], ll[2, 512:] @ ll[3, 512:], rtol=1e-10)
+    np.testing.assert_allclose(kk[0, 64:], kk[2, 64:], rtol=1e-14)       # dims 64..127 never rotate
+
+
 # --------------------------------------------------------------------------- IndexShare
 
 def test_index_share_types_match_printed_layer_pattern(oracle_mod):
