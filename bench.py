@@ -282,6 +282,25 @@ def main():
                    "v_up_proj": proj_entry(ms_up, up_bytes, up_flops)}
     log(f"[bench] absorb_queries: {ms_ab * 1e3:.1f} us, v_up_proj: {ms_up * 1e3:.1f} us ({Rp} rows)")
 
+    # The cache writers for this workload's new tokens (one per row, at most
+    # 8192): both projections of the hidden state, the norms, RoPE and the
+    # scatter into two caches of the same shape as the path's.
+    Nw = min(R, 8192)
+    cw = wl.cache_write_inputs(Nw, max_position=maxv, cache_rows=Nw)
+    cw["slots"] = np.arange(Nw, dtype=np.int64)  # every token written
+    cw_t = {k: (bf(v) if v.dtype == np.uint16 else torch.from_numpy(v).to(dev))
+            for k, v in cw.items() if isinstance(v, np.ndarray)}
+    kc_w = torch.empty((Nw, 128), dtype=torch.bfloat16, device=dev)
+    lc_w = torch.empty((Nw, 576), dtype=torch.bfloat16, device=dev)
+    ws_w = dsa.workspace(dsa.dsa_cache_write_workspace_size(Nw), dev)
+    ms_cw = timed(lambda: dsa.dsa_cache_write(cw_t["hidden"], cw_t["wk"], cw_t["k_norm_weight"], cw_t["k_norm_bias"],
+                                              1e-6, cw_t["kv_a"], cw_t["kv_norm_weight"], 1e-5, cw_t["positions"],
+                                              cw_t["slots"], 1e6, kc_w, lc_w, ws_w, stream=stream))
+    cw_bytes = 704 * 6144 * 2 + (128 * 2 + 512) * 4 + Nw * (6144 * 2 + 128 * 2 + 576 * 2 + 4 + 8)
+    cw_flops = 2 * Nw * 6144 * 704
+    cache_write = dict(tokens=Nw, **proj_entry(ms_cw, cw_bytes, cw_flops))
+    log(f"[bench] cache_write: {ms_cw * 1e3:.1f} us ({Nw} tokens)")
+
     # Step-level algorithmic bytes (whole path) for context.
     step_bytes = int(np.sum(256 * n + 1152 * np.minimum(n, K_TOP) + 82048 + 139264))
     traffic = traffic_from_profiles("indexer", w.name, src_hash(["indexer.hip", "dsa_device.h"]))
@@ -315,6 +334,7 @@ def main():
         "cpu_baseline": cpu,
         "projections": projections,
         "index_share": share,
+        "cache_write": cache_write,
         "step_alg_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }

@@ -222,6 +222,54 @@ DSA_API dsa_status_t dsa_absorb_queries(int32_t num_rows, const void* q_nope, co
 DSA_API dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* kv_b_weight,
                                    float* out, void* hip_stream);
 
+/* ---- Cache writers -----------------------------------------------------
+ *
+ * The rows the path reads, made from a new token's hidden state x (6144-d):
+ *  - indexer key ("GLM-5.1 架构深度拆解" CH3 §3.6 step 2):
+ *      v = LayerNorm(wk x) over 128 dims (population variance, weight, bias),
+ *      key = [RoPE(v[0:64]) || v[64:128]];
+ *  - latent row (same page, CH4 §4.1, §4.5 steps 2-3):
+ *      [c || p] = kv_a_proj_with_mqa x  (512 + 64 outputs),
+ *      row = [RMSNorm(c) over 512 (weight) || RoPE(p)];
+ *  - RoPE ("GLM-5.2 架构 QA" CH1 Q1.4): in a 64-d block, dims i and i + 32
+ *    (i < 32) turn by a = position * rope_theta^(-2i/64):
+ *      y[i] = x[i] cos a - x[i+32] sin a,  y[i+32] = x[i+32] cos a + x[i] sin a.
+ * Projections accumulate in fp32 on bf16 matrix cores; norms run in fp32;
+ * RoPE angles are formed in fp64; results are rounded to bf16
+ * (round-to-nearest-even) as they are stored.
+ */
+
+#define DSA_HIDDEN 6144
+
+/* Workspace bytes dsa_cache_write needs (host arithmetic only; 0 when
+ * num_tokens is outside [1, 2^24]). */
+DSA_API size_t dsa_cache_write_workspace_size(int32_t num_tokens);
+
+/* Computes both cache rows of num_tokens new tokens and writes them at row
+ * slots[t] of each cache (a token whose slot is negative writes nothing):
+ *   hidden          [N, 6144] bf16, 16-B aligned
+ *   wk_weight       [128, 6144] bf16 (nn.Linear layout: one output per row)
+ *   k_norm_weight, k_norm_bias  [128] fp32, 8-B aligned;  k_norm_eps >= 0
+ *   kv_a_weight     [576, 6144] bf16 (rows 0..511 c_kv, 512..575 k_pe)
+ *   kv_norm_weight  [512] fp32, 16-B aligned;  kv_norm_eps >= 0
+ *   positions       [N] int32 RoPE positions;  slots [N] int64 cache rows
+ *   rope_theta      > 0 (1e6 for GLM-5/5.1, 8e6 for GLM-5.2)
+ *   k_idx_cache     [*, 128] bf16 and kv_latent_cache [*, 576] bf16, the
+ *                   caches dsa_indexer_scores / dsa_sparse_mla_attn read; only
+ *                   the rows named by slots are written
+ *   ws              >= dsa_cache_write_workspace_size(N) bytes, 256-B aligned
+ * Slots must be distinct (two tokens on one slot race) and inside the caches
+ * (not checked: the library cannot see their sizes).  Errors: num_tokens
+ * outside [1, 2^24]; NULL or misaligned pointers; a negative or non-finite
+ * eps; rope_theta not finite and > 0; workspace too small; no gfx950 device.
+ */
+DSA_API dsa_status_t dsa_cache_write(int32_t num_tokens, const void* hidden, const void* wk_weight,
+                                     const float* k_norm_weight, const float* k_norm_bias, float k_norm_eps,
+                                     const void* kv_a_weight, const float* kv_norm_weight, float kv_norm_eps,
+                                     const int32_t* positions, const int64_t* slots, double rope_theta,
+                                     void* k_idx_cache, void* kv_latent_cache, void* ws, size_t ws_bytes,
+                                     void* hip_stream);
+
 /* ---- IndexShare: one selection serving several layers ------------------
  *
  * Only "full" layers run the indexer and the top-k; a "shared" layer has no

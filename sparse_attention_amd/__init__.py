@@ -31,6 +31,7 @@ LATENT_DIM = 512
 ROPE_DIM = 64
 ROW_DIM = 576
 TOPK_MAX = 2048
+HIDDEN = 6144
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -88,6 +89,8 @@ def load_library():
         "dsa_absorb_queries": ([i32, P, P, P, P, P], ctypes.c_int),
         "dsa_v_up_proj": ([i32, P, P, P, P], ctypes.c_int),
         "dsa_index_share_source": ([i32, i32, i32, i32], i32),
+        "dsa_cache_write_workspace_size": ([i32], sz),
+        "dsa_cache_write": ([i32, P, P, P, P, f32, P, P, f32, P, P, ctypes.c_double, P, P, P, sz, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sigs.items():
         fn = getattr(lib, name)
@@ -103,7 +106,7 @@ def exported_symbols():
         "dsa_version", "dsa_status_string", "dsa_last_error_detail", "dsa_indexer_scores",
         "dsa_topk_workspace_size", "dsa_topk_select", "dsa_sparse_mla_workspace_size",
         "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step", "dsa_absorb_queries",
-        "dsa_v_up_proj", "dsa_index_share_source",
+        "dsa_v_up_proj", "dsa_index_share_source", "dsa_cache_write_workspace_size", "dsa_cache_write",
     ]
 
 
@@ -250,3 +253,25 @@ def dsa_index_share_source(layer, num_layers=78, leading_full=3, freq=4):
     if src < 0:
         raise DsaError(1, f"dsa_index_share_source({layer}, {num_layers}, {leading_full}, {freq}): bad arguments")
     return int(src)
+
+
+def dsa_cache_write_workspace_size(num_tokens):
+    return int(load_library().dsa_cache_write_workspace_size(int(num_tokens)))
+
+
+def dsa_cache_write(hidden, wk_weight, k_norm_weight, k_norm_bias, k_norm_eps, kv_a_weight, kv_norm_weight,
+                    kv_norm_eps, positions, slots, rope_theta, k_idx_cache, kv_latent_cache, ws, stream=None):
+    """Writes the indexer-key and latent rows of len(hidden) new tokens at
+    rows `slots` of the two caches (negative slot: token skipped)."""
+    lib = load_library()
+    N = int(hidden.shape[0])
+    _check(lib.dsa_cache_write(N, _ptr(hidden, "hidden", _BF16), _ptr(wk_weight, "wk_weight", _BF16),
+                               _ptr(k_norm_weight, "k_norm_weight", (torch.float32,)),
+                               _ptr(k_norm_bias, "k_norm_bias", (torch.float32,)), float(k_norm_eps),
+                               _ptr(kv_a_weight, "kv_a_weight", _BF16),
+                               _ptr(kv_norm_weight, "kv_norm_weight", (torch.float32,)), float(kv_norm_eps),
+                               _ptr(positions, "positions", (torch.int32,)), _ptr(slots, "slots", (torch.int64,)),
+                               float(rope_theta), _ptr(k_idx_cache, "k_idx_cache", _BF16),
+                               _ptr(kv_latent_cache, "kv_latent_cache", _BF16), _ptr(ws, "ws"),
+                               ws.numel() * ws.element_size() if ws is not None else 0,
+                               _stream(stream, hidden)))

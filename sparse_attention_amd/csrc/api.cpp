@@ -321,6 +321,46 @@ dsa_status_t dsa_v_up_proj(int32_t num_rows, const float* o_latent, const void* 
     return after_launch(st, "v_up_proj");
 }
 
+size_t dsa_cache_write_workspace_size(int32_t num_tokens)
+{
+    if (num_tokens < 1 || num_tokens > kMaxRows) return 0;
+    return dsa::cache_write_workspace_bytes(num_tokens);
+}
+
+dsa_status_t dsa_cache_write(int32_t num_tokens, const void* hidden, const void* wk_weight,
+                             const float* k_norm_weight, const float* k_norm_bias, float k_norm_eps,
+                             const void* kv_a_weight, const float* kv_norm_weight, float kv_norm_eps,
+                             const int32_t* positions, const int64_t* slots, double rope_theta, void* k_idx_cache,
+                             void* kv_latent_cache, void* ws, size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    if (num_tokens < 1 || num_tokens > kMaxRows)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "num_tokens=%d outside [1, %d]", num_tokens, kMaxRows);
+    DSA_TRY(check_ptr16(hidden, "hidden"));
+    DSA_TRY(check_ptr16(wk_weight, "wk_weight"));
+    DSA_TRY(check_ptr16(kv_a_weight, "kv_a_weight"));
+    DSA_TRY(check_ptr16(kv_norm_weight, "kv_norm_weight"));
+    DSA_TRY(check_ptr16(k_idx_cache, "k_idx_cache"));
+    DSA_TRY(check_ptr16(kv_latent_cache, "kv_latent_cache"));
+    if (!k_norm_weight || !k_norm_bias || !positions || !slots)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "k_norm_weight, k_norm_bias, positions and slots must not be NULL");
+    if (!aligned(k_norm_weight, 8) || !aligned(k_norm_bias, 8))
+        return fail(DSA_ERR_MISALIGNED, "k_norm_weight and k_norm_bias need 8-byte alignment");
+    if (!aligned(positions, 4)) return fail(DSA_ERR_MISALIGNED, "positions not 4-byte aligned");
+    if (!aligned(slots, 8)) return fail(DSA_ERR_MISALIGNED, "slots not 8-byte aligned");
+    if (!std::isfinite(k_norm_eps) || k_norm_eps < 0.f || !std::isfinite(kv_norm_eps) || kv_norm_eps < 0.f)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "norm eps must be finite and >= 0");
+    if (!std::isfinite(rope_theta) || rope_theta <= 0.0)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
+    DSA_TRY(check_ws(ws, ws_bytes, dsa::cache_write_workspace_bytes(num_tokens)));
+    DSA_TRY(check_device());
+    hipStream_t st = (hipStream_t)hip_stream;
+    dsa::launch_cache_write(num_tokens, (const uint16_t*)hidden, (const uint16_t*)wk_weight, k_norm_weight,
+                            k_norm_bias, k_norm_eps, (const uint16_t*)kv_a_weight, kv_norm_weight, kv_norm_eps,
+                            positions, slots, rope_theta, (uint16_t*)k_idx_cache, (uint16_t*)kv_latent_cache, ws, st);
+    return after_launch(st, "cache_write");
+}
+
 int32_t dsa_index_share_source(int32_t layer, int32_t num_layers, int32_t leading_full, int32_t freq)
 {
     if (num_layers < 1 || layer < 0 || layer >= num_layers || leading_full < 1 || freq < 1) return -1;

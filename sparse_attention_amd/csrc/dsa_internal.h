@@ -52,6 +52,14 @@ void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint1
                            uint16_t* q_abs, hipStream_t stream);
 void launch_v_up_proj(int32_t num_rows, const float* o, const uint16_t* kvb, float* out, hipStream_t stream);
 
+// ---- cache writers ---------------------------------------------------------
+int cache_write_splits(int32_t num_tokens);
+size_t cache_write_workspace_bytes(int32_t num_tokens);
+void launch_cache_write(int32_t num_tokens, const uint16_t* hidden, const uint16_t* wk, const float* k_norm_weight,
+                        const float* k_norm_bias, float k_norm_eps, const uint16_t* kv_a, const float* kv_norm_weight,
+                        float kv_norm_eps, const int32_t* positions, const int64_t* slots, double rope_theta,
+                        uint16_t* k_idx_cache, uint16_t* kv_latent_cache, void* ws, hipStream_t stream);
+
 // Debug aid: when DSA_SYNC_DEBUG=1, synchronize after every launch.
 bool sync_debug();
 

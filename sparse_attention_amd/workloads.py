@@ -40,7 +40,9 @@ SOFTMAX_SCALE = float(np.float32(1.0 / math.sqrt(256.0)))
 INDEX_SCALE = 1.0
 W_SCALE = np.float32(32.0 ** -0.5)
 
-T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN, T_Q_NOPE, T_Q_PE, T_KVB, T_O, T_LAYER = range(13)
+(T_Q_IDX, T_W, T_K_IDX, T_Q_ABS, T_KV, T_LEN, T_TIE_PROTO, T_TIE_ASSIGN, T_Q_NOPE, T_Q_PE, T_KVB, T_O, T_LAYER,
+ T_HIDDEN, T_WK, T_KVA, T_NORM, T_POS) = range(18)
+HIDDEN = 6144
 KVB_SCALE = np.float32(512.0 ** -0.5)   # kv_b_proj rows ~ N(0, 1/512): unit-variance outputs
 
 
@@ -204,6 +206,35 @@ def layer_stack(lengths, num_layers, seed=6):
         s_l = int(np.random.SeedSequence(seed, spawn_key=(T_LAYER, l)).generate_state(1)[0])
         out.append(_decode(f"layer{l}", s_l, lengths, f"layer {l}").generate())
     return out
+
+
+def cache_write_inputs(N, seed=7, max_position=1 << 20, cache_rows=None):
+    """Synthetic inputs of the cache writers for N new tokens: hidden [N,6144]
+    bf16 N(0,1); wk [128,6144] and kv_a [576,6144] bf16 N(0,1/6144) (unit
+    variance outputs); LayerNorm weight 1 + 0.1 N(0,1) and bias 0.1 N(0,1)
+    [128], RMSNorm weight 1 + 0.1 N(0,1) [512] (fp32); positions uniform in
+    [0, max_position) with 0 and max_position - 1 included; slots a random
+    injection into [0, cache_rows) (default 2N + 7), every 7th token -1
+    (skipped)."""
+    g = lambda tid: rng(seed, tid, 0)
+    s = np.float32(HIDDEN ** -0.5)
+    x = np.stack([normal_bf16(seed, T_HIDDEN, t, (HIDDEN,)) for t in range(N)])
+    wk = f32_to_bf16_bits(g(T_WK).standard_normal((128, HIDDEN), dtype=np.float32) * s)
+    kva = f32_to_bf16_bits(g(T_KVA).standard_normal((576, HIDDEN), dtype=np.float32) * s)
+    gn = g(T_NORM)
+    kg = (1 + 0.1 * gn.standard_normal(128)).astype(np.float32)
+    kb = (0.1 * gn.standard_normal(128)).astype(np.float32)
+    kvg = (1 + 0.1 * gn.standard_normal(512)).astype(np.float32)
+    gp = g(T_POS)
+    pos = gp.integers(0, max_position, size=N).astype(np.int32)
+    pos[0] = 0
+    if N > 1:
+        pos[-1] = max_position - 1
+    rows = 2 * N + 7 if cache_rows is None else cache_rows
+    slots = gp.permutation(rows)[:N].astype(np.int64)
+    slots[3::7] = -1
+    return dict(hidden=x, wk=wk, k_norm_weight=kg, k_norm_bias=kb, kv_a=kva, kv_norm_weight=kvg, positions=pos,
+                slots=slots, cache_rows=rows)
 
 
 def projection_inputs(R, seed=5):

@@ -216,3 +216,40 @@ def test_index_share_source_validation_and_other_periods(lib):
     assert [f(l, 8, 1, 2) for l in range(8)] == [0, 0, 2, 2, 4, 4, 6, 6]  # one full, one shared
     with pytest.raises(m.DsaError):
         m.dsa_index_share_source(78)
+
+
+def test_cache_write_workspace_and_validation(lib):
+    assert lib.dsa_cache_write_workspace_size(0) == 0
+    assert lib.dsa_cache_write_workspace_size((1 << 24) + 1) == 0
+    # 64 tokens: one token tile, K split 24 ways; 8192 tokens: no split
+    assert lib.dsa_cache_write_workspace_size(64) == 24 * 64 * 704 * 4
+    assert lib.dsa_cache_write_workspace_size(8192) == 8192 * 704 * 4
+    ws_ok = lib.dsa_cache_write_workspace_size(4)
+    d = dict(N=4, x=0x1000, wk=0x2000, kg=0x3000, kb=0x3200, keps=1e-6, kva=0x4000, kvg=0x5000, kveps=1e-5,
+             pos=0x6000, slots=0x7000, theta=1e6, kc=0x8000, lc=0x9000, ws=0x10000, wsb=ws_ok)
+
+    def f(**kw):
+        a = dict(d, **kw)
+        return lib.dsa_cache_write(a["N"], a["x"], a["wk"], a["kg"], a["kb"], a["keps"], a["kva"], a["kvg"],
+                                   a["kveps"], a["pos"], a["slots"], a["theta"], a["kc"], a["lc"], a["ws"], a["wsb"],
+                                   None)
+    assert f(N=0) == INVALID
+    assert f(x=0) == INVALID
+    assert f(wk=0x2004) == MISALIGNED
+    assert f(kva=0) == INVALID
+    assert f(kvg=0x5004) == MISALIGNED
+    assert f(kg=0) == INVALID
+    assert f(kb=0x3201) == MISALIGNED
+    assert f(kg=0x3004) == MISALIGNED
+    assert f(pos=0) == INVALID
+    assert f(slots=0x7004) == MISALIGNED
+    assert f(keps=-1.0) == INVALID
+    assert f(kveps=float("nan")) == INVALID
+    assert f(theta=0.0) == INVALID
+    assert f(theta=float("inf")) == INVALID
+    assert f(kc=0x8008) == MISALIGNED
+    assert f(lc=0) == INVALID
+    assert f(wsb=ws_ok - 1) == WS_SMALL
+    assert f(ws=0x10010) == MISALIGNED
+    if not HAS_GPU:
+        assert f() == NO_DEVICE

@@ -426,6 +426,99 @@ def test_decode_step_deterministic(dsa):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+# ----------------------------------------------------------------------------- cache writers
+
+SENTINEL = 0x7F7F  # a finite bf16 pattern no written row can be mistaken for in bulk
+
+
+def run_cache_write(dsa, c, theta, eps=(1e-6, 1e-5)):
+    N = c["hidden"].shape[0]
+    kc = torch.full((c["cache_rows"], 128), SENTINEL, dtype=torch.int16, device=DEV)
+    lc = torch.full((c["cache_rows"], 576), SENTINEL, dtype=torch.int16, device=DEV)
+    ws = dsa.workspace(dsa.dsa_cache_write_workspace_size(N), DEV)
+    ws.fill_(255)
+    dsa.dsa_cache_write(dev_bf16(c["hidden"]), dev_bf16(c["wk"]), dev(c["k_norm_weight"]), dev(c["k_norm_bias"]), eps[0],
+                        dev_bf16(c["kv_a"]), dev(c["kv_norm_weight"]), eps[1], dev(c["positions"]), dev(c["slots"]),
+                        theta, kc, lc, ws)
+    torch.cuda.synchronize()
+    return kc.cpu().numpy().view(np.uint16), lc.cpu().numpy().view(np.uint16)
+
+
+def check_cache_rows(got_bits, ref, label):
+    """bf16 results against fp64 rows: within one bf16 rounding (2^-8 |ref|)
+    plus the fp32 arithmetic before it (bounded by 1e-4 of the row's rms),
+    and >= 99.5% of elements equal to bf16(ref)."""
+    got = wl.bf16_bits_to_f32(got_bits).astype(np.float64)
+    rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * rms
+    assert np.all(err <= bound), f"{label}: worst excess {np.max(err - bound):.3e}"
+    same = got_bits == wl.f32_to_bf16_bits(ref.astype(np.float32))
+    assert same.mean() >= 0.995, f"{label}: {same.mean():.4f} equal to bf16(ref)"
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 300, 1000])
+def test_cache_write_against_oracle(dsa, oracle_mod, N):
+    """Both cache rows of N new tokens against the oracle, at positions up to
+    2^20 (RoPE angles far from 0) and theta = 8e6: the rows named by slots
+    hold the results, every other row (including those of tokens with slot
+    -1) keeps its sentinel.  N = 1 and 64 split K 24 ways, 300 twelve, 1000
+    three; 5, 300 and 1000 leave ragged token tiles."""
+    c = wl.cache_write_inputs(N, seed=70 + N)
+    theta = 8e6
+    kc, lc = run_cache_write(dsa, c, theta)
+    key, lat = oracle_mod.cache_rows(c["hidden"], c["wk"], c["k_norm_weight"], c["k_norm_bias"], 1e-6, c["kv_a"],
+                                     c["kv_norm_weight"], 1e-5, c["positions"].astype(np.int64), theta)
+    live = c["slots"] >= 0
+    sl = c["slots"][live]
+    check_cache_rows(kc[sl], key[live], f"key N={N}")
+    check_cache_rows(lc[sl], lat[live], f"latent N={N}")
+    untouched = np.setdiff1d(np.arange(c["cache_rows"]), sl)
+    assert np.all(kc[untouched] == SENTINEL) and np.all(lc[untouched] == SENTINEL)
+
+
+def test_cache_write_prefill_sized_sampled_and_deterministic(dsa, oracle_mod):
+    """8192 tokens (no K split): 48 sampled tokens against the oracle, theta
+    = 1e6; a second call gives the same bytes."""
+    N = 8192
+    c = wl.cache_write_inputs(N, seed=9, max_position=202752)
+    theta = 1e6
+    kc, lc = run_cache_write(dsa, c, theta)
+    kc2, lc2 = run_cache_write(dsa, c, theta)
+    assert np.array_equal(kc, kc2) and np.array_equal(lc, lc2)
+    pick = np.unique(np.concatenate([[0, 1, N - 1], np.random.default_rng(0).choice(N, 45, replace=False)]))
+    pick = pick[c["slots"][pick] >= 0]
+    key, lat = oracle_mod.cache_rows(c["hidden"][pick], c["wk"], c["k_norm_weight"], c["k_norm_bias"], 1e-6,
+                                     c["kv_a"], c["kv_norm_weight"], 1e-5, c["positions"][pick].astype(np.int64),
+                                     theta)
+    check_cache_rows(kc[c["slots"][pick]], key, "key prefill")
+    check_cache_rows(lc[c["slots"][pick]], lat, "latent prefill")
+
+
+def test_cache_write_feeds_the_path(dsa, oracle_mod):
+    """Rows the writer produced are what the indexer and attention read: a
+    decode step over a 3000-position cache written by dsa_cache_write (slots
+    = positions) matches the oracle's step over the oracle's rows rounded to
+    bf16 (recall, and attention on the GPU's own list)."""
+    T = 3000
+    c = wl.cache_write_inputs(T, seed=11, cache_rows=T)
+    c["positions"] = np.arange(T, dtype=np.int32)
+    c["slots"] = np.arange(T, dtype=np.int64)
+    kc, lc = run_cache_write(dsa, c, 1e6)
+    key, lat = oracle_mod.cache_rows(c["hidden"], c["wk"], c["k_norm_weight"], c["k_norm_bias"], 1e-6, c["kv_a"],
+                                     c["kv_norm_weight"], 1e-5, c["positions"].astype(np.int64), 1e6)
+    x = wl.decode(1, T, seed=12).generate(with_caches=False)
+    x["k_idx"], x["kv_latent"] = kc, lc
+    idx, out, lse = run_decode_step(dsa, x)
+    kb = wl.f32_to_bf16_bits(key.astype(np.float32))
+    lb = wl.f32_to_bf16_bits(lat.astype(np.float32))
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(x["visible_len"], x["row_cache_base"], x["q_idx"], x["w"], kb,
+                                                   x["q_abs"], lb, 2048, 1.0, wl.SOFTMAX_SCALE)
+    assert recall_check(idx, idx_ref, s64, x["visible_len"]) >= 0.99
+    ref_out, ref_lse = oracle_mod.sparse_mla(x["row_cache_base"], x["q_abs"], lc, idx, wl.SOFTMAX_SCALE)
+    check_attention(out, lse, ref_out, ref_lse, "written caches")
+
+
 # ----------------------------------------------------------------------------- IndexShare
 
 def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):
