@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--config", default="c3", help="workload: c1 | c3 | c4 | c5")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (oracle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-paged", dest="paged", action="store_false",
+                   help="skip timing the step over paged caches")
     p.add_argument("--no-index-share", dest="index_share", action="store_false",
                    help="skip timing a 4-layer IndexShare group (1 full + 3 shared layers)")
     p.add_argument("--mode", default="decode", choices=["decode", "copy"],
@@ -204,6 +206,17 @@ def main():
     achieved = alg_bytes / (ms_idx * 1e-3) / 1e9
     log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
 
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
     # IndexShare: a 4-layer group in which one "full" layer runs the whole path
     # and three "shared" layers reuse its top-2048 list for their attention
     # (each with its own absorbed queries and latent cache).  Decode configs only.
@@ -243,6 +256,38 @@ def main():
             f"{R / (ms_group * 1e-3):.0f} tokens/s per group")
         del extra
 
+    # Paged caches: the same step over pools of 64-position blocks scattered by
+    # a random permutation (block tables per sequence).  Workloads whose
+    # sequence lengths are all multiples of the block size.
+    paged = None
+    PB = 64
+    if args.paged and np.all(w.seq_len % PB == 0):
+        nblk = int(w.cache_rows // PB)
+        gen_p = torch.Generator(device=dev)
+        gen_p.manual_seed(2024)
+        perm = torch.randperm(nblk, generator=gen_p, device=dev)
+        kpool = torch.empty_like(k_idx).view(nblk, PB, 128)
+        lpool = torch.empty_like(kv).view(nblk, PB, 576)
+        kpool[perm] = k_idx.view(nblk, PB, 128)
+        lpool[perm] = kv.view(nblk, PB, 576)
+        nb = int(w.seq_len.max() // PB)
+        bt = torch.zeros((len(w.seq_len), nb), dtype=torch.int32, device=dev)
+        for s_, (b0, T) in enumerate(zip(w.seq_base, w.seq_len)):
+            bt[s_, :T // PB] = perm[b0 // PB: (b0 + T) // PB].to(torch.int32)
+        seq_of_row = np.searchsorted(w.seq_base, x["row_cache_base"], side="right") - 1
+        prow = dsa.Rows(rows.visible_len, torch.from_numpy(seq_of_row.astype(np.int64)).to(dev), maxv,
+                        flags=rows.flags)
+        pg = dsa.Paged(bt, PB)
+        ws_p = dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, maxv, K_TOP), dev)
+        idx_p = torch.empty_like(idx)
+        ms_paged = timed(lambda: dsa.dsa_decode_step_paged(prow, pg, q_idx, wts, kpool, wl.INDEX_SCALE, q_abs, lpool,
+                                                           wl.SOFTMAX_SCALE, K_TOP, idx_p, out, lse, ws_p,
+                                                           stream=stream))
+        paged = {"block_size": PB, "us_per_step": round(ms_paged * 1e3, 2),
+                 "tokens_per_s": round(R / (ms_paged * 1e-3), 1), "vs_packed": round(ms_step / ms_paged, 4)}
+        log(f"[bench] paged step (blocks of {PB}): {ms_paged * 1e3:.1f} us/step")
+        del kpool, lpool
+
     # The projections on either side of the path (query absorption before it,
     # V up-projection after it), timed alone at this workload's row count
     # (at most 8192 rows), with synthetic kv_b_proj weights.
@@ -252,17 +297,6 @@ def main():
     o_lat = torch.from_numpy(px["o"]).to(dev)
     qa_p = torch.empty((Rp, 64, 576), dtype=torch.bfloat16, device=dev)
     up = torch.empty((Rp, 64, 256), dtype=torch.float32, device=dev)
-
-    def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
 
     ms_ab = timed(lambda: dsa.dsa_absorb_queries(qn, qp, kvb, qa_p, stream=stream))
     ms_up = timed(lambda: dsa.dsa_v_up_proj(o_lat, kvb, up, stream=stream))
@@ -335,6 +369,7 @@ def main():
         "projections": projections,
         "index_share": share,
         "cache_write": cache_write,
+        "paged": paged,
         "step_alg_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }

@@ -186,6 +186,54 @@ DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, 
                              int32_t* indices, float* out_latent, float* out_lse, void* ws,
                              size_t ws_bytes, void* hip_stream);
 
+/* ---- Paged caches -------------------------------------------------------
+ *
+ * The same calls over caches kept in fixed-size blocks of a shared pool, with
+ * a block table per sequence (the serving layout of vLLM's PagedAttention,
+ * which "GLM-5.2 架构 QA" CH2 Q2.6 and CH4 Q4.2 name as the paged store of
+ * the compressed cache in GLM-5.2's serving stack).  Only the
+ * addressing changes: position p of the sequence whose block-table row is s
+ * lives at pool row
+ *     block_table[s * max_blocks + p / block_size] * block_size + p % block_size
+ * in both pools (index keys [*, 128] and latent rows [*, 576]), which share
+ * the block table.  dsa_cache_write fills a pool when its slots are these
+ * rows.  In the *_paged calls rows->row_cache_base[r] is the block-table row
+ * s of row r's sequence (not a cache row); everything else means what it
+ * means above, and `indices` stay logical positions.  Results are bitwise
+ * those of the packed calls on the same logical caches.
+ */
+typedef struct {
+    const int32_t* block_table; /* device: [num_seqs, max_blocks] int32 pool block numbers, 4-B aligned */
+    int32_t max_blocks;         /* host: row stride of block_table, >= ceil(max_visible / block_size) */
+    int32_t block_size;         /* host: positions per block, a power of two in [16, 65536] */
+} dsa_paged_t;
+/* The entries a call reads (blocks below ceil(visible_len[r] / block_size))
+ * must name blocks inside both pools, and pool rows must stay below 2^31;
+ * neither is checked (device data).  Errors: as for the packed calls, plus a
+ * NULL or misaligned block table, a block size that is not a power of two in
+ * [16, 65536], or max_blocks too small for max_visible. */
+
+DSA_API dsa_status_t dsa_indexer_scores_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, const void* q_idx,
+                                              const float* w, const void* k_pool, float index_scale, float* scores,
+                                              int64_t ld, void* hip_stream);
+
+/* Workspace bytes dsa_sparse_mla_attn_paged needs (the packed size plus the
+ * translated index lists). */
+DSA_API size_t dsa_sparse_mla_paged_workspace_size(int32_t num_rows, int32_t k);
+
+DSA_API dsa_status_t dsa_sparse_mla_attn_paged(const dsa_rows_t* rows, const dsa_paged_t* paged,
+                                               const void* q_abs, const void* kv_pool, const int32_t* indices,
+                                               int32_t k, float softmax_scale, float* out_latent, float* out_lse,
+                                               void* ws, size_t ws_bytes, void* hip_stream);
+
+DSA_API size_t dsa_decode_step_paged_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k);
+
+DSA_API dsa_status_t dsa_decode_step_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, const void* q_idx,
+                                           const float* w, const void* k_pool, float index_scale, const void* q_abs,
+                                           const void* kv_pool, float softmax_scale, int32_t k, int32_t* indices,
+                                           float* out_latent, float* out_lse, void* ws, size_t ws_bytes,
+                                           void* hip_stream);
+
 /* ---- Projections on either side of the path ----------------------------
  *
  * kv_b_proj expands the 512-d latent into 64 heads x (192 non-RoPE key dims

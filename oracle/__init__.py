@@ -148,6 +148,15 @@ def cache_rows(hidden, wk, k_norm_weight, k_norm_bias, k_norm_eps, kv_a, kv_norm
     return key, lat
 
 
+def depage(pool, block_table_row, length, block_size):
+    """The logical cache rows [length, D] of one sequence held in a paged
+    pool: position p is pool row block_table_row[p // block_size] *
+    block_size + p % block_size (the block-table addressing of a paged KV
+    cache, vLLM's PagedAttention, which "GLM-5.2 架构 QA" CH2 Q2.6 names)."""
+    rows = [int(block_table_row[p // block_size]) * block_size + p % block_size for p in range(int(length))]
+    return np.asarray(pool)[np.asarray(rows, dtype=np.int64)]
+
+
 # The 78-entry indexer_types array of GLM-5.2 as "GLM-5.2 架构 QA" CH1 Q1.2
 # spells it out: a cold-start block of 3 full then 3 shared layers, then 18
 # periods of one full layer followed by 3 shared ones.

@@ -19,7 +19,9 @@ __all__ = [
     "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk_select",
     "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_attn",
     "dsa_decode_step_workspace_size", "dsa_decode_step", "workspace", "dsa_absorb_queries", "dsa_v_up_proj",
-    "dsa_index_share_source",
+    "dsa_index_share_source", "dsa_cache_write_workspace_size", "dsa_cache_write", "Paged",
+    "dsa_indexer_scores_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_sparse_mla_attn_paged",
+    "dsa_decode_step_paged_workspace_size", "dsa_decode_step_paged", "HIDDEN",
     "INDEX_HEADS", "INDEX_DIM", "HEADS", "LATENT_DIM", "ROPE_DIM", "ROW_DIM", "TOPK_MAX",
     "ROWS_DISTINCT_SEQUENCES",
 ]
@@ -75,6 +77,7 @@ def load_library():
     P = ctypes.c_void_p
     i32, i64, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     rows_p = ctypes.POINTER(_CRows)
+    paged_p = ctypes.POINTER(_CPaged)
     sigs = {
         "dsa_version": ([], ctypes.c_char_p),
         "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -90,6 +93,11 @@ def load_library():
         "dsa_v_up_proj": ([i32, P, P, P, P], ctypes.c_int),
         "dsa_index_share_source": ([i32, i32, i32, i32], i32),
         "dsa_cache_write_workspace_size": ([i32], sz),
+        "dsa_indexer_scores_paged": ([rows_p, paged_p, P, P, P, f32, P, i64, P], ctypes.c_int),
+        "dsa_sparse_mla_paged_workspace_size": ([i32, i32], sz),
+        "dsa_sparse_mla_attn_paged": ([rows_p, paged_p, P, P, P, i32, f32, P, P, P, sz, P], ctypes.c_int),
+        "dsa_decode_step_paged_workspace_size": ([i32, i32, i32], sz),
+        "dsa_decode_step_paged": ([rows_p, paged_p, P, P, P, f32, P, P, f32, i32, P, P, P, P, sz, P], ctypes.c_int),
         "dsa_cache_write": ([i32, P, P, P, P, f32, P, P, f32, P, P, ctypes.c_double, P, P, P, sz, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sigs.items():
@@ -107,6 +115,8 @@ def exported_symbols():
         "dsa_topk_workspace_size", "dsa_topk_select", "dsa_sparse_mla_workspace_size",
         "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step", "dsa_absorb_queries",
         "dsa_v_up_proj", "dsa_index_share_source", "dsa_cache_write_workspace_size", "dsa_cache_write",
+        "dsa_indexer_scores_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_sparse_mla_attn_paged",
+        "dsa_decode_step_paged_workspace_size", "dsa_decode_step_paged",
     ]
 
 
@@ -148,6 +158,14 @@ def _stream(stream, ref):
 ROWS_DISTINCT_SEQUENCES = 1
 
 
+class _CPaged(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+    ]
+
+
 class Rows:
     """Query-row description (dsa_rows_t): device visible_len [R] int32,
     device row_cache_base [R] int64, the host bound max_visible and the
@@ -165,6 +183,25 @@ class Rows:
         self.flags = int(flags)
         self._c = _CRows(self.num_rows, self.max_visible, _ptr(visible_len, "visible_len", (torch.int32,)),
                          _ptr(row_cache_base, "row_cache_base", (torch.int64,)), self.flags)
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+class Paged:
+    """Paged-cache description (dsa_paged_t): device block_table [S, max_blocks]
+    int32 of pool block numbers and the block size (a power of two >= 16).
+    In paged calls a Rows object's row_cache_base holds each row's block-table
+    row."""
+
+    def __init__(self, block_table, block_size):
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+            raise TypeError("block_table must be a contiguous 2-D int32 tensor")
+        self.block_table = block_table
+        self.max_blocks = int(block_table.shape[1])
+        self.block_size = int(block_size)
+        self._c = _CPaged(_ptr(block_table, "block_table", (torch.int32,)), self.max_blocks, self.block_size)
 
     @property
     def c(self):
@@ -275,3 +312,43 @@ def dsa_cache_write(hidden, wk_weight, k_norm_weight, k_norm_bias, k_norm_eps, k
                                _ptr(kv_latent_cache, "kv_latent_cache", _BF16), _ptr(ws, "ws"),
                                ws.numel() * ws.element_size() if ws is not None else 0,
                                _stream(stream, hidden)))
+
+
+def dsa_indexer_scores_paged(rows, paged, q_idx, w, k_pool, index_scale, scores, ld=None, stream=None):
+    lib = load_library()
+    ld = scores.shape[-1] if ld is None else ld
+    _check(lib.dsa_indexer_scores_paged(rows.c, paged.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
+                                        _ptr(k_pool, "k_pool", _BF16), float(index_scale),
+                                        _ptr(scores, "scores", (torch.float32,)), int(ld), _stream(stream, scores)))
+
+
+def dsa_sparse_mla_paged_workspace_size(num_rows, k):
+    return int(load_library().dsa_sparse_mla_paged_workspace_size(int(num_rows), int(k)))
+
+
+def dsa_sparse_mla_attn_paged(rows, paged, q_abs, kv_pool, indices, k, softmax_scale, out_latent, out_lse=None,
+                              ws=None, stream=None):
+    lib = load_library()
+    _check(lib.dsa_sparse_mla_attn_paged(rows.c, paged.c, _ptr(q_abs, "q_abs", _BF16), _ptr(kv_pool, "kv_pool", _BF16),
+                                         _ptr(indices, "indices", (torch.int32,)), int(k), float(softmax_scale),
+                                         _ptr(out_latent, "out_latent", (torch.float32,)),
+                                         _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         _stream(stream, out_latent)))
+
+
+def dsa_decode_step_paged_workspace_size(num_rows, max_visible, k):
+    return int(load_library().dsa_decode_step_paged_workspace_size(int(num_rows), int(max_visible), int(k)))
+
+
+def dsa_decode_step_paged(rows, paged, q_idx, w, k_pool, index_scale, q_abs, kv_pool, softmax_scale, k, indices,
+                          out_latent, out_lse=None, ws=None, stream=None):
+    lib = load_library()
+    _check(lib.dsa_decode_step_paged(rows.c, paged.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
+                                     _ptr(k_pool, "k_pool", _BF16), float(index_scale), _ptr(q_abs, "q_abs", _BF16),
+                                     _ptr(kv_pool, "kv_pool", _BF16), float(softmax_scale), int(k),
+                                     _ptr(indices, "indices", (torch.int32,)),
+                                     _ptr(out_latent, "out_latent", (torch.float32,)),
+                                     _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
+                                     _stream(stream, out_latent)))

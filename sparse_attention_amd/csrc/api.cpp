@@ -126,6 +126,27 @@ dsa_status_t after_launch(hipStream_t stream, const char* what)
 
 size_t scores_ld(int32_t max_visible) { return dsa::align_up((size_t)max_visible, 4); }
 
+constexpr dsa::PagedCache kPacked{nullptr, 0, 0};
+
+// Validates a block-table description against the rows and converts it.
+dsa_status_t check_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, dsa::PagedCache* out)
+{
+    if (!paged) return fail(DSA_ERR_INVALID_ARGUMENT, "paged is NULL");
+    if (!paged->block_table) return fail(DSA_ERR_INVALID_ARGUMENT, "paged->block_table is NULL");
+    if (!aligned(paged->block_table, 4)) return fail(DSA_ERR_MISALIGNED, "block_table not 4-byte aligned");
+    const int32_t B = paged->block_size;
+    if (B < 16 || B > 65536 || (B & (B - 1)) != 0)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "block_size=%d is not a power of two in [16, 65536]", B);
+    const int64_t need = ((int64_t)rows->max_visible + B - 1) / B;
+    if (paged->max_blocks < need)
+        return fail(DSA_ERR_INVALID_ARGUMENT, "max_blocks=%d < %lld blocks of max_visible", paged->max_blocks,
+                    (long long)need);
+    int lg = 0;
+    while ((1 << lg) < B) lg++;
+    *out = dsa::PagedCache{paged->block_table, paged->max_blocks, lg};
+    return DSA_OK;
+}
+
 #define DSA_TRY(expr)                        \
     do {                                     \
         dsa_status_t _s = (expr);            \
@@ -164,11 +185,13 @@ const char* dsa_status_string(dsa_status_t s)
 
 const char* dsa_last_error_detail(void) { return g_detail; }
 
-dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
-                                float index_scale, float* scores, int64_t ld, void* hip_stream)
+}  // extern "C"
+
+namespace {
+
+dsa_status_t indexer_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_idx, const float* w,
+                          const void* k_idx, float index_scale, float* scores, int64_t ld, void* hip_stream)
 {
-    g_detail[0] = '\0';
-    DSA_TRY(check_rows(rows));
     DSA_TRY(check_ptr16(q_idx, "q_idx"));
     DSA_TRY(check_ptr16(w, "w"));
     DSA_TRY(check_ptr16(k_idx, "k_idx"));
@@ -179,8 +202,63 @@ dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const
     hipStream_t st = (hipStream_t)hip_stream;
     dsa::launch_indexer_scores(rows->num_rows, rows->max_visible, rows->visible_len, rows->row_cache_base,
                                (const uint16_t*)q_idx, w, (const uint16_t*)k_idx, index_scale, scores, ld,
-                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, st);
+                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, pc, st);
     return after_launch(st, "indexer");
+}
+
+dsa_status_t attn_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_abs, const void* kv_latent,
+                       const int32_t* indices, int32_t k, float softmax_scale, float* out_latent, float* out_lse,
+                       void* ws, hipStream_t st)
+{
+    const int64_t* base = rows->row_cache_base;
+    const int32_t* idx = indices;
+    void* aws = ws;
+    if (pc.block_table) {
+        // Selected positions -> pool rows (and zero row bases) ahead of the
+        // attention's workspace.
+        const int32_t R = rows->num_rows;
+        char* p = (char*)ws;
+        int32_t* phys = (int32_t*)p;
+        p += dsa::align_up((size_t)R * k * 4, 256);
+        int64_t* zero = (int64_t*)p;
+        p += dsa::align_up((size_t)R * 8, 256);
+        aws = p;
+        dsa::launch_page_indices(R, k, rows->row_cache_base, indices, pc, phys, zero, st);
+        DSA_TRY(after_launch(st, "sparse_mla/page_indices"));
+        base = zero;
+        idx = phys;
+    }
+    dsa::launch_sparse_mla(rows->num_rows, base, (const uint16_t*)q_abs, (const uint16_t*)kv_latent, idx, k,
+                           softmax_scale, out_latent, out_lse, aws, st, pc.block_table != nullptr);
+    return after_launch(st, "sparse_mla");
+}
+
+size_t paged_attn_extra(int32_t num_rows, int32_t k)
+{
+    return dsa::align_up((size_t)num_rows * k * 4, 256) + dsa::align_up((size_t)num_rows * 8, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_indexer_scores(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                                float index_scale, float* scores, int64_t ld, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    return indexer_impl(rows, kPacked, q_idx, w, k_idx, index_scale, scores, ld, hip_stream);
+}
+
+dsa_status_t dsa_indexer_scores_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, const void* q_idx,
+                                      const float* w, const void* k_pool, float index_scale, float* scores,
+                                      int64_t ld, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    dsa::PagedCache pc;
+    DSA_TRY(check_paged(rows, paged, &pc));
+    return indexer_impl(rows, pc, q_idx, w, k_pool, index_scale, scores, ld, hip_stream);
 }
 
 size_t dsa_topk_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
@@ -214,12 +292,21 @@ size_t dsa_sparse_mla_workspace_size(int32_t num_rows, int32_t k)
     return dsa::attn_workspace_bytes(num_rows, k);
 }
 
-dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_abs, const void* kv_latent,
-                                 const int32_t* indices, int32_t k, float softmax_scale, float* out_latent,
-                                 float* out_lse, void* ws, size_t ws_bytes, void* hip_stream)
+size_t dsa_sparse_mla_paged_workspace_size(int32_t num_rows, int32_t k)
 {
-    g_detail[0] = '\0';
-    DSA_TRY(check_rows(rows));
+    if (num_rows < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
+    return paged_attn_extra(num_rows, k) + dsa::attn_workspace_bytes(num_rows, k);
+}
+
+}  // extern "C"
+
+namespace {
+
+dsa_status_t check_attn_args(const dsa_rows_t* rows, const void* q_abs, const void* kv_latent,
+                             const int32_t* indices, int32_t k, float softmax_scale, const float* out_latent,
+                             const float* out_lse)
+{
+    (void)rows;
     DSA_TRY(check_ptr16(q_abs, "q_abs"));
     DSA_TRY(check_ptr16(kv_latent, "kv_latent"));
     DSA_TRY(check_k(k));
@@ -228,12 +315,40 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_abs, cons
     DSA_TRY(check_ptr16(out_latent, "out_latent"));
     if (out_lse && !aligned(out_lse, 4)) return fail(DSA_ERR_MISALIGNED, "out_lse not 4-byte aligned");
     if (!good_scale(softmax_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_abs, const void* kv_latent,
+                                 const int32_t* indices, int32_t k, float softmax_scale, float* out_latent,
+                                 float* out_lse, void* ws, size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_attn_args(rows, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse));
     DSA_TRY(check_ws(ws, ws_bytes, dsa_sparse_mla_workspace_size(rows->num_rows, k)));
     DSA_TRY(check_device());
-    hipStream_t st = (hipStream_t)hip_stream;
-    dsa::launch_sparse_mla(rows->num_rows, rows->row_cache_base, (const uint16_t*)q_abs,
-                           (const uint16_t*)kv_latent, indices, k, softmax_scale, out_latent, out_lse, ws, st);
-    return after_launch(st, "sparse_mla");
+    return attn_impl(rows, kPacked, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse, ws,
+                     (hipStream_t)hip_stream);
+}
+
+dsa_status_t dsa_sparse_mla_attn_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, const void* q_abs,
+                                       const void* kv_pool, const int32_t* indices, int32_t k, float softmax_scale,
+                                       float* out_latent, float* out_lse, void* ws, size_t ws_bytes,
+                                       void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    dsa::PagedCache pc;
+    DSA_TRY(check_paged(rows, paged, &pc));
+    DSA_TRY(check_attn_args(rows, q_abs, kv_pool, indices, k, softmax_scale, out_latent, out_lse));
+    DSA_TRY(check_ws(ws, ws_bytes, dsa_sparse_mla_paged_workspace_size(rows->num_rows, k)));
+    DSA_TRY(check_device());
+    return attn_impl(rows, pc, q_abs, kv_pool, indices, k, softmax_scale, out_latent, out_lse, ws,
+                     (hipStream_t)hip_stream);
 }
 
 size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
@@ -245,13 +360,21 @@ size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int
     return b;
 }
 
-dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
-                             float index_scale, const void* q_abs, const void* kv_latent, float softmax_scale,
-                             int32_t k, int32_t* indices, float* out_latent, float* out_lse, void* ws,
-                             size_t ws_bytes, void* hip_stream)
+size_t dsa_decode_step_paged_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
 {
-    g_detail[0] = '\0';
-    DSA_TRY(check_rows(rows));
+    const size_t b = dsa_decode_step_workspace_size(num_rows, max_visible, k);
+    return b ? b + paged_attn_extra(num_rows, k) : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+dsa_status_t decode_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_idx, const float* w,
+                         const void* k_idx, float index_scale, const void* q_abs, const void* kv_latent,
+                         float softmax_scale, int32_t k, int32_t* indices, float* out_latent, float* out_lse,
+                         void* ws, size_t ws_bytes, void* hip_stream)
+{
     DSA_TRY(check_ptr16(q_idx, "q_idx"));
     DSA_TRY(check_ptr16(w, "w"));
     DSA_TRY(check_ptr16(k_idx, "k_idx"));
@@ -264,7 +387,9 @@ dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const fl
     if (out_lse && !aligned(out_lse, 4)) return fail(DSA_ERR_MISALIGNED, "out_lse not 4-byte aligned");
     if (!good_scale(index_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "index_scale must be finite and > 0");
     if (!good_scale(softmax_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-    DSA_TRY(check_ws(ws, ws_bytes, dsa_decode_step_workspace_size(rows->num_rows, rows->max_visible, k)));
+    DSA_TRY(check_ws(ws, ws_bytes,
+                     pc.block_table ? dsa_decode_step_paged_workspace_size(rows->num_rows, rows->max_visible, k)
+                                    : dsa_decode_step_workspace_size(rows->num_rows, rows->max_visible, k)));
     DSA_TRY(check_device());
 
     hipStream_t st = (hipStream_t)hip_stream;
@@ -279,14 +404,40 @@ dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const fl
 
     dsa::launch_indexer_scores(R, rows->max_visible, rows->visible_len, rows->row_cache_base, (const uint16_t*)q_idx,
                                w, (const uint16_t*)k_idx, index_scale, scores, ld,
-                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, st);
+                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, pc, st);
     DSA_TRY(after_launch(st, "decode_step/indexer"));
     dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, R, rows->max_visible);
     dsa::launch_topk(R, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);
     DSA_TRY(after_launch(st, "decode_step/topk"));
-    dsa::launch_sparse_mla(R, rows->row_cache_base, (const uint16_t*)q_abs, (const uint16_t*)kv_latent, indices, k,
-                           softmax_scale, out_latent, out_lse, aws, st);
-    return after_launch(st, "decode_step/sparse_mla");
+    return attn_impl(rows, pc, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse, aws, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                             float index_scale, const void* q_abs, const void* kv_latent, float softmax_scale,
+                             int32_t k, int32_t* indices, float* out_latent, float* out_lse, void* ws,
+                             size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    return decode_impl(rows, kPacked, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices,
+                       out_latent, out_lse, ws, ws_bytes, hip_stream);
+}
+
+dsa_status_t dsa_decode_step_paged(const dsa_rows_t* rows, const dsa_paged_t* paged, const void* q_idx,
+                                   const float* w, const void* k_pool, float index_scale, const void* q_abs,
+                                   const void* kv_pool, float softmax_scale, int32_t k, int32_t* indices,
+                                   float* out_latent, float* out_lse, void* ws, size_t ws_bytes, void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    dsa::PagedCache pc;
+    DSA_TRY(check_paged(rows, paged, &pc));
+    return decode_impl(rows, pc, q_idx, w, k_pool, index_scale, q_abs, kv_pool, softmax_scale, k, indices,
+                       out_latent, out_lse, ws, ws_bytes, hip_stream);
 }
 
 dsa_status_t dsa_absorb_queries(int32_t num_rows, const void* q_nope, const void* q_pe, const void* kv_b_weight,

@@ -9,13 +9,22 @@
 
 namespace dsa {
 
+// A paged cache: position p of the sequence whose block-table row is s sits at
+// pool row (block_table[s * max_blocks + (p >> log2_block)] << log2_block) |
+// (p & (2^log2_block - 1)).  block_table == nullptr: a packed cache.
+struct PagedCache {
+    const int32_t* block_table;
+    int64_t max_blocks;
+    int log2_block;
+};
+
 // ---- indexer -------------------------------------------------------------
 // Indexer workgroups per row.
 int indexer_pick_chunk(int32_t num_rows, int32_t max_visible);
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis,
                            const int64_t* base, const uint16_t* q, const float* w,
                            const uint16_t* kc, float scale, float* scores, int64_t ld,
-                           bool distinct_sequences, hipStream_t stream);
+                           bool distinct_sequences, const PagedCache& paged, hipStream_t stream);
 
 // ---- top-k ---------------------------------------------------------------
 constexpr int TK_CHUNK = 4096;     // scores one top-k workgroup owns
@@ -45,7 +54,15 @@ int attn_pick_splits(int32_t num_rows, int32_t k);
 size_t attn_workspace_bytes(int32_t num_rows, int32_t k);
 void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa,
                        const uint16_t* kv, const int32_t* idx, int32_t k, float softmax_scale,
-                       float* out, float* lse, void* ws, hipStream_t stream);
+                       float* out, float* lse, void* ws, hipStream_t stream, bool pad_rows = false);
+
+// Logical selection -> physical pool rows of a paged latent cache; a negative
+// entry becomes -1 - (pool row of the sequence's position 0), the row the
+// attention's padding slots then fetch (launch_sparse_mla with pad_rows).
+// Also zeroes the num_rows cache bases the attention adds.  Enqueued on
+// `stream`.
+void launch_page_indices(int32_t num_rows, int32_t k, const int64_t* seq, const int32_t* idx,
+                         const PagedCache& paged, int32_t* phys, int64_t* zero_base, hipStream_t stream);
 
 // ---- projections on either side of the attention -------------------------
 void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* kvb,

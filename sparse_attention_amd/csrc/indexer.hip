@@ -61,10 +61,14 @@ __device__ __forceinline__ bool block_is_shared(const int64_t* __restrict__ base
     return __ballot(mine != base[r0]) == 0ull;
 }
 
+// Paged caches: positions live in blocks of 2^lg rows; row base[r]'s sequence
+// has its physical block numbers in bt[base[r] * mb ..].  Blocks hold at least
+// 16 positions, so a 16-aligned position group never straddles two blocks.
+template <bool PAGED>
 __global__ __launch_bounds__(512) void indexer_tile_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
     const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
-    int64_t ld, int num_rows)
+    int64_t ld, int num_rows, PagedCache pm)
 {
     const int blk = blockIdx.y;
     if (!block_is_shared(base, num_rows, blk)) return;
@@ -103,7 +107,8 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     __syncthreads();
     const int nmax = s_nmax;
     const int ntile = (nmax + IDX_TILE_POS - 1) / IDX_TILE_POS;
-    const uint16_t* kb = kc + base[r0] * 128;
+    const uint16_t* kb = PAGED ? kc : kc + base[r0] * 128;
+    const int32_t* btr = PAGED ? pm.block_table + base[r0] * pm.max_blocks : nullptr;
 
     // Staging roles: thread t moves 16 bytes (chunk t & 15) of positions
     // (t >> 4) + 32 h, h < NH, of a tile.  Positions past nmax are clamped
@@ -114,7 +119,10 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
 #pragma unroll
         for (int h = 0; h < NH; h++) {
             const int pos = min(tt * IDX_TILE_POS + sp_pos + 32 * h, nmax - 1);
-            dst[h] = load_u32x4(kb + (int64_t)pos * 128 + sp_chunk * 8);
+            int64_t prow = pos;
+            if constexpr (PAGED)
+                prow = ((int64_t)btr[pos >> pm.log2_block] << pm.log2_block) | (pos & ((1 << pm.log2_block) - 1));
+            dst[h] = load_u32x4(kb + prow * 128 + sp_chunk * 8);
         }
     };
     int tt = blockIdx.x;
@@ -206,10 +214,11 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
 // which keeps DRAM pages open.  Each wave loads each 16-position group of its
 // next block as soon as the same group of the current block has gone
 // through the matrix cores.
+template <bool PAGED>
 __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
     const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
-    int64_t ld, int num_rows, int skip_shared)
+    int64_t ld, int num_rows, int skip_shared, PagedCache pm)
 {
     const int r = blockIdx.y;
     const int n = vis[r];
@@ -238,24 +247,41 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
         w1[v] = w[r * 32 + 16 + 4 * g + v] * scale;
     }
 
-    const uint16_t* kb = kc + base[r] * 128;
+    const uint16_t* kb = PAGED ? kc : kc + base[r] * 128;
+    const int32_t* btr = PAGED ? pm.block_table + base[r] * pm.max_blocks : nullptr;
     float* srow = scores + (int64_t)r * ld;
 
     bf16x8 kv[IDX_GROUPS][4];
-    auto load = [&](int p0, int u) {
+    // Paged: pool block of each 16-position group of a 64-position block
+    // (wave-uniform; a group never straddles two blocks, and clamped lanes
+    // stay in their group's block).  Looked up one block-step ahead of the
+    // key loads that use it, so those loads do not wait on the table.
+    int pbn[IDX_GROUPS] = {}, pbnn[IDX_GROUPS] = {};
+    auto lookup = [&](int p0, int (&dst)[IDX_GROUPS]) {
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int u = 0; u < IDX_GROUPS; u++) dst[u] = btr[min(p0 + 16 * u, n - 1) >> pm.log2_block];
+        }
+    };
+    auto load = [&](int p0, int u, const int (&pb)[IDX_GROUPS]) {
         // Reads past the row's visible range are clamped onto its last
         // position; their results are never stored.
         const int pc = min(p0 + 16 * u + j, n - 1);
-        const uint16_t* kp = kb + (int64_t)pc * 128 + 8 * g;
+        int64_t prow = pc;
+        if constexpr (PAGED) prow = ((int64_t)pb[u] << pm.log2_block) | (pc & ((1 << pm.log2_block) - 1));
+        const uint16_t* kp = kb + prow * 128 + 8 * g;
 #pragma unroll
         for (int s = 0; s < 4; s++) kv[u][s] = load_bf16x8(kp + 32 * s);
     };
 
+    lookup(wr * IDX_BLOCK, pbn);
 #pragma unroll
-    for (int u = 0; u < IDX_GROUPS; u++) load(wr * IDX_BLOCK, u);
+    for (int u = 0; u < IDX_GROUPS; u++) load(wr * IDX_BLOCK, u, pbn);
+    lookup((wr + nw) * IDX_BLOCK, pbn);
     for (int b = wr; b * IDX_BLOCK < n; b += nw) {
         const int p0 = b * IDX_BLOCK;
         const bool more = (b + nw) * IDX_BLOCK < n;  // wave-uniform
+        if (PAGED && (b + 2 * nw) * IDX_BLOCK < n) lookup((b + 2 * nw) * IDX_BLOCK, pbnn);
         float part[IDX_GROUPS];
 #pragma unroll
         for (int u = 0; u < IDX_GROUPS; u++) {
@@ -268,7 +294,7 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
             }
             // The group's registers are free once its MFMAs have issued: the
             // next block's group goes out now, not after the whole block.
-            if (more) load((b + nw) * IDX_BLOCK, u);
+            if (more) load((b + nw) * IDX_BLOCK, u, pbn);
             float acc = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; v++) acc += w0[v] * relu_bits(a0[v]);
@@ -281,6 +307,10 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
         const float mine = xrow_reduce_scatter4(part);
         const int pos = p0 + 16 * g + j;
         if (pos < n) srow[pos] = mine;
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int u = 0; u < IDX_GROUPS; u++) pbn[u] = pbnn[u];
+        }
     }
 }
 
@@ -300,8 +330,9 @@ int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
 
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis, const int64_t* base,
                            const uint16_t* q, const float* w, const uint16_t* kc, float scale, float* scores,
-                           int64_t ld, bool distinct_sequences, hipStream_t stream)
+                           int64_t ld, bool distinct_sequences, const PagedCache& paged, hipStream_t stream)
 {
+    const bool pg = paged.block_table != nullptr;
     const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
     if (nblk > 0) {
         // Workgroups per shared block: enough for ~2 per CU overall, never
@@ -311,12 +342,20 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
         if (cx > 8) cx = 8;
         if (cx > tiles) cx = tiles;
         if (cx < 1) cx = 1;
-        hipLaunchKernelGGL(indexer_tile_kernel, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc, scale,
-                           scores, ld, num_rows);
+        if (pg)
+            hipLaunchKernelGGL(indexer_tile_kernel<true>, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
+                               scale, scores, ld, num_rows, paged);
+        else
+            hipLaunchKernelGGL(indexer_tile_kernel<false>, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
+                               scale, scores, ld, num_rows, paged);
     }
     dim3 grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
-    hipLaunchKernelGGL(indexer_rows_kernel, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores, ld,
-                       num_rows, nblk > 0 ? 1 : 0);
+    if (pg)
+        hipLaunchKernelGGL(indexer_rows_kernel<true>, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores,
+                           ld, num_rows, nblk > 0 ? 1 : 0, paged);
+    else
+        hipLaunchKernelGGL(indexer_rows_kernel<false>, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores,
+                           ld, num_rows, nblk > 0 ? 1 : 0, paged);
 }
 
 }  // namespace dsa

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
                                                            const int32_t* __restrict__ idx, int k,
-                                                           float scale_log2, int split_len,
+                                                           float scale_log2, int split_len, int pad_rows,
                                                            float* __restrict__ out, float* __restrict__ lse,
                                                            float* __restrict__ part_o,
                                                            float2* __restrict__ part_ml)
@@ -154,8 +154,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
 #pragma unroll
         for (int u = 0; u < 3; u++) {
             const int i = threadIdx.x + AT_THREADS * u;
-            if (i >= nslots) v[u] = -1;
-            last = v[u] >= 0 ? i : last;
+            last = (i < nslots && v[u] >= 0) ? i : last;  // slots past the split hold its last slot: masked by nslots
         }
         if (threadIdx.x < AT_STAGES * AT_TILE) sid[threadIdx.x / AT_TILE][threadIdx.x % AT_TILE] = v[0];
 #pragma unroll
@@ -307,8 +306,11 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
         // consecutive 16-byte LDS chunks (lane order); output wave ob issues
         // instructions q = ob + 8 i (five for ob < 4, four otherwise), and lane
         // L fetches whichever logical chunk belongs at LDS chunk 64 q + L
-        // under the swizzle.  Padding slots fetch the sequence's first latent
-        // row (always present); their softmax weight is zero.  The loads are
+        // under the swizzle.  Padding slots fetch a row that is always present
+        // (their softmax weight is zero, but a non-finite row would still
+        // poison P.V): the sequence's first latent row, or, when pad_rows is
+        // set (index lists translated to pool rows), row -1 - entry, which
+        // the translation points at the sequence's first row.  The loads are
         // spread over the PV MFMAs: a wave waiting for the address unit leaves
         // the matrix core to the other output wave of its SIMD.
         const bool five = ob < AT_GQ - 4 * AT_OWAVES;  // wave-uniform
@@ -325,7 +327,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
             const int p = q * 64 + lane;
             const int row = p / AT_CHUNKS;
             const int part = (p - row * AT_CHUNKS) ^ (row & 7);
-            gather16_to_lds(kvrow + (int64_t)max(gid[i], 0) * 576 + part * 8, dst);
+            const int64_t gr = gid[i] >= 0 ? (int64_t)gid[i] : (pad_rows ? -1 - (int64_t)gid[i] : 0);
+            gather16_to_lds(kvrow + gr * 576 + part * 8, dst);
         };
         auto issue = [&](int t) {
             gather_ids(t);
@@ -544,7 +547,7 @@ size_t attn_workspace_bytes(int32_t num_rows, int32_t k)
 
 void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa, const uint16_t* kv,
                        const int32_t* idx, int32_t k, float softmax_scale, float* out, float* lse, void* ws,
-                       hipStream_t stream)
+                       hipStream_t stream, bool pad_rows)
 {
     const int s = attn_pick_splits(num_rows, k);
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
@@ -556,7 +559,7 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
         part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
     }
     hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k,
-                       softmax_scale * LOG2E, split_len, out, lse, part_o, part_ml);
+                       softmax_scale * LOG2E, split_len, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
     if (s > 1)
         hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(64, num_rows), dim3(128), 0, stream, part_o, part_ml, s,
                            out, lse);

@@ -519,6 +519,140 @@ def test_cache_write_feeds_the_path(dsa, oracle_mod):
     check_attention(out, lse, ref_out, ref_lse, "written caches")
 
 
+# ----------------------------------------------------------------------------- paged caches
+
+NAN_BF16 = 0x7FC0
+
+
+def page_caches(x, seq_base, seq_len, B, seed):
+    """Scatter the packed caches of x into pools of B-row blocks: every
+    sequence gets a random set of pool blocks (spare blocks interleaved);
+    rows no sequence owns hold NaN, so a wrong address poisons the result.
+    Returns (key pool, latent pool, block table [S, max_blocks], block-table
+    row of each query row)."""
+    g = np.random.default_rng(seed)
+    nb = [(int(T) + B - 1) // B for T in seq_len]
+    total = sum(nb) + sum(nb) // 2 + 3
+    perm = g.permutation(total).astype(np.int32)
+    bt = np.zeros((len(seq_len), max(nb)), np.int32)
+    kpool = np.full((total * B, 128), NAN_BF16, np.uint16)
+    lpool = np.full((total * B, 576), NAN_BF16, np.uint16)
+    o = 0
+    for s_, (b0, T) in enumerate(zip(seq_base, seq_len)):
+        blocks = perm[o:o + nb[s_]]
+        o += nb[s_]
+        bt[s_, :nb[s_]] = blocks
+        pos = np.arange(int(T))
+        rows = blocks[pos // B].astype(np.int64) * B + pos % B
+        kpool[rows] = x["k_idx"][b0:b0 + T]
+        lpool[rows] = x["kv_latent"][b0:b0 + T]
+    seq_of_row = (np.searchsorted(seq_base, x["row_cache_base"], side="right") - 1).astype(np.int64)
+    return kpool, lpool, bt, seq_of_row
+
+
+def mixed_paged_inputs():
+    x = mixed_block_inputs()
+    seq_len = np.array([3000, 700, 700, 2100], np.int64)
+    seq_base = np.concatenate([[0], np.cumsum(seq_len)[:-1]]).astype(np.int64)
+    return x, seq_base, seq_len
+
+
+@pytest.mark.parametrize("B", [16, 64, 256])
+def test_paged_calls_equal_packed_calls(dsa, oracle_mod, B):
+    """Indexer (row and shared-block paths), attention and the whole step over
+    paged pools give bitwise the results of the packed calls on the same
+    logical caches; the pools depage (oracle) back to the packed caches; the
+    paged step agrees with the oracle on sampled rows."""
+    x, seq_base, seq_len = mixed_paged_inputs()
+    kpool, lpool, bt, seq_of_row = page_caches(x, seq_base, seq_len, B, seed=B)
+    for s_ in range(len(seq_len)):
+        b0, T = int(seq_base[s_]), int(seq_len[s_])
+        assert np.array_equal(oracle_mod.depage(lpool, bt[s_], T, B), x["kv_latent"][b0:b0 + T])
+        assert np.array_equal(oracle_mod.depage(kpool, bt[s_], T, B), x["k_idx"][b0:b0 + T])
+    d = device_inputs(x)
+    vis = x["visible_len"]
+    R, k = len(vis), 2048
+    rows = make_rows(dsa, vis, x["row_cache_base"])
+    prow = make_rows(dsa, vis, seq_of_row)
+    paged = dsa.Paged(dev(bt), B)
+    kp, lp = dev_bf16(kpool), dev_bf16(lpool)
+    ld = ld_for(int(vis.max()))
+    s_packed = torch.zeros((R, ld), dtype=torch.float32, device=DEV)
+    s_paged = torch.zeros((R, ld), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_scores(rows, d["q_idx"], d["w"], d["k_idx"], 1.0, s_packed)
+    dsa.dsa_indexer_scores_paged(prow, paged, d["q_idx"], d["w"], kp, 1.0, s_paged)
+    torch.cuda.synchronize()
+    a, b = s_packed.cpu().numpy(), s_paged.cpu().numpy()
+    for r in range(R):
+        n = int(vis[r])
+        assert np.array_equal(a[r, :n].view(np.uint32), b[r, :n].view(np.uint32)), r
+    # attention on one index list, packed vs paged
+    idx = run_topk(dsa, vis, a, k)
+    di = dev(idx.astype(np.int32))
+    outs = []
+    for paged_call in (False, True):
+        out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+        if paged_call:
+            ws = dsa.workspace(dsa.dsa_sparse_mla_paged_workspace_size(R, k), DEV)
+            dsa.dsa_sparse_mla_attn_paged(prow, paged, d["q_abs"], lp, di, k, wl.SOFTMAX_SCALE, out, lse, ws)
+        else:
+            ws = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, k), DEV)
+            dsa.dsa_sparse_mla_attn(rows, d["q_abs"], d["kv_latent"], di, k, wl.SOFTMAX_SCALE, out, lse, ws)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    # the whole step
+    idx_a, out_a, lse_a = run_decode_step(dsa, x, d=d)
+    ws = dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, int(vis.max()), k), DEV)
+    ws.fill_(255)
+    idx_b = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out_b = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+    dsa.dsa_decode_step_paged(prow, paged, d["q_idx"], d["w"], kp, wl.INDEX_SCALE, d["q_abs"], lp, wl.SOFTMAX_SCALE,
+                              k, idx_b, out_b, lse_b, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_a, idx_b.cpu().numpy())
+    assert np.array_equal(out_a.view(np.uint32), out_b.cpu().numpy().view(np.uint32))
+    assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
+    # and against the oracle on sampled rows, from the depaged caches
+    rs = [0, 31, 40, 64, 68]
+    y = sub(x, rs)
+    s64, _, idx_ref, out_ref, lse_ref = oracle_mod.decode_step(y["visible_len"], y["row_cache_base"], y["q_idx"],
+                                                               y["w"], y["k_idx"], y["q_abs"], y["kv_latent"], k, 1.0,
+                                                               wl.SOFTMAX_SCALE)
+    assert recall_check(idx_a[rs], idx_ref, s64, y["visible_len"]) >= 0.999
+    ref_out, ref_lse = oracle_mod.sparse_mla(y["row_cache_base"], y["q_abs"], y["kv_latent"], idx_a[rs],
+                                             wl.SOFTMAX_SCALE)
+    check_attention(out_b.cpu().numpy()[rs], lse_b.cpu().numpy()[rs], ref_out, ref_lse, f"paged B={B}")
+
+
+def test_paged_decode_step_full_size_equals_packed(dsa):
+    """64 sequences x 32,768 positions in 64-row blocks scattered over the
+    pool: the paged step gives bitwise the packed step's selection, output
+    and LSE."""
+    w, x = inputs("c3")
+    B = 64
+    kpool, lpool, bt, seq_of_row = page_caches(x, w.seq_base, w.seq_len, B, seed=3)
+    d = device_inputs(x)
+    vis = x["visible_len"]
+    R, k = len(vis), 2048
+    idx_a, out_a, lse_a = run_decode_step(dsa, x, d=d)
+    prow = make_rows(dsa, vis, seq_of_row, flags=dsa.ROWS_DISTINCT_SEQUENCES)
+    paged = dsa.Paged(dev(bt), B)
+    ws = dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, int(vis.max()), k), DEV)
+    idx_b = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out_b = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+    dsa.dsa_decode_step_paged(prow, paged, d["q_idx"], d["w"], dev_bf16(kpool), wl.INDEX_SCALE, d["q_abs"],
+                              dev_bf16(lpool), wl.SOFTMAX_SCALE, k, idx_b, out_b, lse_b, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_a, idx_b.cpu().numpy())
+    assert np.array_equal(out_a.view(np.uint32), out_b.cpu().numpy().view(np.uint32))
+    assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
+
+
 # ----------------------------------------------------------------------------- IndexShare
 
 def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):

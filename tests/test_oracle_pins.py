@@ -438,6 +438,20 @@ def test_cache_rows_norm_invariants(oracle_mod):
     np.testing.assert_allclose(kk[0, 64:], kk[2, 64:], rtol=1e-14)       # dims 64..127 never rotate
 
 
+# --------------------------------------------------------------------------- paged caches
+
+def test_depage_identity_table_and_hand_permutation(oracle_mod):
+    """An identity block table returns the pool's leading rows; a hand-made
+    table over a pool whose rows hold their own row number returns exactly
+    the rows worked out by hand (block 1 -> pool block 2, etc.)."""
+    pool = np.arange(12 * 3).reshape(12, 3)
+    np.testing.assert_array_equal(oracle_mod.depage(pool, [0, 1, 2], 10, 4), pool[:10])
+    pool = np.arange(16)[:, None]                       # row i holds i
+    got = oracle_mod.depage(pool, [3, 0, 2], 10, 4)[:, 0]
+    # logical 0..3 -> pool 12..15, 4..7 -> 0..3, 8..9 -> 8..9
+    np.testing.assert_array_equal(got, [12, 13, 14, 15, 0, 1, 2, 3, 8, 9])
+
+
 # --------------------------------------------------------------------------- IndexShare
 
 def test_index_share_types_match_printed_layer_pattern(oracle_mod):
