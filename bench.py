@@ -363,7 +363,7 @@ def main():
                    "index_heads": 32, "index_dim": 128, "heads": 64, "latent_row": 576},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "indexer_rows_kernel", "kernel_us": round(ms_idx * 1e3, 2),
+                     "kernel": "indexer_rows_kernel<false>", "kernel_us": round(ms_idx * 1e3, 2),
                      "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "projections": projections,
