@@ -118,7 +118,10 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
                                                            float* __restrict__ part_o,
                                                            float2* __restrict__ part_ml)
 {
-    const int r = blockIdx.y;
+    // Rows in reverse: in a causal prefill chunk the last rows select the
+    // most positions, and starting them first shortens the tail (the results
+    // do not depend on the order).
+    const int r = gridDim.y - 1 - blockIdx.y;
     const int sp = blockIdx.x;
     const int nsplit = gridDim.x;
     const int lane = threadIdx.x & 63;
