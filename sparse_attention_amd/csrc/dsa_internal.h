@@ -29,7 +29,7 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
 // ---- top-k ---------------------------------------------------------------
 constexpr int TK_CHUNK = 4096;     // scores one top-k workgroup owns
 constexpr int TK_BINS = 4096;      // 12-bit top radix digit
-constexpr int TK_CAP = 4096;       // candidate slots per row
+constexpr int TK_CAP = 8192;       // candidate slots per row
 constexpr int TK_ROWST = 8;        // u32 words of per-row state
 constexpr int TK_CHUNKST = 4;      // u32 words of per-chunk state
 constexpr int TK_MAX_CHUNKS = 4096;  // DSA_MAX_VISIBLE / TK_CHUNK
@@ -37,10 +37,11 @@ constexpr int TK_MAX_CHUNKS = 4096;  // DSA_MAX_VISIBLE / TK_CHUNK
 constexpr int TR_ROW_PATH_MAXN = 65536;  // calls with max_visible up to this use it
 
 struct TopkWorkspace {
-    uint32_t* hist;            // [R][TK_BINS]
     uint32_t* rowst;           // [R][TK_ROWST]
     uint32_t* chunkst;         // [R][CH][TK_CHUNKST]
     unsigned long long* cand;  // [R][TK_CAP]
+    int32_t* longrows;         // [R]: rows the multi-workgroup kernels own, in row order
+    uint32_t* nlong;           // their count
     int32_t chunks;            // CH
 };
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible);

@@ -321,12 +321,13 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
 
 int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
 {
-    // Workgroups per row: about 8192 in total, but never more waves than
-    // 64-position blocks in the longest row.  Many short waves beat fewer long
-    // ones here (measured: long-context decode 145 vs 152 us at 4096).
+    // Workgroups per row: about 8192 in total, but at least two 64-position
+    // blocks of the longest row per wave (measured on 64 x 32,768 and
+    // 16 x 202,752 decode: 94 and 143 us, against 94-102 and 149 us with 4096
+    // workgroups and 96 and 145 us with one block per wave).
     const int64_t blocks = (max_visible + IDX_BLOCK - 1) / IDX_BLOCK;
     int64_t cx = (8192 + num_rows - 1) / num_rows;
-    const int64_t cap = (blocks + IDX_WAVES - 1) / IDX_WAVES;
+    const int64_t cap = (blocks + 2 * IDX_WAVES - 1) / (2 * IDX_WAVES);
     if (cx > cap) cx = cap;
     if (cx < 1) cx = 1;
     return (int)cx;

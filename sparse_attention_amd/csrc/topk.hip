@@ -13,19 +13,23 @@
 // Longer rows are split over workgroups, because a single CU streams too
 // slowly for them; only integer counts are combined across workgroups, so the
 // result does not depend on scheduling:
-//   1. zero     per-row histogram and counters
-//   2. hist     rows x chunks: LDS histogram of the top 12 key bits, merged
-//               into the row histogram with integer atomics
-//   3. filter   rows x chunks: every workgroup finds the same threshold bin b0
-//               from the row histogram; counts the chunk's elements above b0
-//               and appends the elements inside b0 (candidates) to a per-row
-//               candidate list
-//   4. resolve  one workgroup per row: radix-selects the remaining 20 key bits
-//               among the candidates (or, if they overflowed the list, among
-//               the row itself) to get the exact threshold key theta and the
-//               number need_eq of theta-valued elements to keep; then turns
-//               per-chunk counts into per-chunk output offsets
-//   5. write    rows x chunks: ordered compaction; an element is kept if its
+//   1. sample   per long row, in the one-workgroup-per-row kernel (which owns
+//               the short rows): a lower bound theta_lo on the k-th largest
+//               key, the exact order statistic of 8,192 sampled keys at about
+//               1.5x the k-th largest's expected sample rank.  With more than
+//               64 rows, one workgroup then lists the long rows (in row
+//               order) and the kernels below walk that list with fixed grids;
+//               else they run one workgroup row per query row
+//   2. filter   rows x chunks: elements with key >= theta_lo are appended to a
+//               per-row candidate list (one atomic slot reservation per
+//               workgroup; only the set matters)
+//   3. resolve  one workgroup per row: a three-round radix select (12, 12, 8
+//               key bits) for the exact threshold key theta and the number
+//               need_eq of theta-valued elements to keep, over the candidates
+//               when they number at least k and fit the list (then they hold
+//               theta and everything above it), else over the row itself;
+//               then per-chunk output offsets by block scans
+//   4. write    rows x chunks: ordered compaction; an element is kept if its
 //               key exceeds theta, or equals theta and fewer than need_eq
 //               theta-valued elements precede it in position order
 #include "dsa_device.h"
@@ -40,9 +44,9 @@ constexpr int TK_PER_THREAD = TK_CHUNK / TK_THREADS;  // 16
 constexpr int RS_THREADS = 512;
 
 // Row state words.
-constexpr int RS_CAND = 0, RS_B0 = 1, RS_GT0 = 2, RS_THETA = 3, RS_NEEDEQ = 4;
+constexpr int RS_CAND = 0, RS_THLO = 1, RS_THETA = 3, RS_NEEDEQ = 4;
 // Chunk state words.
-constexpr int CS_GTBIN = 0, CS_OFFSET = 1, CS_EQBEFORE = 2;
+constexpr int CS_OFFSET = 1, CS_EQBEFORE = 2;
 
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64).
 template <int NT>
@@ -120,13 +124,108 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* h, uint32_t n
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* __restrict__ hist, uint32_t* __restrict__ rowst)
+// Sampled lower bound of one long row (n > TR_ROW_PATH_MAXN, so n is well
+// above TS_SAMPLES): TS_BLOCKS blocks of TS_BLOCK consecutive positions spread
+// evenly over the row; theta_lo = the key of the rho-th largest sample, with
+// rho = 1.5 x the rank the k-th largest element has in the sample (k m / n)
+// plus 16, found exactly by a three-round radix select over the sample keys.
+// Stores theta_lo and clears the row's candidate counter.  Called by a whole
+// TP_THREADS workgroup; keys[] and h[] are its LDS.
+constexpr int TP_THREADS = 1024;
+constexpr int TS_BLOCKS = 32;
+constexpr int TS_BLOCK = 256;
+constexpr int TS_SAMPLES = TS_BLOCKS * TS_BLOCK;  // 8 per thread
+static_assert(TS_SAMPLES == 8 * TP_THREADS, "eight samples per thread");
+
+__device__ void topk_sample_row(const float* __restrict__ row, int n, int k, uint32_t* __restrict__ rs,
+                                uint32_t* keys, uint32_t* h, uint32_t* sh, uint32_t* s_bin, uint32_t* s_above)
 {
-    const int r = blockIdx.x;
-    uint32_t* h = hist + (int64_t)r * TK_BINS;
-    for (int i = threadIdx.x; i < TK_BINS; i += 256) h[i] = 0u;
-    if (threadIdx.x < TK_ROWST) rowst[(int64_t)r * TK_ROWST + threadIdx.x] = 0u;
+    const int t = threadIdx.x;
+    const int blk = t >> 5, o = 8 * (t & 31);
+    // 4-aligned block start, the block inside the row: start + 255 < n.
+    const int start = (int)(((int64_t)(n - TS_BLOCK) * blk / (TS_BLOCKS - 1)) & ~3LL);
+    const float4 v0 = *reinterpret_cast<const float4*>(row + start + o);
+    const float4 v1 = *reinterpret_cast<const float4*>(row + start + o + 4);
+    uint32_t kk[8] = {score_key(v0.x), score_key(v0.y), score_key(v0.z), score_key(v0.w),
+                      score_key(v1.x), score_key(v1.y), score_key(v1.z), score_key(v1.w)};
+    for (int i = t; i < TK_BINS; i += TP_THREADS) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; e++) atomicAdd(&h[kk[e] >> 20], 1u);
+    __syncthreads();
+    const uint32_t rho = min((uint32_t)TS_SAMPLES,
+                             (uint32_t)((3LL * k * TS_SAMPLES + 2LL * n - 1) / (2LL * n)) + 16u);
+    find_threshold_bin<TP_THREADS, TK_BINS>(h, rho, s_bin, s_above, sh);
+    const uint32_t b0 = *s_bin, need1 = rho - *s_above;
+    for (int i = t; i < TK_BINS; i += TP_THREADS) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        if ((kk[e] >> 20) == b0) atomicAdd(&h[(kk[e] >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    find_threshold_bin<TP_THREADS, TK_BINS>(h, need1, s_bin, s_above, sh);
+    const uint32_t pre = (b0 << 12) | *s_bin, need2 = need1 - *s_above;
+    for (int i = t; i < 256; i += TP_THREADS) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        if ((kk[e] >> 8) == pre) atomicAdd(&h[kk[e] & 0xffu], 1u);
+    __syncthreads();
+    if (t < 256) {
+        // 256 bins over 1024 threads: the bin search runs in the first 256.
+        uint32_t c = h[255 - t];
+        const uint32_t incl = wave_inclusive_scan(c);
+        if ((t & 63) == 63) sh[t >> 6] = incl;
+        keys[t] = incl;  // scratch: inclusive count from the top, per bin
+    }
+    __syncthreads();
+    if (t < 256) {
+        uint32_t before = 0;
+        for (int w = 0; w < (t >> 6); w++) before += sh[w];
+        const uint32_t incl = before + keys[t], c = h[255 - t];
+        if (incl >= need2 && incl - c < need2) {
+            rs[RS_THLO] = (pre << 8) | (uint32_t)(255 - t);
+            rs[RS_CAND] = 0u;
+        }
+    }
+    __syncthreads();  // LDS free for the caller's next row
 }
+
+// Many rows: one workgroup lists, in row order, the rows the multi-workgroup
+// kernels own (n > min_n, hence n > k); the kernels below walk that list with
+// grids of a fixed size, so a call with many short rows and a few long ones
+// does not launch rows x chunks workgroups that would mostly exit at once.
+// (Few rows: no list; the kernels below run one workgroup row per query row.)
+__global__ __launch_bounds__(TP_THREADS) void topk_prep_kernel(const int32_t* __restrict__ vis, int num_rows,
+                                                               int min_n, int32_t* __restrict__ longrows,
+                                                               uint32_t* __restrict__ nlong)
+{
+    __shared__ uint32_t sh[TP_THREADS / 64];
+    // Thread t owns rows [t * per, (t + 1) * per): count, scan, then write.
+    const int per = (num_rows + TP_THREADS - 1) / TP_THREADS;
+    const int r0 = threadIdx.x * per, r1 = min(num_rows, r0 + per);
+    uint32_t cnt = 0;
+    for (int r = r0; r < r1; r++) cnt += vis[r] > min_n ? 1u : 0u;
+    uint32_t total;
+    uint32_t slot = block_exclusive_scan<TP_THREADS>(cnt, &total, sh);
+    for (int r = r0; r < r1; r++)
+        if (vis[r] > min_n) longrows[slot++] = r;
+    if (threadIdx.x == 0) *nlong = total;
+}
+
+// Item li of the list-walking kernels: query row li itself (direct mode,
+// longrows == nullptr; short rows are skipped), or list entry li.
+__device__ __forceinline__ uint32_t topk_items(const int32_t* longrows, const uint32_t* nlong, int num_rows)
+{
+    return longrows ? *nlong : (uint32_t)num_rows;
+}
+__device__ __forceinline__ int topk_item_row(const int32_t* longrows, uint32_t li)
+{
+    return longrows ? longrows[li] : (int)li;
+}
+
+// Grid rows of the list-walking kernels.
+constexpr int TK_LIST_GRID = 64;
 
 // Loads the TK_PER_THREAD keys of thread `tid` in chunk [start, end): thread
 // tid owns positions start + 16 tid .. +15 (position order = thread order).
@@ -153,126 +252,139 @@ __device__ __forceinline__ void load_chunk_keys(const float* __restrict__ row, i
     }
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const int32_t* __restrict__ vis,
-                                                               const float* __restrict__ scores, int64_t ld, int k,
-                                                               uint32_t* __restrict__ hist, int min_n)
-{
-    const int r = blockIdx.y;
-    const int n = vis[r];
-    const int start = blockIdx.x * TK_CHUNK;
-    if (n <= k || n <= min_n || start >= n) return;
-    const int end = min(n, start + TK_CHUNK);
-    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
-    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = 0u;
-    __syncthreads();
-    uint32_t key[TK_PER_THREAD], present;
-    load_chunk_keys(scores + (int64_t)r * ld, start, end, key, present);
-#pragma unroll
-    for (int i = 0; i < TK_PER_THREAD; i++)
-        if (present & (1u << i)) atomicAdd(&h[key[i] >> 20], 1u);
-    __syncthreads();
-    uint32_t* gh = hist + (int64_t)r * TK_BINS;
-    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS)
-        if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
+// Rows x chunks: every element whose key is >= the row's sampled bound
+// theta_lo becomes a candidate (key, position); one integer atomic per
+// workgroup reserves its slots in the row's list (the list order is
+// irrelevant: the selection below depends only on the set).
 __global__ __launch_bounds__(TK_THREADS) void topk_filter_kernel(const int32_t* __restrict__ vis,
-                                                                 const float* __restrict__ scores, int64_t ld, int k,
-                                                                 const uint32_t* __restrict__ hist,
+                                                                 const float* __restrict__ scores, int64_t ld,
                                                                  uint32_t* __restrict__ rowst,
-                                                                 uint32_t* __restrict__ chunkst, int chunks,
-                                                                 unsigned long long* __restrict__ cand, int min_n)
+                                                                 unsigned long long* __restrict__ cand,
+                                                                 const int32_t* __restrict__ longrows,
+                                                                 const uint32_t* __restrict__ nlong, int num_rows,
+                                                                 int min_n)
 {
-    const int r = blockIdx.y;
-    const int c = blockIdx.x;
-    const int n = vis[r];
-    const int start = c * TK_CHUNK;
-    if (n <= k || n <= min_n || start >= n) return;
-    const int end = min(n, start + TK_CHUNK);
-    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
     __shared__ uint32_t sh[TK_THREADS / 64];
-    __shared__ uint32_t s_b0, s_gt0, s_base;
-    const uint32_t* gh = hist + (int64_t)r * TK_BINS;
-    for (int i = threadIdx.x; i < TK_BINS; i += TK_THREADS) h[i] = gh[i];
-    __syncthreads();
-    find_threshold_bin<TK_THREADS, TK_BINS>(h, (uint32_t)k, &s_b0, &s_gt0, sh);
-    const uint32_t b0 = s_b0;
-
-    uint32_t key[TK_PER_THREAD], present;
-    load_chunk_keys(scores + (int64_t)r * ld, start, end, key, present);
-    uint32_t gt = 0, nc = 0;
+    __shared__ uint32_t s_base;
+    const uint32_t nl = topk_items(longrows, nlong, num_rows);
+    for (uint32_t li = blockIdx.y; li < nl; li += gridDim.y) {
+        const int r = topk_item_row(longrows, li);
+        const int n = vis[r];
+        const int start = blockIdx.x * TK_CHUNK;
+        if (n <= min_n || start >= n) continue;
+        const int end = min(n, start + TK_CHUNK);
+        uint32_t* rs = rowst + (int64_t)r * TK_ROWST;
+        const uint32_t thlo = rs[RS_THLO];
+        uint32_t key[TK_PER_THREAD], present;
+        load_chunk_keys(scores + (int64_t)r * ld, start, end, key, present);
+        uint32_t sel = 0u;
 #pragma unroll
-    for (int i = 0; i < TK_PER_THREAD; i++) {
-        if (!(present & (1u << i))) continue;
-        const uint32_t b = key[i] >> 20;
-        gt += (b > b0) ? 1u : 0u;
-        nc += (b == b0) ? 1u : 0u;
-    }
-    uint32_t gt_total, nc_total;
-    (void)block_exclusive_scan<TK_THREADS>(gt, &gt_total, sh);
-    const uint32_t nc_pre = block_exclusive_scan<TK_THREADS>(nc, &nc_total, sh);
-    if (threadIdx.x == 0) {
-        s_base = nc_total ? atomicAdd(&rowst[(int64_t)r * TK_ROWST + RS_CAND], nc_total) : 0u;
-        chunkst[((int64_t)r * chunks + c) * TK_CHUNKST + CS_GTBIN] = gt_total;
-        if (c == 0) {
-            rowst[(int64_t)r * TK_ROWST + RS_B0] = b0;
-            rowst[(int64_t)r * TK_ROWST + RS_GT0] = s_gt0;
-        }
-    }
-    __syncthreads();
-    uint32_t slot = s_base + nc_pre;
-    unsigned long long* cr = cand + (int64_t)r * TK_CAP;
-    const int t0 = start + TK_PER_THREAD * threadIdx.x;
+        for (int i = 0; i < TK_PER_THREAD; i++)
+            if (((present >> i) & 1u) && key[i] >= thlo) sel |= 1u << i;
+        uint32_t total;
+        const uint32_t pre = block_exclusive_scan<TK_THREADS>(__popc(sel), &total, sh);
+        if (threadIdx.x == 0) s_base = total ? atomicAdd(&rs[RS_CAND], total) : 0u;
+        __syncthreads();
+        uint32_t slot = s_base + pre;
+        unsigned long long* cr = cand + (int64_t)r * TK_CAP;
+        const int t0 = start + TK_PER_THREAD * threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < TK_PER_THREAD; i++) {
-        if (!(present & (1u << i))) continue;
-        if ((key[i] >> 20) != b0) continue;
-        if (slot < (uint32_t)TK_CAP) cr[slot] = ((unsigned long long)key[i] << 32) | (uint32_t)(t0 + i);
-        slot++;
+        for (int i = 0; i < TK_PER_THREAD; i++)
+            if ((sel >> i) & 1u) {
+                if (slot < (uint32_t)TK_CAP) cr[slot] = ((unsigned long long)key[i] << 32) | (uint32_t)(t0 + i);
+                slot++;
+            }
+        __syncthreads();  // s_base is read before the next item overwrites it
     }
 }
 
-// One workgroup per row (rows with n > k only).
+// One workgroup per long row: the exact threshold key theta (the k-th
+// largest key) and need_eq (theta-valued elements to keep) by a three-round
+// radix select, then per-chunk output offsets.  Fast path: the candidates
+// (every element >= theta_lo) number at least k and fit the list, so theta
+// is among them and every element above theta is a candidate.  Otherwise (a
+// misleading sample, or ties filling the list) the same rounds run over the
+// whole row, read from memory: slower, equally exact.
 __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t* __restrict__ vis,
                                                                   const float* __restrict__ scores, int64_t ld,
                                                                   int k, uint32_t* __restrict__ rowst,
                                                                   uint32_t* __restrict__ chunkst, int chunks,
-                                                                  const unsigned long long* __restrict__ cand, int min_n)
+                                                                  const unsigned long long* __restrict__ cand,
+                                                                  const int32_t* __restrict__ longrows,
+                                                                  const uint32_t* __restrict__ nlong, int num_rows,
+                                                                  int min_n)
 {
-    const int r = blockIdx.x;
-    const int n = vis[r];
-    if (n <= k || n <= min_n) return;
     __shared__ unsigned long long cl[TK_CAP];
     __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
-    __shared__ uint32_t cgt[TK_MAX_CHUNKS / 2];  // per-chunk counts, see note below
+    __shared__ uint32_t cgt[TK_MAX_CHUNKS / 2];  // per-chunk counts, in windows of chunks
     __shared__ uint32_t ceq[TK_MAX_CHUNKS / 2];
     __shared__ uint32_t sh[RS_THREADS / 64];
     __shared__ uint32_t s_bin, s_above;
+    const uint32_t nl = topk_items(longrows, nlong, num_rows);
+    for (uint32_t li = blockIdx.x; li < nl; li += gridDim.x) {
+    const int r = topk_item_row(longrows, li);
+    const int n = vis[r];
+    if (n <= min_n) continue;
+    __syncthreads();  // the previous item is done with the shared state
 
     uint32_t* rs = rowst + (int64_t)r * TK_ROWST;
     const uint32_t m = rs[RS_CAND];
-    const uint32_t b0 = rs[RS_B0];
-    const uint32_t need = (uint32_t)k - rs[RS_GT0];
-    const bool overflow = m > (uint32_t)TK_CAP;
+    const bool fast = m >= (uint32_t)k && m <= (uint32_t)TK_CAP;
     const float* row = scores + (int64_t)r * ld;
     const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;
-
-    if (!overflow)
+    if (fast)
         for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) cl[i] = cand[(int64_t)r * TK_CAP + i];
 
-    // Digit 2: key bits 19..8 among elements whose top 12 bits equal b0.
+    uint32_t theta, need_eq;
+    if (fast) {
+        // Radix rounds relative to the candidates' own key range [theta_lo,
+        // max]: 12 bits of (key - lo) per round, so the candidates (which
+        // share few top-bit bins) spread over the histogram instead of piling
+        // onto a handful of LDS counters.
+        uint32_t mx = 0u;
+        for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) mx = max(mx, (uint32_t)(cl[i] >> 32));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+        if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < RS_THREADS / 64; w++) mx = max(mx, sh[w]);
+        __syncthreads();
+        uint32_t lo = rs[RS_THLO], hi = mx, nd = (uint32_t)k;
+        for (;;) {
+            const uint32_t span = hi - lo;
+            const int shift = span < (uint32_t)TK_BINS ? 0 : (32 - __clz(span)) - 12;
+            for (int i = threadIdx.x; i < TK_BINS; i += RS_THREADS) h[i] = 0u;
+            __syncthreads();
+            for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) {
+                const uint32_t key = (uint32_t)(cl[i] >> 32);
+                if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> shift], 1u);
+            }
+            __syncthreads();
+            find_threshold_bin<RS_THREADS, TK_BINS>(h, nd, &s_bin, &s_above, sh);
+            nd -= s_above;
+            lo += s_bin << shift;
+            hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << shift) - 1));
+            if (shift == 0) break;  // wave-uniform: every thread holds the same lo, hi
+        }
+        theta = lo;
+        need_eq = nd;
+    } else {
+    // Whole row, absolute key bits.  Round 1: bits 31..20.
     for (int i = threadIdx.x; i < TK_BINS; i += RS_THREADS) h[i] = 0u;
     __syncthreads();
-    if (!overflow) {
-        for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) {
-            const uint32_t key = (uint32_t)(cl[i] >> 32);
-            atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
-        }
-    } else {
-        for (int t = threadIdx.x; t < n; t += RS_THREADS) {
-            const uint32_t key = score_key(row[t]);
-            if ((key >> 20) == b0) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
-        }
+    for (int t = threadIdx.x; t < n; t += RS_THREADS) atomicAdd(&h[score_key(row[t]) >> 20], 1u);
+    __syncthreads();
+    find_threshold_bin<RS_THREADS, TK_BINS>(h, (uint32_t)k, &s_bin, &s_above, sh);
+    const uint32_t b0 = s_bin;
+    const uint32_t need = (uint32_t)k - s_above;
+
+    // Round 2: key bits 19..8 among keys whose top 12 bits equal b0.
+    for (int i = threadIdx.x; i < TK_BINS; i += RS_THREADS) h[i] = 0u;
+    __syncthreads();
+    for (int t = threadIdx.x; t < n; t += RS_THREADS) {
+        const uint32_t key = score_key(row[t]);
+        if ((key >> 20) == b0) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
     }
     __syncthreads();
     find_threshold_bin<RS_THREADS, TK_BINS>(h, need, &s_bin, &s_above, sh);
@@ -280,28 +392,23 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
     const uint32_t need2 = need - s_above;
     const uint32_t pre20 = (b0 << 12) | b1;  // top 24 bits of theta
 
-    // Digit 3: key bits 7..0 among elements whose top 24 bits equal pre20.
+    // Round 3: key bits 7..0 among keys whose top 24 bits equal pre20.
     for (int i = threadIdx.x; i < 512; i += RS_THREADS) h[i] = 0u;
     __syncthreads();
-    if (!overflow) {
-        for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) {
-            const uint32_t key = (uint32_t)(cl[i] >> 32);
-            if ((key >> 8) == pre20) atomicAdd(&h[key & 0xffu], 1u);
-        }
-    } else {
-        for (int t = threadIdx.x; t < n; t += RS_THREADS) {
-            const uint32_t key = score_key(row[t]);
-            if ((key >> 8) == pre20) atomicAdd(&h[key & 0xffu], 1u);
-        }
+    for (int t = threadIdx.x; t < n; t += RS_THREADS) {
+        const uint32_t key = score_key(row[t]);
+        if ((key >> 8) == pre20) atomicAdd(&h[key & 0xffu], 1u);
     }
     __syncthreads();
     find_threshold_bin<RS_THREADS, 512>(h, need2, &s_bin, &s_above, sh);
-    const uint32_t theta = (pre20 << 8) | s_bin;
-    const uint32_t need_eq = need2 - s_above;
+    theta = (pre20 << 8) | s_bin;
+    need_eq = need2 - s_above;
+    }
 
-    // Per-chunk counts, inside bin b0, of keys > theta and keys == theta.
-    // Chunks are processed in windows of TK_MAX_CHUNKS / 2 to bound LDS.
-    uint32_t offs = 0, eqb = 0;  // running totals (thread 0)
+    // Per-chunk counts of keys > theta and keys == theta (all such elements
+    // are candidates on the fast path).  Chunks are processed in windows of
+    // TK_MAX_CHUNKS / 2 to bound LDS.
+    uint32_t offs = 0, eqb = 0;  // running totals (the same in every thread)
     for (int w0 = 0; w0 < nch; w0 += TK_MAX_CHUNKS / 2) {
         const int w1 = min(nch, w0 + TK_MAX_CHUNKS / 2);
         for (int i = threadIdx.x; i < w1 - w0; i += RS_THREADS) {
@@ -309,11 +416,10 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
             ceq[i] = 0u;
         }
         __syncthreads();
-        if (!overflow) {
+        if (fast) {
             for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) {
                 const uint32_t key = (uint32_t)(cl[i] >> 32);
-                const int pos = (int)(uint32_t)cl[i];
-                const int cc = pos / TK_CHUNK;
+                const int cc = (int)(uint32_t)cl[i] / TK_CHUNK;
                 if (cc < w0 || cc >= w1) continue;
                 if (key > theta) atomicAdd(&cgt[cc - w0], 1u);
                 else if (key == theta) atomicAdd(&ceq[cc - w0], 1u);
@@ -322,25 +428,32 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
             const int t_end = min(n, w1 * TK_CHUNK);
             for (int t = w0 * TK_CHUNK + threadIdx.x; t < t_end; t += RS_THREADS) {
                 const uint32_t key = score_key(row[t]);
-                if ((key >> 20) != b0) continue;
                 const int cc = t / TK_CHUNK - w0;
                 if (key > theta) atomicAdd(&cgt[cc], 1u);
                 else if (key == theta) atomicAdd(&ceq[cc], 1u);
             }
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int cc = w0; cc < w1; cc++) {
-                uint32_t* cs = chunkst + ((int64_t)r * chunks + cc) * TK_CHUNKST;
-                const uint32_t gtc = cs[CS_GTBIN] + cgt[cc - w0];
-                const uint32_t eqc = ceq[cc - w0];
-                const uint32_t left = need_eq > eqb ? need_eq - eqb : 0u;
-                const uint32_t take = left < eqc ? left : eqc;
-                cs[CS_OFFSET] = offs;
-                cs[CS_EQBEFORE] = eqb;
-                offs += gtc + take;
-                eqb += eqc;
+        // Output offsets in chunk order: chunk i keeps its elements above
+        // theta plus as many theta-valued ones as remain of need_eq after the
+        // chunks before it (two block scans per RS_THREADS chunks).
+        for (int c0 = 0; c0 < w1 - w0; c0 += RS_THREADS) {
+            const int i = c0 + threadIdx.x;
+            const bool in = i < w1 - w0;
+            const uint32_t gtc = in ? cgt[i] : 0u;
+            const uint32_t eqc = in ? ceq[i] : 0u;
+            uint32_t eq_tot, o_tot;
+            const uint32_t eq_before = eqb + block_exclusive_scan<RS_THREADS>(eqc, &eq_tot, sh);
+            const uint32_t left = need_eq > eq_before ? need_eq - eq_before : 0u;
+            const uint32_t take = left < eqc ? left : eqc;
+            const uint32_t o_before = offs + block_exclusive_scan<RS_THREADS>(gtc + take, &o_tot, sh);
+            if (in) {
+                uint32_t* cs = chunkst + ((int64_t)r * chunks + w0 + i) * TK_CHUNKST;
+                cs[CS_OFFSET] = o_before;
+                cs[CS_EQBEFORE] = eq_before;
             }
+            offs += o_tot;
+            eqb += eq_tot;
         }
         __syncthreads();
     }
@@ -348,30 +461,28 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
         rs[RS_THETA] = theta;
         rs[RS_NEEDEQ] = need_eq;
     }
+    }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(const int32_t* __restrict__ vis,
                                                                 const float* __restrict__ scores, int64_t ld, int k,
                                                                 const uint32_t* __restrict__ rowst,
                                                                 const uint32_t* __restrict__ chunkst, int chunks,
-                                                                int32_t* __restrict__ indices, int min_n)
+                                                                int32_t* __restrict__ indices,
+                                                                const int32_t* __restrict__ longrows,
+                                                                const uint32_t* __restrict__ nlong, int num_rows,
+                                                                int min_n)
 {
-    const int r = blockIdx.y;
+    __shared__ uint32_t sh[TK_THREADS / 64];
+    const uint32_t nl = topk_items(longrows, nlong, num_rows);
+    for (uint32_t li = blockIdx.y; li < nl; li += gridDim.y) {
+    const int r = topk_item_row(longrows, li);
     const int c = blockIdx.x;
-    const int n = vis[r];
-    if (n <= min_n) return;  // the one-workgroup-per-row kernel owns this row
+    const int n = vis[r];  // > min_n > k for the rows this path owns
     const int start = c * TK_CHUNK;
     int32_t* out = indices + (int64_t)r * k;
-    if (n <= k) {
-        // Every visible position is kept; chunk 0 also writes the padding.
-        for (int t = start + threadIdx.x; t < min(n, start + TK_CHUNK); t += TK_THREADS) out[t] = t;
-        if (c == 0)
-            for (int t = n + threadIdx.x; t < k; t += TK_THREADS) out[t] = -1;
-        return;
-    }
-    if (start >= n) return;
+    if (n <= min_n || start >= n) continue;
     const int end = min(n, start + TK_CHUNK);
-    __shared__ uint32_t sh[TK_THREADS / 64];
     const uint32_t theta = rowst[(int64_t)r * TK_ROWST + RS_THETA];
     const uint32_t need_eq = rowst[(int64_t)r * TK_ROWST + RS_NEEDEQ];
     const uint32_t* cs = chunkst + ((int64_t)r * chunks + c) * TK_CHUNKST;
@@ -406,11 +517,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_write_kernel(const int32_t* _
             if (pos < (uint32_t)k) out[pos] = t0 + i;
             pos++;
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per row, for rows of at most TR_ROW_PATH_MAXN positions.  The
-// row is read from memory once, into registers: thread t holds the scores of
+// One workgroup per row, for rows of at most TR_ROW_PATH_MAXN positions (for
+// longer rows the workgroup runs the sampling step of the multi-workgroup
+// path and leaves the rest to it).  The row is read from memory once, into
+// registers: thread t holds the scores of
 // positions 4 (t + TR_THREADS u) + q, q < 4, for every group u the row
 // reaches.  A workgroup of 16 waves shares one CU, so the per-element work is
 // kept to a few VALU operations: the full pass compares raw floats (exact:
@@ -490,11 +604,12 @@ __device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0
 
 __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __restrict__ vis,
                                                                const float* __restrict__ scores, int64_t ld,
-                                                               int k, int32_t* __restrict__ indices, int max_n)
+                                                               int k, int32_t* __restrict__ indices, int max_n,
+                                                               uint32_t* __restrict__ long_rowst)
 {
+    static_assert(TR_THREADS == TP_THREADS, "the sampling step runs on this workgroup");
     const int r = blockIdx.x;
     const int n = vis[r];
-    if (n > max_n) return;  // the multi-workgroup kernels own this row
     int32_t* out = indices + (int64_t)r * k;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -511,6 +626,13 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
     __shared__ float wmax[TR_WAVES];
     __shared__ uint32_t sh[TR_THREADS / 64];
     __shared__ uint32_t s_bin, s_above, s_cnt;
+    if (n > max_n) {
+        // The multi-workgroup kernels own this row; its first step, the
+        // sampled lower bound, runs here (the candidate list is free LDS).
+        topk_sample_row(scores + (int64_t)r * ld, n, k, long_rowst + (int64_t)r * TK_ROWST,
+                        reinterpret_cast<uint32_t*>(cand), hs, sh, &s_bin, &s_above);
+        return;
+    }
 
     // ---- the row, into registers ---------------------------------------------
     const float* row = scores + (int64_t)r * ld;
@@ -809,10 +931,11 @@ size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible)
     const size_t R = (size_t)num_rows;
     const size_t CH = (size_t)((max_visible + TK_CHUNK - 1) / TK_CHUNK);
     size_t b = 0;
-    b += align_up(R * TK_BINS * 4, 256);
     b += align_up(R * TK_ROWST * 4, 256);
     b += align_up(R * CH * TK_CHUNKST * 4, 256);
     b += align_up(R * TK_CAP * 8, 256);
+    b += align_up(R * 4, 256);  // list of long rows
+    b += 256;                   // its length
     return b;
 }
 
@@ -822,13 +945,15 @@ TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visib
     const int32_t CH = (max_visible + TK_CHUNK - 1) / TK_CHUNK;
     char* p = (char*)ws;
     TopkWorkspace tw;
-    tw.hist = (uint32_t*)p;
-    p += align_up(R * TK_BINS * 4, 256);
     tw.rowst = (uint32_t*)p;
     p += align_up(R * TK_ROWST * 4, 256);
     tw.chunkst = (uint32_t*)p;
     p += align_up(R * (size_t)CH * TK_CHUNKST * 4, 256);
     tw.cand = (unsigned long long*)p;
+    p += align_up(R * TK_CAP * 8, 256);
+    tw.longrows = (int32_t*)p;
+    p += align_up(R * 4, 256);
+    tw.nlong = (uint32_t*)p;
     tw.chunks = CH;
     return tw;
 }
@@ -839,20 +964,29 @@ void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, cons
     // Rows of up to TR_ROW_PATH_MAXN positions take one workgroup each; longer
     // rows (present only when max_visible exceeds it) are split over
     // workgroups.  Each kernel skips the rows the other path owns.
+    // The row kernel also samples the long rows (the first step of their
+    // path), so it goes first.
+    const bool has_long = max_visible > TR_ROW_PATH_MAXN;
     hipLaunchKernelGGL(topk_rows_kernel, dim3(num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
-                       indices, (int)TR_ROW_PATH_MAXN);
-    if (max_visible <= TR_ROW_PATH_MAXN) return;
+                       indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr);
+    if (!has_long) return;
     const int CH = tw.chunks;
     const int min_n = TR_ROW_PATH_MAXN;
-    dim3 g2(CH, num_rows);
-    hipLaunchKernelGGL(topk_zero_kernel, dim3(num_rows), dim3(256), 0, stream, tw.hist, tw.rowst);
-    hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist, min_n);
-    hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.hist,
-                       tw.rowst, tw.chunkst, CH, tw.cand, min_n);
-    hipLaunchKernelGGL(topk_resolve_kernel, dim3(num_rows), dim3(RS_THREADS), 0, stream, vis, scores, ld, k,
-                       tw.rowst, tw.chunkst, CH, tw.cand, min_n);
+    // Few rows: one workgroup row per query row (short rows exit at once).
+    // Many rows: a list of the long ones and fixed grids that walk it.
+    const bool listed = num_rows > TK_LIST_GRID;
+    int32_t* lr = listed ? tw.longrows : nullptr;
+    const int G = listed ? TK_LIST_GRID : num_rows;
+    dim3 g2(CH, G);
+    if (listed)
+        hipLaunchKernelGGL(topk_prep_kernel, dim3(1), dim3(TP_THREADS), 0, stream, vis, num_rows, min_n, lr,
+                           tw.nlong);
+    hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, tw.rowst, tw.cand, lr,
+                       tw.nlong, num_rows, min_n);
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3(listed ? 256 : num_rows), dim3(RS_THREADS), 0, stream, vis,
+                       scores, ld, k, tw.rowst, tw.chunkst, CH, tw.cand, lr, tw.nlong, num_rows, min_n);
     hipLaunchKernelGGL(topk_write_kernel, g2, dim3(TK_THREADS), 0, stream, vis, scores, ld, k, tw.rowst,
-                       tw.chunkst, CH, indices, min_n);
+                       tw.chunkst, CH, indices, lr, tw.nlong, num_rows, min_n);
 }
 
 }  // namespace dsa

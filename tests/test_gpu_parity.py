@@ -261,6 +261,28 @@ def test_topk_bitexact_rows_beyond_one_workgroup(dsa, oracle_mod, kind):
         assert np.array_equal(got, ref), k
 
 
+def test_topk_bitexact_many_rows_few_long(dsa, oracle_mod):
+    """More than 64 rows, a few of them longer than 65,536 positions: the
+    long rows are listed on the device and walked by fixed grids (the short
+    ones stay with the one-workgroup-per-row kernel).  Long rows sit at the
+    start, middle and end of the batch, and include ties and all-equal rows."""
+    g = np.random.default_rng(77)
+    R = 150
+    lens = g.integers(1, 65537, size=R).astype(np.int32)
+    lens[:4] = [2048, 1, 2049, 65536]
+    long_at = [0, 5, 6, 71, 72, 100, 149]
+    lens[long_at] = [65537, 150000, 99999, 70000, 131072, 66000, 120001]
+    kinds = {5: "ties", 72: "zeros", 100: "coarse"}
+    n = int(lens.max())
+    s = wl.random_scores(31, R, n, kind="normal")
+    for r, kd in kinds.items():
+        s[r] = wl.random_scores(40 + r, 1, n, kind=kd)[0]
+    got = run_topk(dsa, lens, s, 2048)
+    ref = oracle_mod.topk(lens, s, 2048)
+    bad = [r for r in range(R) if not np.array_equal(got[r], ref[r])]
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("name, rows", [("c1", [0]), ("c4", [3, 9]), ("c2", [0, 2047, 2048, 2049, 5000, 8191])])
 def test_topk_bitexact_on_oracle_scores(dsa, oracle_mod, name, rows):
     w, x = inputs(name)
