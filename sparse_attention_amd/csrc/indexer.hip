@@ -196,7 +196,7 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
                 // Lane group g stores row 4 wave + g: 16 consecutive scores.
                 const float mine = xrow_reduce_scatter4(part);
                 const int pos = p0 + 16 * pg + j;
-                if (pos < nmine) scores[(int64_t)(r0 + 4 * wave + g) * ld + pos] = mine;
+                if (pos < nmine) __builtin_nontemporal_store(mine, &scores[(int64_t)(r0 + 4 * wave + g) * ld + pos]);
             }
             if (u + 1 < NU) {
 #pragma unroll
@@ -309,7 +309,9 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
         // consecutive scores per store.
         const float mine = xrow_reduce_scatter4(part);
         const int pos = p0 + 16 * g + j;
-        if (pos < n) srow[pos] = mine;
+        // Scores go out as non-temporal stores: they are read once, by the
+        // next kernel, and dirty lines left in L2 cost the kernel-end write-back.
+        if (pos < n) __builtin_nontemporal_store(mine, &srow[pos]);
         if constexpr (PAGED) {
 #pragma unroll
             for (int u = 0; u < IDX_GROUPS; u++) pbn[u] = pbnn[u];

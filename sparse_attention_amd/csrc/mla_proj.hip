@@ -137,7 +137,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
             const int rr = 8 * i + (lane >> 3), ch = lane & 7;  // row of the wave's 16, 16-byte chunk
             const int r = mt * PJ_TM + 16 * wave + rr;
             const u32x4 val = *reinterpret_cast<const u32x4*>(&ct[wave][rr][8 * ch]);
-            if (r < R) *reinterpret_cast<u32x4*>(qa + ((int64_t)r * 64 + h) * PJ_ROW + PJ_TN * nt + 8 * ch) = val;
+            // Non-temporal: the output is not re-read here, and dirty L2 lines
+            // cost the kernel-end write-back.
+            if (r < R)
+                __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(qa + ((int64_t)r * 64 + h) * PJ_ROW +
+                                                                          PJ_TN * nt + 8 * ch));
         }
         if (nt == 0) {
             // q_pe passes through: 64 rows x 8 chunks of 16 bytes.
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict
             if (r < R) {
                 float* orow = out + ((int64_t)r * 64 + h) * PJ_VDIM + PJ_TN * nt + j;
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) orow[16 * nb] = acc[nb][v];
+                for (int nb = 0; nb < 4; nb++) __builtin_nontemporal_store(acc[nb][v], &orow[16 * nb]);  // not re-read
             }
         }
     }

@@ -466,13 +466,16 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
             }
         }
         // Only this wave touches its region: LDS keeps its accesses in order.
+        // Non-temporal stores: the output (or the split partials, read once
+        // by the combine kernel) would otherwise be written back from L2 at
+        // the kernel's end.
         float* dst = nsplit == 1 ? out + (int64_t)r * 64 * 512 + c0
                                  : part_o + ((int64_t)r * nsplit + sp) * 64 * 512 + c0;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int h = 4 * i + (lane >> 4), c = 4 * (lane & 15);
             const floatx4 val = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
-            *reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c));
         }
     }
 }
@@ -520,7 +523,8 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     float4 res = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    *reinterpret_cast<float4*>(out + ((int64_t)r * 64 + h) * 512 + 4 * threadIdx.x) = res;
+    __builtin_nontemporal_store(floatx4{res.x, res.y, res.z, res.w},
+                                reinterpret_cast<floatx4*>(out + ((int64_t)r * 64 + h) * 512 + 4 * threadIdx.x));
     if (lse && threadIdx.x == 0) lse[(int64_t)r * 64 + h] = L > 0.f ? (M + log2f(L)) * LN2 : -INFINITY;
 }
 
