@@ -40,9 +40,13 @@ constexpr int PJ_ROPE = 64;    // qk_rope_head_dim
 constexpr int PJ_ROW = PJ_LAT + PJ_ROPE;
 constexpr int PJ_KVB = PJ_NOPE + PJ_VDIM;  // kv_b_proj rows per head
 constexpr int PJ_TM = 64;      // rows of R per tile
-constexpr int PJ_TN = 64;      // columns of N per workgroup
-constexpr int AB_PITCH = 160;  // bytes per staged W_UK row (64 bf16 + 32; spreads the 16 rows a read touches)
 constexpr int VU_PITCH = 1040; // bytes per staged W_UV row (512 bf16 + 16)
+// Columns of N per workgroup (TN, a template parameter): 64 for small R (the
+// weights are the traffic: more workgroups stream them); for the absorption at
+// large R 256 (each A row tile is re-read from L2 by every column tile of its
+// head, so fewer, wider column tiles cut that traffic: 8192 rows in 306
+// instead of ~395 us).
+constexpr int PJ_WIDE_ROWS = 512;  // R above this takes the wide absorption tiles
 
 __device__ __forceinline__ uint16_t to_bf16(float x)
 {
@@ -65,15 +69,19 @@ __device__ __forceinline__ ProjTile proj_tile()
     return ProjTile{b, p & 63, p >> 6};
 }
 
+template <int TN>
 __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __restrict__ qn,
                                                      const uint16_t* __restrict__ qp,
                                                      const uint16_t* __restrict__ kvb, uint16_t* __restrict__ qa)
 {
-    const ProjTile tile = proj_tile<PJ_LAT / PJ_TN>();
-    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_LAT / PJ_TN));
+    constexpr int ABP = 2 * TN + 32;  // bytes per staged W_UK row (TN bf16 + 32: spreads the rows a read touches)
+    constexpr int CPR = TN / 8;       // 16-byte chunks per staged row
+    constexpr int NB = TN / 16;       // 16-column blocks per wave
+    const ProjTile tile = proj_tile<PJ_LAT / TN>();
+    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_LAT / TN));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
-    __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_NOPE * AB_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t ct[4][16][PJ_TN + 8];  // output staging, per wave
+    __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_NOPE * ABP];
+    __shared__ __attribute__((aligned(16))) uint16_t ct[4][16][TN + 8];  // output staging, per wave
     constexpr int KS = PJ_NOPE / 32;  // k-steps
 
     // A operand of row tile mt: lane (j, g) holds q_nope[row][32 s + 8 g .. +8]
@@ -86,22 +94,23 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
     };
 
     // Every global load of the prologue goes out before the one barrier:
-    // W_UK,h[0:192][64 nt .. +64] (192 rows x 8 chunks of 16 bytes) and the
+    // W_UK,h[0:192][TN nt .. +TN] (192 rows x CPR chunks of 16 bytes) and the
     // first row tile's A operand.
-    const uint16_t* W = kvb + (int64_t)h * PJ_KVB * PJ_LAT + PJ_TN * nt;
-    u32x4 wreg[PJ_NOPE * 8 / 256];
+    const uint16_t* W = kvb + (int64_t)h * PJ_KVB * PJ_LAT + TN * nt;
+    constexpr int WPT = PJ_NOPE * CPR / 256;  // chunks per thread
+    u32x4 wreg[WPT];
 #pragma unroll
-    for (int i = 0; i < PJ_NOPE * 8 / 256; i++) {
+    for (int i = 0; i < WPT; i++) {
         const int c = threadIdx.x + 256 * i;
-        wreg[i] = load_u32x4(W + (int64_t)(c >> 3) * PJ_LAT + 8 * (c & 7));
+        wreg[i] = load_u32x4(W + (int64_t)(c / CPR) * PJ_LAT + 8 * (c % CPR));
     }
     const int mtiles = (R + PJ_TM - 1) / PJ_TM;
     bf16x8 a[KS];
     load_a(grp, a);
 #pragma unroll
-    for (int i = 0; i < PJ_NOPE * 8 / 256; i++) {
+    for (int i = 0; i < WPT; i++) {
         const int c = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(wt + (c >> 3) * AB_PITCH + 16 * (c & 7)) = wreg[i];
+        *reinterpret_cast<u32x4*>(wt + (c / CPR) * ABP + 16 * (c % CPR)) = wreg[i];
     }
     __syncthreads();
 
@@ -110,18 +119,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
         const bool more = mt + ngrp < mtiles;  // uniform
         bf16x8 an[KS];
         if (more) load_a(mt + ngrp, an);
-        floatx4 acc[4];
+        floatx4 acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; s++) {
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 // Lane (j, g): rows 32 s + 8 g + (j >> 2) (+4), columns
                 // 16 nb + 4 (j & 3) .. +3; it receives column 16 nb + j of
                 // rows 32 s + 8 g .. +7, the same K order as its A operand.
-                const uint8_t* lo = wt + (32 * s + 8 * g + (j >> 2)) * AB_PITCH + 2 * (16 * nb + 4 * (j & 3));
-                const bf16x8 b = lds_read_tr_pair((const uint16_t*)lo, (const uint16_t*)(lo + 4 * AB_PITCH));
+                const uint8_t* lo = wt + (32 * s + 8 * g + (j >> 2)) * ABP + 2 * (16 * nb + 4 * (j & 3));
+                const bf16x8 b = lds_read_tr_pair((const uint16_t*)lo, (const uint16_t*)(lo + 4 * ABP));
                 acc[nb] = mfma_16x16x32(a[s], b, acc[nb]);
             }
         }
@@ -131,17 +140,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
 #pragma unroll
         for (int v = 0; v < 4; v++)
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++) ct[wave][4 * g + v][16 * nb + j] = to_bf16(acc[nb][v]);
+            for (int nb = 0; nb < NB; nb++) ct[wave][4 * g + v][16 * nb + j] = to_bf16(acc[nb][v]);
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int rr = 8 * i + (lane >> 3), ch = lane & 7;  // row of the wave's 16, 16-byte chunk
+        for (int i = 0; i < 16 * CPR / 64; i++) {
+            const int q = 64 * i + lane, rr = q / CPR, ch = q % CPR;  // row of the wave's 16, 16-byte chunk
             const int r = mt * PJ_TM + 16 * wave + rr;
             const u32x4 val = *reinterpret_cast<const u32x4*>(&ct[wave][rr][8 * ch]);
             // Non-temporal: the output is not re-read here, and dirty L2 lines
             // cost the kernel-end write-back.
             if (r < R)
                 __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(qa + ((int64_t)r * 64 + h) * PJ_ROW +
-                                                                          PJ_TN * nt + 8 * ch));
+                                                                          TN * nt + 8 * ch));
         }
         if (nt == 0) {
             // q_pe passes through: 64 rows x 8 chunks of 16 bytes.
@@ -159,13 +168,15 @@ __global__ __launch_bounds__(256) void absorb_kernel(int R, const uint16_t* __re
     }
 }
 
+template <int TN>
 __global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict__ o,
                                                   const uint16_t* __restrict__ kvb, float* __restrict__ out)
 {
-    const ProjTile tile = proj_tile<PJ_VDIM / PJ_TN>();
-    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_VDIM / PJ_TN));
+    constexpr int NB = TN / 16;  // 16-column blocks per wave
+    const ProjTile tile = proj_tile<PJ_VDIM / TN>();
+    const int nt = tile.nt, h = tile.h, grp = tile.grp, ngrp = gridDim.x / (64 * (PJ_VDIM / TN));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
-    __shared__ __attribute__((aligned(16))) uint8_t wt[PJ_TN * VU_PITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t wt[TN * VU_PITCH];
     constexpr int KS = PJ_LAT / 32;  // k-steps
 
     // A operand of row tile mt, rounded to bf16 as it arrives: lane (j, g)
@@ -187,34 +198,38 @@ __global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict
         }
     };
 
-    // Prologue loads before the one barrier: W_UV,h rows 64 nt .. +64 (all
-    // 512 columns, 64 rows x 64 chunks of 16 bytes), then the first row tile.
-    const uint16_t* W = kvb + ((int64_t)h * PJ_KVB + PJ_NOPE + PJ_TN * nt) * PJ_LAT;
-    u32x4 wreg[PJ_TN * 64 / 256];
-#pragma unroll
-    for (int i = 0; i < PJ_TN * 64 / 256; i++) {
-        const int c = threadIdx.x + 256 * i;
-        wreg[i] = load_u32x4(W + (int64_t)(c >> 6) * PJ_LAT + 8 * (c & 63));
-    }
+    // Prologue: W_UV,h rows TN nt .. +TN (all 512 columns, 64 chunks of 16
+    // bytes per row) into LDS, 64 rows per pass so that at most 64 KB are
+    // held in registers, then the first row tile.
+    const uint16_t* W = kvb + ((int64_t)h * PJ_KVB + PJ_NOPE + TN * nt) * PJ_LAT;
     const int mtiles = (R + PJ_TM - 1) / PJ_TM;
     bf16x8 a[KS];
-    load_a(grp, a);
 #pragma unroll
-    for (int i = 0; i < PJ_TN * 64 / 256; i++) {
-        const int c = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(wt + (c >> 6) * VU_PITCH + 16 * (c & 63)) = wreg[i];
+    for (int half = 0; half < TN / 64; half++) {
+        u32x4 wreg[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int c = 4096 * half + threadIdx.x + 256 * i;
+            wreg[i] = load_u32x4(W + (int64_t)(c >> 6) * PJ_LAT + 8 * (c & 63));
+        }
+        if (half == TN / 64 - 1) load_a(grp, a);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int c = 4096 * half + threadIdx.x + 256 * i;
+            *reinterpret_cast<u32x4*>(wt + (c >> 6) * VU_PITCH + 16 * (c & 63)) = wreg[i];
+        }
     }
     __syncthreads();
 
     for (int mt = grp; mt < mtiles; mt += ngrp) {
         const bool more = mt + ngrp < mtiles;  // uniform
-        floatx4 acc[4];
+        floatx4 acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; nb++) acc[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; s++) {
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 // Lane (j, g): value dim 16 nb + j, latent columns 32 s + 8 g .. +7.
                 const bf16x8 b = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(wt + (16 * nb + j) * VU_PITCH + 2 * (32 * s + 8 * g)));
@@ -227,9 +242,9 @@ __global__ __launch_bounds__(256) void vup_kernel(int R, const float* __restrict
         for (int v = 0; v < 4; v++) {
             const int r = mt * PJ_TM + 16 * wave + 4 * g + v;
             if (r < R) {
-                float* orow = out + ((int64_t)r * 64 + h) * PJ_VDIM + PJ_TN * nt + j;
+                float* orow = out + ((int64_t)r * 64 + h) * PJ_VDIM + TN * nt + j;
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) __builtin_nontemporal_store(acc[nb][v], &orow[16 * nb]);  // not re-read
+                for (int nb = 0; nb < NB; nb++) __builtin_nontemporal_store(acc[nb][v], &orow[16 * nb]);  // not re-read
             }
         }
     }
@@ -250,16 +265,25 @@ int proj_row_groups(int32_t num_rows, int col_tiles)
 void launch_absorb_queries(int32_t num_rows, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* kvb,
                            uint16_t* q_abs, hipStream_t stream)
 {
-    const int ct = PJ_LAT / PJ_TN;
-    hipLaunchKernelGGL(absorb_kernel, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream, num_rows,
-                       q_nope, q_pe, kvb, q_abs);
+    if (num_rows > PJ_WIDE_ROWS) {
+        constexpr int ct = PJ_LAT / 256;
+        hipLaunchKernelGGL(absorb_kernel<256>, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream,
+                           num_rows, q_nope, q_pe, kvb, q_abs);
+    } else {
+        constexpr int ct = PJ_LAT / 64;
+        hipLaunchKernelGGL(absorb_kernel<64>, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream,
+                           num_rows, q_nope, q_pe, kvb, q_abs);
+    }
 }
 
 void launch_v_up_proj(int32_t num_rows, const float* o, const uint16_t* kvb, float* out, hipStream_t stream)
 {
-    const int ct = PJ_VDIM / PJ_TN;
-    hipLaunchKernelGGL(vup_kernel, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream, num_rows, o,
-                       kvb, out);
+    // 64-column tiles at every size: with 128 the fp32 A prefetch, its bf16
+    // operands and the accumulators exceed the register file (measured at
+    // 8192 rows: 1211 us with spills, against 530 us).
+    constexpr int ct = PJ_VDIM / 64;
+    hipLaunchKernelGGL(vup_kernel<64>, dim3(ct * 64 * proj_row_groups(num_rows, ct)), dim3(256), 0, stream,
+                       num_rows, o, kvb, out);
 }
 
 }  // namespace dsa

@@ -733,12 +733,13 @@ def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):
 U32 = 2.0 ** -24  # fp32 unit roundoff
 
 
-@pytest.mark.parametrize("R", [1, 5, 64, 130, 1024])
+@pytest.mark.parametrize("R", [1, 5, 64, 130, 1000, 1024])
 def test_absorb_queries_against_oracle(dsa, oracle_mod, R):
     """q_abs = [W_UK^T q_nope || q_pe]: the 512 absorbed columns within the
     error of fp32 accumulation over 192 products plus one bf16 rounding
     (at most 2^-8 |ref|: half an ulp of an 8-bit significand); the RoPE
-    part copied bit for bit.  R = 5, 130 leave ragged row tiles; R = 1024 makes
+    part copied bit for bit.  R = 5, 130 leave ragged row tiles; R = 1000 and
+    1024 take the 256-column tiles (1000 with a ragged last row tile) and make
     each workgroup walk several row tiles."""
     x = wl.projection_inputs(R, seed=5 + R)
     qa = torch.empty((R, 64, 576), dtype=torch.bfloat16, device=DEV)
