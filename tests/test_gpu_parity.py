@@ -650,6 +650,64 @@ def test_paged_calls_equal_packed_calls(dsa, oracle_mod, B):
     check_attention(out_b.cpu().numpy()[rs], lse_b.cpu().numpy()[rs], ref_out, ref_lse, f"paged B={B}")
 
 
+def test_cache_writer_fills_paged_pools_for_the_paged_step(dsa, oracle_mod):
+    """The next-row pieces together: dsa_cache_write scatters three sequences'
+    new tokens into block-scattered pools (slots = pool rows from the block
+    table), then dsa_decode_step_paged runs over those pools.  It must equal,
+    bit for bit, the packed step over packed caches written by the same
+    writer, and agree with the oracle on the depaged pools."""
+    B = 64
+    lens = np.array([3000, 2048, 777], np.int64)
+    S = len(lens)
+    seq_base = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    T = int(lens.sum())
+    c = wl.cache_write_inputs(T, seed=13, cache_rows=T)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int32)
+    c["positions"] = pos
+    nb = [(int(L) + B - 1) // B for L in lens]
+    nblk = sum(nb) + 5
+    perm = np.random.default_rng(3).permutation(nblk).astype(np.int32)
+    bt = np.zeros((S, max(nb)), np.int32)
+    o = 0
+    for i in range(S):
+        bt[i, :nb[i]] = perm[o:o + nb[i]]
+        o += nb[i]
+    seq_of_tok = np.repeat(np.arange(S), lens)
+    pool_rows = bt[seq_of_tok, pos // B].astype(np.int64) * B + pos % B
+    # packed caches and pools, both written by the cache writer
+    c["slots"] = np.arange(T, dtype=np.int64)
+    kc_packed, lc_packed = run_cache_write(dsa, c, 1e6)
+    c["slots"] = pool_rows
+    c["cache_rows"] = nblk * B
+    kpool, lpool = run_cache_write(dsa, c, 1e6)
+    # one decode row per sequence (sees the whole sequence)
+    q = wl.decode(S, 1, seed=21).generate(with_caches=False)
+    vis = lens.astype(np.int32)
+    R, k = S, 2048
+    x = dict(q_idx=q["q_idx"], w=q["w"], q_abs=q["q_abs"], visible_len=vis, row_cache_base=seq_base,
+             k_idx=kc_packed, kv_latent=lc_packed)
+    idx_a, out_a, lse_a = run_decode_step(dsa, x)
+    d = device_inputs(x)
+    prow = make_rows(dsa, vis, np.arange(S, dtype=np.int64))
+    paged = dsa.Paged(dev(bt), B)
+    ws = dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, int(vis.max()), k), DEV)
+    idx_b = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out_b = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+    dsa.dsa_decode_step_paged(prow, paged, d["q_idx"], d["w"], dev_bf16(kpool), wl.INDEX_SCALE, d["q_abs"],
+                              dev_bf16(lpool), wl.SOFTMAX_SCALE, k, idx_b, out_b, lse_b, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_a, idx_b.cpu().numpy())
+    assert np.array_equal(out_a.view(np.uint32), out_b.cpu().numpy().view(np.uint32))
+    assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
+    for i in range(S):
+        L = int(lens[i])
+        assert np.array_equal(oracle_mod.depage(lpool, bt[i], L, B), lc_packed[seq_base[i]:seq_base[i] + L])
+        assert np.array_equal(oracle_mod.depage(kpool, bt[i], L, B), kc_packed[seq_base[i]:seq_base[i] + L])
+    ref_out, ref_lse = oracle_mod.sparse_mla(seq_base, q["q_abs"], lc_packed, idx_a, wl.SOFTMAX_SCALE)
+    check_attention(out_b.cpu().numpy(), lse_b.cpu().numpy(), ref_out, ref_lse, "written paged pools")
+
+
 def test_paged_decode_step_full_size_equals_packed(dsa):
     """64 sequences x 32,768 positions in 64-row blocks scattered over the
     pool: the paged step gives bitwise the packed step's selection, output
