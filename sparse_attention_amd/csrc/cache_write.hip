@@ -225,6 +225,135 @@ __global__ __launch_bounds__(256) void cw_gemm_resident_kernel(int N, int mtiles
     cw_store(part, N, tl.mt, tl.ct, tl.s, wr, wc, j, g, acc);
 }
 
+// Large batches: 128 x 128 output tiles, four waves of 64 x 64 (4 x 4 MFMA
+// blocks each), no K split.  Each staged byte of A now feeds 128 columns and
+// each of B 128 tokens (a 64 x 64 tile re-reads both from L2 twice as
+// often), and a wave issues 8 LDS reads per 16 MFMAs instead of 8 per 8.
+// Loads run three stages ahead through a register ring (the loop is unrolled
+// by three so the ring slots are static and the compiler's wait counts exact),
+// then move to a double-buffered LDS stage.  Column tile 0 is wk, tiles 1..5
+// are kv_a rows 128 (t - 1) .. +127 (the last one half past row 575: those
+// rows are clamped on load and their columns never stored).
+constexpr int CB_T = 128;                      // tile rows and columns
+constexpr int CB_CT = (CW_COLS + CB_T - 1) / CB_T;  // 6 column tiles
+constexpr int CB_PITCH = CW_TK + 8;            // staged row, bf16 (144 bytes)
+constexpr int CB_MIN_TOKENS = 2048;            // batches from this size take this kernel
+
+struct CbLoader {
+    const uint16_t* xa[4];
+    const uint16_t* wb[4];
+    int so[4];
+    __device__ CbLoader(int N, int mt, int ct, const uint16_t* x, const uint16_t* wk, const uint16_t* kva)
+    {
+        const int tid = threadIdx.x, lr = tid >> 3, lk = (tid & 7) * 8;
+        const uint16_t* W = ct == 0 ? wk : kva + (size_t)(ct - 1) * CB_T * CW_HID;
+        const int wrows = ct == 0 ? CW_KEY : min(CB_T, CW_ROW - (ct - 1) * CB_T);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = lr + 32 * i;
+            xa[i] = x + (size_t)min(mt * CB_T + r, N - 1) * CW_HID + lk;  // ragged tail: clamp
+            wb[i] = W + (size_t)min(r, wrows - 1) * CW_HID + lk;
+            so[i] = r * CB_PITCH + lk;
+        }
+    }
+};
+
+__global__ __launch_bounds__(256, 2) void cw_gemm_big_kernel(int N, int mtiles, const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wk,
+                                                            const uint16_t* __restrict__ kva,
+                                                            float* __restrict__ part)
+{
+    // Workgroup -> (column tile, token tile): the 6 column tiles of a token
+    // tile are numbered 8 apart, so they share an XCD and its L2.
+    const int L = blockIdx.x, xc = L & 7, i8 = L >> 3;
+    const int ct = i8 % CB_CT, mt = (i8 / CB_CT) * 8 + xc;
+    if (mt >= mtiles) return;
+    const CbLoader ld(N, mt, ct, x, wk, kva);
+
+    __shared__ __attribute__((aligned(16))) uint16_t sa[2][CB_T * CB_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[2][CB_T * CB_PITCH];
+
+    u32x4 ra[3][4], rb[3][4];  // register ring: stage st lives in slot st % 3
+    auto issue = [&](u32x4 (&a)[4], u32x4 (&b)[4], int st) {
+        const int off = st * CW_TK;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            a[i] = load_u32x4(ld.xa[i] + off);
+            b[i] = load_u32x4(ld.wb[i] + off);
+        }
+    };
+    auto stage_to_lds = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            *reinterpret_cast<u32x4*>(&sa[buf][ld.so[i]]) = a[i];
+            *reinterpret_cast<u32x4*>(&sb[buf][ld.so[i]]) = b[i];
+        }
+    };
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64, j = lane & 15, g = lane >> 4;
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto mfma_stage = [&](int buf) {
+        const uint16_t* A = sa[buf];
+        const uint16_t* B = sb[buf];
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            const int ko = kk * 32 + g * 8;
+            bf16x8 av[4], bv[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                av[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + (wr + 16 * q + j) * CB_PITCH + ko));
+                bv[q] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(B + (wc + 16 * q + j) * CB_PITCH + ko));
+            }
+#pragma unroll
+            for (int a = 0; a < 4; a++)
+#pragma unroll
+                for (int b = 0; b < 4; b++) acc[a][b] = mfma_16x16x32(av[a], bv[b], acc[a][b]);
+        }
+    };
+
+    // Prologue: stages 0..2 requested, stage 0 staged.
+    issue(ra[0], rb[0], 0);
+    issue(ra[1], rb[1], 1);
+    issue(ra[2], rb[2], 2);
+    stage_to_lds(ra[0], rb[0], 0);
+    __syncthreads();
+    // Step st: request stage st + 3 into slot st % 3 (stage st is in LDS),
+    // multiply stage st, stage st + 1 into the other LDS buffer.
+    auto step = [&](int st, u32x4 (&a0)[4], u32x4 (&b0)[4], u32x4 (&a1)[4], u32x4 (&b1)[4]) {
+        if (st + 3 < CW_STAGES) issue(a0, b0, st + 3);
+        mfma_stage(st & 1);
+        if (st + 1 < CW_STAGES) stage_to_lds(a1, b1, (st + 1) & 1);
+        __syncthreads();
+    };
+    static_assert(CW_STAGES % 3 == 0, "the ring walks whole rounds");
+    for (int st = 0; st < CW_STAGES; st += 3) {
+        step(st, ra[0], rb[0], ra[1], rb[1]);
+        step(st + 1, ra[1], rb[1], ra[2], rb[2]);
+        step(st + 2, ra[2], rb[2], ra[0], rb[0]);
+    }
+
+    // D lane layout: element v of block (a, b) is D[4g + v][j].
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int row = mt * CB_T + wr + 16 * a + 4 * g + v;
+            if (row < N) {
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const int col = ct * CB_T + wc + 16 * b + j;
+                    if (col < CW_COLS) part[(size_t)row * CW_COLS + col] = acc[a][b][v];
+                }
+            }
+        }
+}
+
 // WPT waves per token (1, or 4 when K is split at least 4 ways).  Wave sub of
 // a token sums splits [sub * per, (sub + 1) * per) in split order with every
 // load issued first; with WPT = 4 the four partial sums meet in LDS and wave
@@ -377,6 +506,7 @@ int cw_row_tiles(int32_t n) { return (n + CW_TM - 1) / CW_TM; }
 // least 512 workgroups, each split at least 8 stages deep.
 int cache_write_splits(int32_t num_tokens)
 {
+    if (num_tokens >= CB_MIN_TOKENS) return 1;  // the 128 x 128 kernel
     const int mtiles = cw_row_tiles(num_tokens);
     if (mtiles <= 3) return CW_STAGES / CW_RES;
     static const int kDiv[] = {1, 2, 3, 4, 6, 8, 12};
@@ -399,7 +529,12 @@ void launch_cache_write(int32_t num_tokens, const uint16_t* hidden, const uint16
     const int mtiles = cw_row_tiles(num_tokens);
     const int pairs8 = (mtiles * S + 7) / 8 * 8;  // (token tile, split) pairs, padded to whole XCD rounds
     float* part = reinterpret_cast<float*>(ws);
-    if (S == CW_STAGES / CW_RES)
+    if (num_tokens >= CB_MIN_TOKENS) {
+        const int mt128 = (num_tokens + CB_T - 1) / CB_T;
+        const int rounds = (mt128 + 7) / 8;  // token tiles per XCD slot, padded to whole rounds
+        hipLaunchKernelGGL(cw_gemm_big_kernel, dim3(CB_CT * 8 * rounds), dim3(256), 0, stream, (int)num_tokens,
+                           mt128, hidden, wk, kv_a, part);
+    } else if (S == CW_STAGES / CW_RES)
         hipLaunchKernelGGL(cw_gemm_resident_kernel, dim3(CW_CT * pairs8), dim3(256), 0, stream, (int)num_tokens,
                            mtiles, hidden, wk, kv_a, part);
     else
