@@ -355,6 +355,7 @@ size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int
 {
     if (num_rows < 1 || max_visible < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
     size_t b = dsa::align_up((size_t)num_rows * scores_ld(max_visible) * 4, 256);
+    b += dsa::align_up(dsa::indexer_list_bytes(num_rows), 256);
     b += dsa::align_up(dsa_topk_workspace_size(num_rows, max_visible, k), 256);
     b += dsa::align_up(dsa_sparse_mla_workspace_size(num_rows, k), 256);
     return b;
@@ -398,13 +399,15 @@ dsa_status_t decode_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, cons
     char* p = (char*)ws;
     float* scores = (float*)p;
     p += dsa::align_up((size_t)R * ld * 4, 256);
+    void* lws = p;  // the indexer's row list (used when rows may share blocks)
+    p += dsa::align_up(dsa::indexer_list_bytes(R), 256);
     void* tws = p;
     p += dsa::align_up(dsa_topk_workspace_size(R, rows->max_visible, k), 256);
     void* aws = p;
 
     dsa::launch_indexer_scores(R, rows->max_visible, rows->visible_len, rows->row_cache_base, (const uint16_t*)q_idx,
                                w, (const uint16_t*)k_idx, index_scale, scores, ld,
-                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, pc, st);
+                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, pc, st, lws);
     DSA_TRY(after_launch(st, "decode_step/indexer"));
     dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, R, rows->max_visible);
     dsa::launch_topk(R, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);

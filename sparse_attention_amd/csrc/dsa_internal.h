@@ -24,7 +24,11 @@ int indexer_pick_chunk(int32_t num_rows, int32_t max_visible);
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis,
                            const int64_t* base, const uint16_t* q, const float* w,
                            const uint16_t* kc, float scale, float* scores, int64_t ld,
-                           bool distinct_sequences, const PagedCache& paged, hipStream_t stream);
+                           bool distinct_sequences, const PagedCache& paged, hipStream_t stream,
+                           void* list_ws = nullptr);
+// Workspace the row list of launch_indexer_scores needs (list_ws, 256-B aligned).
+size_t indexer_list_offset(int32_t num_rows);
+size_t indexer_list_bytes(int32_t num_rows);
 
 // ---- top-k ---------------------------------------------------------------
 constexpr int TK_CHUNK = 4096;     // scores one top-k workgroup owns

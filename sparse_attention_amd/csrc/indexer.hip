@@ -210,28 +210,23 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     }
 }
 
-// Grid: (waves_per_row / 4, rows).  The waves of one row sweep it together:
-// wave wr of the row scores 64-position blocks wr, wr + NW, wr + 2 NW, ...
-// (NW = waves per row), so the waves in flight read one compact, advancing
-// window of the key cache per row instead of thousands of scattered streams,
-// which keeps DRAM pages open.  Each wave loads each 16-position group of its
-// next block as soon as the same group of the current block has gone
-// through the matrix cores.
+// One wave's share of row r: 64-position blocks wr, wr + nw, wr + 2 nw, ...
+// (nw = waves per row; every wave works on its own, no workgroup barrier).
+// The waves of a row thus read one compact, advancing window of the key cache
+// instead of thousands of scattered streams, which keeps DRAM pages open.
+// Each wave loads each 16-position group of its next block as soon as the
+// same group of the current block has gone through the matrix cores.
 template <bool PAGED>
-__global__ __launch_bounds__(256) void indexer_rows_kernel(
-    const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
-    const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
-    int64_t ld, int num_rows, int skip_shared, PagedCache pm)
+__device__ __forceinline__ void indexer_row(int r, int wr, int nw, const int32_t* __restrict__ vis,
+                                            const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
+                                            const float* __restrict__ w, const uint16_t* __restrict__ kc,
+                                            float scale, float* __restrict__ scores, int64_t ld,
+                                            const PagedCache& pm)
 {
-    const int r = blockIdx.y;
     const int n = vis[r];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int nw = gridDim.x * IDX_WAVES;
-    if (skip_shared && block_is_shared(base, num_rows, r / IDX_TILE_ROWS)) return;  // the tile kernel owns it
-    const int wr = blockIdx.x * IDX_WAVES + wave;
     if (wr * IDX_BLOCK >= n) return;
 
     // A operands: Q[r][16 hb + j][32 s + 8 g .. +8] for head blocks hb = 0, 1.
@@ -319,6 +314,72 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     }
 }
 
+// Grid: (workgroups per row, rows): grid row y scores row y.  With rowlist
+// set, grid row y walks list entries y, y + gridDim.y, ... instead (the rows
+// no shared block owns; see indexer_list_kernel).
+template <bool PAGED>
+__global__ __launch_bounds__(256) void indexer_rows_kernel(
+    const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
+    const float* __restrict__ w, const uint16_t* __restrict__ kc, float scale, float* __restrict__ scores,
+    int64_t ld, int num_rows, int skip_shared, PagedCache pm, const int32_t* __restrict__ rowlist,
+    const uint32_t* __restrict__ nlist)
+{
+    const int wr = blockIdx.x * IDX_WAVES + (threadIdx.x >> 6);
+    const int nw = gridDim.x * IDX_WAVES;
+    if (!rowlist) {
+        const int r = blockIdx.y;
+        if (skip_shared && block_is_shared(base, num_rows, r / IDX_TILE_ROWS)) return;  // the tile kernel owns it
+        indexer_row<PAGED>(r, wr, nw, vis, base, q, w, kc, scale, scores, ld, pm);
+        return;
+    }
+    const uint32_t cnt = *nlist;
+    for (uint32_t li = blockIdx.y; li < cnt; li += gridDim.y)
+        indexer_row<PAGED>(rowlist[li], wr, nw, vis, base, q, w, kc, scale, scores, ld, pm);
+}
+
+// One workgroup: lists, in row order, the rows that no shared 32-row block
+// owns (the rows the row kernel scores), so that a batch mixing a long
+// prefill chunk with decode rows can give those rows many workgroups each
+// instead of the one per row a grid over all rows affords.
+constexpr int IL_THREADS = 1024;
+constexpr int IL_GRID = 64;  // grid rows of the row kernel in list mode
+__global__ __launch_bounds__(IL_THREADS) void indexer_list_kernel(const int64_t* __restrict__ base, int num_rows,
+                                                                  int32_t* __restrict__ rowlist,
+                                                                  uint32_t* __restrict__ nlist)
+{
+    __shared__ uint32_t sh[IL_THREADS / 64];
+    const int nb = (num_rows + IDX_TILE_ROWS - 1) / IDX_TILE_ROWS;
+    const int per = (nb + IL_THREADS - 1) / IL_THREADS;
+    const int b0 = threadIdx.x * per, b1 = min(nb, b0 + per);
+    auto listed = [&](int b) {  // rows of block b the row kernel owns
+        const int r0 = b * IDX_TILE_ROWS;
+        const int rn = min(IDX_TILE_ROWS, num_rows - r0);
+        if (rn < IDX_TILE_ROWS) return rn;  // a partial block is never shared
+        const int64_t b_0 = base[r0];
+        for (int i = 1; i < IDX_TILE_ROWS; i++)
+            if (base[r0 + i] != b_0) return IDX_TILE_ROWS;
+        return 0;
+    };
+    uint32_t cnt = 0;
+    for (int b = b0; b < b1; b++) cnt += (uint32_t)listed(b);
+    // Exclusive scan of the per-thread counts.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+    for (int i = 0; i < IL_THREADS / 64; i++) {
+        before += i < wave ? sh[i] : 0u;
+        total += sh[i];
+    }
+    uint32_t slot = before + incl - cnt;
+    for (int b = b0; b < b1; b++) {
+        const int nr = listed(b);
+        for (int i = 0; i < nr; i++) rowlist[slot++] = b * IDX_TILE_ROWS + i;
+    }
+    if (threadIdx.x == 0) *nlist = total;
+}
+
 }  // namespace
 
 int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
@@ -337,7 +398,8 @@ int indexer_pick_chunk(int32_t num_rows, int32_t max_visible)
 
 void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t* vis, const int64_t* base,
                            const uint16_t* q, const float* w, const uint16_t* kc, float scale, float* scores,
-                           int64_t ld, bool distinct_sequences, const PagedCache& paged, hipStream_t stream)
+                           int64_t ld, bool distinct_sequences, const PagedCache& paged, hipStream_t stream,
+                           void* list_ws)
 {
     const bool pg = paged.block_table != nullptr;
     const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
@@ -356,13 +418,28 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
             hipLaunchKernelGGL(indexer_tile_kernel<false>, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
                                scale, scores, ld, num_rows, paged);
     }
+    int32_t* rowlist = nullptr;
+    uint32_t* nlist = nullptr;
     dim3 grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
+    if (nblk > 0 && list_ws) {
+        // Rows that may share blocks: list the others and give each of them
+        // the workgroups of a batch of at most IL_GRID rows.
+        rowlist = reinterpret_cast<int32_t*>(list_ws);
+        nlist = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(list_ws) + indexer_list_offset(num_rows));
+        hipLaunchKernelGGL(indexer_list_kernel, dim3(1), dim3(IL_THREADS), 0, stream, base, (int)num_rows, rowlist,
+                           nlist);
+        const int G = num_rows < IL_GRID ? num_rows : IL_GRID;
+        grid = dim3(indexer_pick_chunk(G, max_visible), G);
+    }
     if (pg)
         hipLaunchKernelGGL(indexer_rows_kernel<true>, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores,
-                           ld, num_rows, nblk > 0 ? 1 : 0, paged);
+                           ld, num_rows, nblk > 0 ? 1 : 0, paged, rowlist, nlist);
     else
         hipLaunchKernelGGL(indexer_rows_kernel<false>, grid, dim3(256), 0, stream, vis, base, q, w, kc, scale, scores,
-                           ld, num_rows, nblk > 0 ? 1 : 0, paged);
+                           ld, num_rows, nblk > 0 ? 1 : 0, paged, rowlist, nlist);
 }
+
+size_t indexer_list_offset(int32_t num_rows) { return align_up((size_t)num_rows * 4, 256); }
+size_t indexer_list_bytes(int32_t num_rows) { return indexer_list_offset(num_rows) + 256; }
 
 }  // namespace dsa

@@ -439,6 +439,39 @@ def test_decode_step_attention_matches_standalone_call(dsa, R):
         assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref_lse.view(np.uint32)), rep
 
 
+def test_decode_step_rows_beside_shared_blocks(dsa, oracle_mod):
+    """A batch mixing a prefill chunk (two full 32-row blocks on one sequence,
+    which the shared-block kernel scores) with decode rows of very different
+    lengths: the decode step lists the other rows on the device and gives
+    each many workgroups.  Its selection and output must equal, bit for bit,
+    the separate calls (whose indexer scores every row directly), and the
+    long rows must agree with the oracle."""
+    T0 = 5000
+    chunk_vis = np.arange(T0 - 63, T0 + 1)
+    dec = [70000, 12000, 100, 3000, 2049, 1]
+    vis = np.concatenate([chunk_vis, dec]).astype(np.int32)
+    seq_len = np.array([T0] + dec, np.int64)
+    seq_base = np.concatenate([[0], np.cumsum(seq_len)[:-1]]).astype(np.int64)
+    base = np.concatenate([np.zeros(64), seq_base[1:]]).astype(np.int64)
+    w = wl.Workload(name="mixdec", seed=23, visible_len=vis, row_cache_base=base, seq_len=seq_len,
+                    seq_base=seq_base, row_seq=np.zeros(len(vis), np.int64))
+    x = w.generate()
+    d = device_inputs(x)
+    idx_a, out_a, lse_a = run_decode_step(dsa, x, d=d)
+    scores = run_indexer(dsa, x, d=d)
+    idx_b = run_topk(dsa, vis, scores, 2048)
+    out_b, lse_b = run_attn(dsa, x, idx_b, 2048, d=d)
+    assert np.array_equal(idx_a, idx_b)
+    assert np.array_equal(out_a.view(np.uint32), out_b.view(np.uint32))
+    assert np.array_equal(lse_a.view(np.uint32), lse_b.view(np.uint32))
+    rows = [0, 63, 64, 65, 67]
+    y = sub(x, rows)
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(y["visible_len"], y["row_cache_base"], y["q_idx"], y["w"],
+                                                   y["k_idx"], y["q_abs"], y["kv_latent"], 2048, 1.0,
+                                                   wl.SOFTMAX_SCALE)
+    assert recall_check(idx_a[rows], idx_ref, s64, y["visible_len"]) >= 0.999
+
+
 def test_decode_step_deterministic(dsa):
     w, x = inputs("c3")
     d = device_inputs(x)
