@@ -28,6 +28,21 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+// Grids with one row of workgroups per item (a query row, a block of rows):
+// items past what grid y takes spill into z, so that y stays within its
+// launch limit and each dimension within 2^32 work-items at any item count.
+// Dispatch order is unchanged: x fastest, then the items in order.
+constexpr unsigned GRID_Y_MAX = 65535;
+
+inline dim3 item_grid(unsigned x, int64_t items)
+{
+    const unsigned y = items < (int64_t)GRID_Y_MAX ? (unsigned)items : GRID_Y_MAX;
+    return dim3(x, y, (unsigned)((items + y - 1) / y));
+}
+
+// This workgroup's item; the last z slice may run past the item count.
+__device__ __forceinline__ int grid_item() { return (int)(blockIdx.z * gridDim.y + blockIdx.y); }
+
 __device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

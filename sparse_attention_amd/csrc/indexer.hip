@@ -73,7 +73,9 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     // Last blocks first: in a causal prefill chunk they see the most
     // positions, so starting them early shortens the tail (measured on an
     // 8,192-position prefill: 267 vs 336 us).
-    const int blk = gridDim.y - 1 - blockIdx.y;
+    const int nblk = num_rows / IDX_TILE_ROWS;
+    if (grid_item() >= nblk) return;
+    const int blk = nblk - 1 - grid_item();
     if (!block_is_shared(base, num_rows, blk)) return;
     const int r0 = blk * IDX_TILE_ROWS;
     const int lane = threadIdx.x & 63;
@@ -314,9 +316,9 @@ __device__ __forceinline__ void indexer_row(int r, int wr, int nw, const int32_t
     }
 }
 
-// Grid: (workgroups per row, rows): grid row y scores row y.  With rowlist
-// set, grid row y walks list entries y, y + gridDim.y, ... instead (the rows
-// no shared block owns; see indexer_list_kernel).
+// Grid: (workgroups per row, rows as items): item r scores row r.  With
+// rowlist set, grid row y walks list entries y, y + gridDim.y, ... instead
+// (the rows no shared block owns; see indexer_list_kernel).
 template <bool PAGED>
 __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int32_t* __restrict__ vis, const int64_t* __restrict__ base, const uint16_t* __restrict__ q,
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(256) void indexer_rows_kernel(
     const int wr = blockIdx.x * IDX_WAVES + (threadIdx.x >> 6);
     const int nw = gridDim.x * IDX_WAVES;
     if (!rowlist) {
-        const int r = blockIdx.y;
+        const int r = grid_item();
+        if (r >= num_rows) return;
         if (skip_shared && block_is_shared(base, num_rows, r / IDX_TILE_ROWS)) return;  // the tile kernel owns it
         indexer_row<PAGED>(r, wr, nw, vis, base, q, w, kc, scale, scores, ld, pm);
         return;
@@ -412,15 +415,15 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
         if (cx > tiles) cx = tiles;
         if (cx < 1) cx = 1;
         if (pg)
-            hipLaunchKernelGGL(indexer_tile_kernel<true>, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
+            hipLaunchKernelGGL(indexer_tile_kernel<true>, item_grid(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
                                scale, scores, ld, num_rows, paged);
         else
-            hipLaunchKernelGGL(indexer_tile_kernel<false>, dim3(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
+            hipLaunchKernelGGL(indexer_tile_kernel<false>, item_grid(cx, nblk), dim3(512), 0, stream, vis, base, q, w, kc,
                                scale, scores, ld, num_rows, paged);
     }
     int32_t* rowlist = nullptr;
     uint32_t* nlist = nullptr;
-    dim3 grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
+    dim3 grid = item_grid(indexer_pick_chunk(num_rows, max_visible), num_rows);
     if (nblk > 0 && list_ws) {
         // Rows that may share blocks: list the others and give each of them
         // the workgroups of a batch of at most IL_GRID rows.

@@ -14,22 +14,25 @@ namespace dsa {
 
 namespace {
 
-// One thread per (row, selected slot); the row's block-table row is read
-// through the cache (a 2048-entry selection touches at most 2048 entries).
+// One thread per (row, selected slot), grid-strided past PI_MAX_GRID
+// workgroups; the row's block-table row is read through the cache (a
+// 2048-entry selection touches at most 2048 entries).
+constexpr int64_t PI_MAX_GRID = 1 << 16;
+
 __global__ __launch_bounds__(256) void page_indices_kernel(int64_t total, int k, const int64_t* __restrict__ seq,
                                                            const int32_t* __restrict__ idx, PagedCache pm,
                                                            int32_t* __restrict__ phys, int64_t* __restrict__ zero_base)
 {
-    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (o >= total) return;
-    const int64_t r = o / k;
-    if (o - r * k == 0) zero_base[r] = 0;
-    const int32_t p = idx[o];
-    const int32_t* btr = pm.block_table + seq[r] * pm.max_blocks;
-    // Padding: -1 - (row of position 0), a row every sequence has, for the
-    // attention's masked gathers to read.
-    phys[o] = p >= 0 ? (btr[p >> pm.log2_block] << pm.log2_block) | (p & ((1 << pm.log2_block) - 1))
-                     : -1 - (btr[0] << pm.log2_block);
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+        const int64_t r = o / k;
+        if (o - r * k == 0) zero_base[r] = 0;
+        const int32_t p = idx[o];
+        const int32_t* btr = pm.block_table + seq[r] * pm.max_blocks;
+        // Padding: -1 - (row of position 0), a row every sequence has, for
+        // the attention's masked gathers to read.
+        phys[o] = p >= 0 ? (btr[p >> pm.log2_block] << pm.log2_block) | (p & ((1 << pm.log2_block) - 1))
+                         : -1 - (btr[0] << pm.log2_block);
+    }
 }
 
 }  // namespace
@@ -38,8 +41,9 @@ void launch_page_indices(int32_t num_rows, int32_t k, const int64_t* seq, const 
                          const PagedCache& paged, int32_t* phys, int64_t* zero_base, hipStream_t stream)
 {
     const int64_t total = (int64_t)num_rows * k;
-    hipLaunchKernelGGL(page_indices_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, (int)k,
-                       seq, idx, paged, phys, zero_base);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(page_indices_kernel, dim3((unsigned)(blocks < PI_MAX_GRID ? blocks : PI_MAX_GRID)), dim3(256),
+                       0, stream, total, (int)k, seq, idx, paged, phys, zero_base);
 }
 
 }  // namespace dsa

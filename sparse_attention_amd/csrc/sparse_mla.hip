@@ -113,7 +113,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
                                                            const int32_t* __restrict__ idx, int k,
-                                                           float scale_log2, int split_len, int pad_rows,
+                                                           int num_rows, float scale_log2, int split_len,
+                                                           int pad_rows,
                                                            float* __restrict__ out, float* __restrict__ lse,
                                                            float* __restrict__ part_o,
                                                            float2* __restrict__ part_ml)
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
     // Rows in reverse: in a causal prefill chunk the last rows select the
     // most positions, and starting them first shortens the tail (the results
     // do not depend on the order).
-    const int r = gridDim.y - 1 - blockIdx.y;
+    if (grid_item() >= num_rows) return;
+    const int r = num_rows - 1 - grid_item();
     const int sp = blockIdx.x;
     const int nsplit = gridDim.x;
     const int lane = threadIdx.x & 63;
@@ -486,11 +488,13 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
 // split order, so results do not depend on scheduling.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __restrict__ part_o,
                                                                 const float2* __restrict__ part_ml, int nsplit,
-                                                                float* __restrict__ out, float* __restrict__ lse)
+                                                                int num_rows, float* __restrict__ out,
+                                                                float* __restrict__ lse)
 {
     constexpr int MAXS = 16;  // attn_pick_splits never returns more
     const int h = blockIdx.x;
-    const int r = blockIdx.y;
+    const int r = grid_item();
+    if (r >= num_rows) return;
     const float2* ml = part_ml + (int64_t)r * nsplit * 64 + h;
     const float* po = part_o + ((int64_t)r * nsplit * 64 + h) * 512 + 4 * threadIdx.x;
     float2 e[MAXS];
@@ -565,11 +569,11 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
         part_o = (float*)ws;
         part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
     }
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, num_rows), dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k,
-                       softmax_scale * LOG2E, split_len, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
+    hipLaunchKernelGGL(sparse_mla_kernel, item_grid(s, num_rows), dim3(AT_THREADS), 0, stream, base, qa, kv, idx,
+                       k, (int)num_rows, softmax_scale * LOG2E, split_len, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
     if (s > 1)
-        hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3(64, num_rows), dim3(128), 0, stream, part_o, part_ml, s,
-                           out, lse);
+        hipLaunchKernelGGL(sparse_mla_combine_kernel, item_grid(64, num_rows), dim3(128), 0, stream, part_o, part_ml,
+                           s, (int)num_rows, out, lse);
 }
 
 }  // namespace dsa

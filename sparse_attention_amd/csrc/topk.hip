@@ -605,10 +605,11 @@ __device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0
 __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __restrict__ vis,
                                                                const float* __restrict__ scores, int64_t ld,
                                                                int k, int32_t* __restrict__ indices, int max_n,
-                                                               uint32_t* __restrict__ long_rowst)
+                                                               uint32_t* __restrict__ long_rowst, int num_rows)
 {
     static_assert(TR_THREADS == TP_THREADS, "the sampling step runs on this workgroup");
-    const int r = blockIdx.x;
+    const int r = grid_item();
+    if (r >= num_rows) return;
     const int n = vis[r];
     int32_t* out = indices + (int64_t)r * k;
     const int tid = threadIdx.x;
@@ -967,8 +968,8 @@ void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, cons
     // The row kernel also samples the long rows (the first step of their
     // path), so it goes first.
     const bool has_long = max_visible > TR_ROW_PATH_MAXN;
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
-                       indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr);
+    hipLaunchKernelGGL(topk_rows_kernel, item_grid(1, num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
+                       indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr, (int)num_rows);
     if (!has_long) return;
     const int CH = tw.chunks;
     const int min_n = TR_ROW_PATH_MAXN;

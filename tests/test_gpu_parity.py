@@ -472,6 +472,52 @@ def test_decode_step_rows_beside_shared_blocks(dsa, oracle_mod):
     assert recall_check(idx_a[rows], idx_ref, s64, y["visible_len"]) >= 0.999
 
 
+def test_decode_step_rows_past_grid_y_limit(dsa, oracle_mod):
+    """70,000 decode rows, more than a launch grid's y dimension holds: every
+    per-row kernel spills its rows into z.  Each row's per-row inputs are one
+    of 509 drawn templates (row r uses r % 509), with its own length and cache
+    base, so a row computed as another or not at all shows.  Every row is
+    checked for whole selection counts and finite outputs; rows on both
+    sides of the y limit are checked against the oracle."""
+    R, NT, CACHE = 70000, 509, 6144
+    r = np.arange(R, dtype=np.int64)
+    vis = (1 + (r * 7919) % 4096).astype(np.int32)
+    base = ((r * 97) % 2048).astype(np.int64)
+    w = wl.Workload(name="manyrows", seed=31, visible_len=vis[:NT], row_cache_base=base[:NT],
+                    seq_len=np.array([CACHE], np.int64), seq_base=np.zeros(1, np.int64), row_seq=np.zeros(NT, np.int64))
+    x = w.generate()
+    tmpl = torch.from_numpy(r % NT).to(DEV)
+    q_idx = dev_bf16(x["q_idx"]).index_select(0, tmpl)
+    wts = dev(x["w"]).index_select(0, tmpl)
+    q_abs = dev_bf16(x["q_abs"]).index_select(0, tmpl)
+    k = 2048
+    rows = make_rows(dsa, vis, base)
+    idx = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((R, 64, 512), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((R, 64), float("nan"), dtype=torch.float32, device=DEV)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, int(vis.max()), k), DEV)
+    dsa.dsa_decode_step(rows, q_idx, wts, dev_bf16(x["k_idx"]), wl.INDEX_SCALE, q_abs, dev_bf16(x["kv_latent"]),
+                        wl.SOFTMAX_SCALE, k, idx, out, lse, ws)
+    torch.cuda.synchronize()
+    vis_d = dev(vis).to(torch.int64)
+    assert torch.equal((idx >= 0).sum(1), torch.clamp(vis_d, max=k))
+    assert bool((idx < vis_d[:, None]).all()) and bool((idx >= -1).all())
+    assert bool(torch.isfinite(lse).all()) and bool(torch.isfinite(out).all())
+    pick = [0, 1, 2, 65534, 65535, 65536, 65537, 69998, 69999]
+    pick += [int(v) for v in np.random.default_rng(31).integers(0, R, 4)]
+    pick += [int(np.flatnonzero(vis[65535:] > k)[0]) + 65535, int(np.flatnonzero(vis[65535:] <= k)[0]) + 65535]
+    sel = torch.tensor(pick, device=DEV)
+    g_idx = idx.index_select(0, sel).cpu().numpy()
+    g_out = out.index_select(0, sel).cpu().numpy()
+    g_lse = lse.index_select(0, sel).cpu().numpy()
+    t = np.asarray(pick) % NT
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(vis[pick], base[pick], x["q_idx"][t], x["w"][t], x["k_idx"],
+                                                   x["q_abs"][t], x["kv_latent"], k, 1.0, wl.SOFTMAX_SCALE)
+    assert recall_check(g_idx, idx_ref, s64, vis[pick]) >= 0.999
+    ref_out, ref_lse = oracle_mod.sparse_mla(base[pick], x["q_abs"][t], x["kv_latent"], g_idx, wl.SOFTMAX_SCALE)
+    check_attention(g_out, g_lse, ref_out, ref_lse, "rows past the y limit")
+
+
 def test_decode_step_deterministic(dsa):
     w, x = inputs("c3")
     d = device_inputs(x)
