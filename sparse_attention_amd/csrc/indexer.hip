@@ -358,13 +358,22 @@ __global__ __launch_bounds__(IL_THREADS) void indexer_list_kernel(const int64_t*
         const int r0 = b * IDX_TILE_ROWS;
         const int rn = min(IDX_TILE_ROWS, num_rows - r0);
         if (rn < IDX_TILE_ROWS) return rn;  // a partial block is never shared
-        const int64_t b_0 = base[r0];
-        for (int i = 1; i < IDX_TILE_ROWS; i++)
-            if (base[r0 + i] != b_0) return IDX_TILE_ROWS;
-        return 0;
+        // Every load issued before any compare: one memory round trip.
+        int64_t v[IDX_TILE_ROWS];
+#pragma unroll
+        for (int i = 0; i < IDX_TILE_ROWS; i++) v[i] = base[r0 + i];
+        bool same = true;
+#pragma unroll
+        for (int i = 1; i < IDX_TILE_ROWS; i++) same &= v[i] == v[0];
+        return same ? 0 : IDX_TILE_ROWS;
     };
-    uint32_t cnt = 0;
-    for (int b = b0; b < b1; b++) cnt += (uint32_t)listed(b);
+    // The first 32 blocks' verdicts are kept for the second pass.
+    uint32_t cnt = 0, owned = 0;
+    for (int b = b0; b < b1; b++) {
+        const int nr = listed(b);
+        if (b - b0 < 32 && nr > 0) owned |= 1u << (b - b0);
+        cnt += (uint32_t)nr;
+    }
     // Exclusive scan of the per-thread counts.
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_inclusive_scan(cnt);
@@ -377,7 +386,8 @@ __global__ __launch_bounds__(IL_THREADS) void indexer_list_kernel(const int64_t*
     }
     uint32_t slot = before + incl - cnt;
     for (int b = b0; b < b1; b++) {
-        const int nr = listed(b);
+        const int nr = b - b0 < 32 ? ((owned >> (b - b0)) & 1u ? min(IDX_TILE_ROWS, num_rows - b * IDX_TILE_ROWS) : 0)
+                                   : listed(b);
         for (int i = 0; i < nr; i++) rowlist[slot++] = b * IDX_TILE_ROWS + i;
     }
     if (threadIdx.x == 0) *nlist = total;

@@ -8,7 +8,9 @@
 // -0.0 == +0.0, equal scores go to the lower position, NaN lowest.
 //
 // Design: a radix select on the order-preserving 32-bit key of each score.
-// Rows of at most 65,536 positions take one 1024-thread workgroup each (one
+// Calls whose rows all have at most 8,192 positions take one 256-thread
+// workgroup per row, several rows to a CU (topk_short_kernel).  Otherwise
+// rows of at most 65,536 positions take one 1024-thread workgroup each (one
 // streaming pass over the row, the rest in LDS; see topk_rows_kernel).
 // Longer rows are split over workgroups, because a single CU streams too
 // slowly for them; only integer counts are combined across workgroups, so the
@@ -924,6 +926,165 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
     }
 }
 
+// Calls whose rows all have at most TS_MAXN positions (a prefill chunk of up
+// to 8,192 tokens, short decode rows): 256 threads per row and the row's keys
+// held in registers, 32 per thread.  The radix rounds histogram those
+// registers directly (11-bit digits relative to the row's key range, so at
+// most three rounds), without a candidate list, so a workgroup needs ~19 KB
+// of LDS and several rows share a CU, where the 1024-thread kernel holds a CU
+// for each row in turn.  Same order and output as topk_rows_kernel: theta is
+// the k-th largest key, every larger key is kept, and of the theta-valued
+// elements the first need_eq in position order.
+constexpr int TS_THREADS = 256;
+constexpr int TS_GROUPS = 8;                         // float4 groups per thread
+constexpr int TS_MAXN = 4 * TS_THREADS * TS_GROUPS;  // 8,192
+constexpr int TS_BINS = 2048;                        // 11-bit digit
+constexpr int TS_WORDS = TS_MAXN / 32;               // bitmap words: one per thread
+static_assert(TS_WORDS == TS_THREADS, "thread t owns bitmap word t");
+
+__global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* __restrict__ vis,
+                                                                const float* __restrict__ scores, int64_t ld,
+                                                                int k, int32_t* __restrict__ indices, int num_rows)
+{
+    const int r = grid_item();
+    if (r >= num_rows) return;
+    const int n = vis[r];
+    int32_t* out = indices + (int64_t)r * k;
+    const int tid = threadIdx.x;
+    if (n <= k) {
+        for (int t = tid; t < k; t += TS_THREADS) out[t] = t < n ? t : -1;
+        return;
+    }
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2][TS_BINS];  // radix rounds, alternating
+    __shared__ uint32_t gtbits[TS_WORDS];
+    __shared__ uint32_t eqbits[TS_WORDS];
+    __shared__ uint32_t sh[TS_THREADS / 64];
+    __shared__ uint32_t wlo[TS_THREADS / 64], whi[TS_THREADS / 64];
+    __shared__ uint32_t s_bin, s_above, s_cnt;
+
+    // ---- the row's keys, into registers ------------------------------------
+    // Element (u, q) of thread t is position 4 (t + TS_THREADS u) + q.  A
+    // 4-aligned group starting below n lies inside the row allocation (ld is
+    // a multiple of 4 and n <= ld); lanes past the row re-read its last group
+    // and are masked out by the position test.
+    const float* row = scores + (int64_t)r * ld;
+    const int nu = (n + 4 * TS_THREADS - 1) / (4 * TS_THREADS);
+    const int lim = n - 4 * tid;  // element (u, q) is in the row iff 4 TS_THREADS u + q < lim
+    uint32_t key[TS_GROUPS][4];
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int u = 0; u < TS_GROUPS; u++) {
+        if (u < nu) {
+            const int p = min(4 * (tid + TS_THREADS * u), (n - 1) & ~3);
+            const float4 v = *reinterpret_cast<const float4*>(row + p);
+            key[u][0] = key_of(v.x);
+            key[u][1] = key_of(v.y);
+            key[u][2] = key_of(v.z);
+            key[u][3] = key_of(v.w);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if (4 * TS_THREADS * u + q < lim) {
+                    kmin = min(kmin, key[u][q]);
+                    kmax = max(kmax, key[u][q]);
+                }
+            }
+        }
+    }
+    for (int i = tid; i < 2 * TS_BINS / 4; i += TS_THREADS)
+        reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    gtbits[tid] = 0u;
+    eqbits[tid] = 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane == 0) {
+        wlo[wave] = kmin;
+        whi[wave] = kmax;
+    }
+    __syncthreads();  // histograms and bitmaps cleared, range published
+    uint32_t lo = wlo[0], hi = whi[0];
+#pragma unroll
+    for (int w = 1; w < TS_THREADS / 64; w++) {
+        lo = min(lo, wlo[w]);
+        hi = max(hi, whi[w]);
+    }
+
+    // ---- radix rounds on [lo, hi] ----------------------------------------
+    // Each round histograms (key - lo) >> shift over the keys in [lo, hi]
+    // and narrows [lo, hi] to the bin holding the need-th largest (k < n, so
+    // it exists).  A histogram is cleared for the round after next.
+    uint32_t need = (uint32_t)k;
+    uint32_t eq_total = 0;
+    for (int round = 0;; round++) {
+        uint32_t* h = hist[round & 1];
+        const int shift = max(0, bitlen(hi - lo) - 11);
+#pragma unroll
+        for (int u = 0; u < TS_GROUPS; u++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t kk = key[u][q];
+                if (u < nu && 4 * TS_THREADS * u + q < lim && kk >= lo && kk <= hi)
+                    atomicAdd(&h[(kk - lo) >> shift], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold_bin<TS_THREADS, TS_BINS>(h, need, &s_bin, &s_above, sh, &s_cnt);
+        const uint32_t bin = s_bin;
+        need -= s_above;
+        const uint32_t cnt = s_cnt;
+        for (int i = tid; i < TS_BINS / 4; i += TS_THREADS)
+            reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t nlo = lo + (bin << shift);
+        hi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
+        lo = nlo;
+        if (shift == 0) {
+            eq_total = cnt;
+            break;
+        }
+    }
+    const uint32_t theta = lo, need_eq = need;
+    (void)eq_total;
+
+    // ---- bitmaps, then the ordered output (thread t owns word t) --------
+#pragma unroll
+    for (int u = 0; u < TS_GROUPS; u++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint32_t kk = key[u][q];
+            const int p = 4 * (tid + TS_THREADS * u) + q;
+            if (u < nu && 4 * TS_THREADS * u + q < lim && kk >= theta) {
+                if (kk > theta) atomicOr(&gtbits[p >> 5], 1u << (p & 31));
+                else atomicOr(&eqbits[p >> 5], 1u << (p & 31));
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t g = gtbits[tid], e = eqbits[tid];
+    // Both counts in one scan (each total is at most TS_MAXN < 2^16).
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan<TS_THREADS>((uint32_t)__popc(g) | ((uint32_t)__popc(e) << 16),
+                                                             &tot, sh);
+    const uint32_t gt_before = before & 0xffffu, eq_before = before >> 16;
+    // The theta-valued elements kept are the first need_eq in position order.
+    uint32_t keep = 0, ee = e;
+    for (uint32_t left = need_eq > eq_before ? need_eq - eq_before : 0u; ee && left; left--) {
+        const uint32_t low = ee & (0u - ee);
+        keep |= low;
+        ee ^= low;
+    }
+    uint32_t sel = g | keep;
+    uint32_t pos = gt_before + min(eq_before, need_eq);
+    while (sel) {
+        const int bit = __ffs(sel) - 1;
+        sel &= sel - 1u;
+        if (pos < (uint32_t)k) out[pos] = (tid << 5) + bit;  // exactly k are selected
+        pos++;
+    }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible)
@@ -967,6 +1128,11 @@ void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, cons
     // workgroups.  Each kernel skips the rows the other path owns.
     // The row kernel also samples the long rows (the first step of their
     // path), so it goes first.
+    if (max_visible <= TS_MAXN) {
+        hipLaunchKernelGGL(topk_short_kernel, item_grid(1, num_rows), dim3(TS_THREADS), 0, stream, vis, scores, ld, k,
+                           indices, (int)num_rows);
+        return;
+    }
     const bool has_long = max_visible > TR_ROW_PATH_MAXN;
     hipLaunchKernelGGL(topk_rows_kernel, item_grid(1, num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
                        indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr, (int)num_rows);

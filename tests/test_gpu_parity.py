@@ -221,6 +221,37 @@ def test_topk_bitexact_synthetic(dsa, oracle_mod, kind, k):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "signed_zeros", "coarse", "tiny"])
+@pytest.mark.parametrize("k", [2048, 1, 7, 300])
+def test_topk_bitexact_short_rows(dsa, oracle_mod, kind, k):
+    """Calls whose rows all have at most 8,192 positions take the 256-thread
+    kernel: every length class up to the limit, NaN, infinities, and a row
+    with more NaN than the selection can avoid (NaN orders lowest, the lower
+    positions first)."""
+    lens = np.array([1, 5, 300, 2047, 2048, 2049, 4095, 4096, 4097, 5000, 8191, 8192, 3000], np.int32)
+    s = wl.random_scores(zlib.crc32(f"short/{kind}/{k}".encode()) % 1000, len(lens), int(lens.max()), kind=kind)
+    s[2, 7] = np.nan
+    s[6, 100:110] = -np.inf
+    s[7, 3] = np.inf
+    s[12, 1000:2900] = np.nan
+    got = run_topk(dsa, lens, s, k)
+    ref = oracle_mod.topk(lens, s, k)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_short_and_long_kernels_agree(dsa):
+    """The same rows of at most 8,192 positions, once alone (256-thread
+    kernel) and once beside a longer row (1024-thread kernel)."""
+    lens = np.array([2049, 3000, 4097, 6000, 8192, 8000, 2500], np.int32)
+    kinds = ["normal", "ties", "coarse", "tiny", "normal", "zeros", "signed_zeros"]
+    s = np.concatenate([wl.random_scores(60 + i, 1, 9000, kind=kd) for i, kd in enumerate(kinds)])
+    short = run_topk(dsa, lens, s[:, :8192], 2048)
+    long_lens = np.concatenate([lens, [9000]]).astype(np.int32)
+    long_s = np.concatenate([s, wl.random_scores(70, 1, 9000, kind="normal")])
+    both = run_topk(dsa, long_lens, long_s, 2048)
+    assert np.array_equal(short, both[: len(lens)])
+
+
 def test_topk_bitexact_long_rows_and_overflow(dsa, oracle_mod):
     # 65,536-position rows (one workgroup per row): normal scores (sampled
     # fast path), 8-valued ties and all-equal rows (candidate overflow, exact
