@@ -85,6 +85,10 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
 
     __shared__ __attribute__((aligned(16))) uint8_t keys[2][IDX_TILE_POS * IDX_KEY_PITCH];
     __shared__ int s_nmax;
+    // Each wave's 4 rows x 128 scores of the current tile, gathered here so
+    // that they leave as 16-byte row pieces (two stores per lane per tile
+    // instead of eight 4-byte ones).
+    __shared__ __attribute__((aligned(16))) float sst[8][4][IDX_TILE_POS + 4];
     if (threadIdx.x == 0) s_nmax = 0;
     __syncthreads();
     if (threadIdx.x < IDX_TILE_ROWS) atomicMax(&s_nmax, vis[r0 + threadIdx.x]);
@@ -136,9 +140,6 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
     for (int h = 0; h < NH; h++) pre[h] = u32x4{0u, 0u, 0u, 0u};
     if (tt < ntile) load_tile(tt, pre);
     int buf = 0;
-    int nmine = nrow[0];
-#pragma unroll
-    for (int i = 1; i < 4; i++) nmine = (g == i) ? nrow[i] : nmine;
     for (; tt < ntile; tt += gridDim.x, buf ^= 1) {
 #pragma unroll
         for (int h = 0; h < NH; h++)
@@ -195,19 +196,37 @@ __global__ __launch_bounds__(512) void indexer_tile_kernel(
             if ((u & 3) == 3) {
                 const int pg = u >> 2;
                 if (pg + 2 < NU / 4) ldkv(pg + 2);  // its buffer's last reader was unit u
-                // Lane group g stores row 4 wave + g: 16 consecutive scores.
-                const float mine = xrow_reduce_scatter4(part);
-                const int pos = p0 + 16 * pg + j;
-                if (pos < nmine) __builtin_nontemporal_store(mine, &scores[(int64_t)(r0 + 4 * wave + g) * ld + pos]);
+                // Lane group g holds row 4 wave + g: 16 consecutive scores.
+                sst[wave][g][16 * pg + j] = xrow_reduce_scatter4(part);
             }
             if (u + 1 < NU) {
 #pragma unroll
                 for (int q = 0; q < 8; q++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU (measured best of 1..4)
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // The tile's scores, lane l taking row 4 wave + (l >> 4), positions
+        // 8 (l & 15) .. + 7 (same wave, so no barrier).  Non-temporal: read
+        // once, by the top-k; dirty L2 lines would cost the kernel-end
+        // write-back.
+        const int g2 = lane >> 4, c = (lane & 15) * 8;
+        const float4 v0 = *reinterpret_cast<const float4*>(&sst[wave][g2][c]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&sst[wave][g2][c + 4]);
+        int lim = nrow[0];
+#pragma unroll
+        for (int i = 1; i < 4; i++) lim = (g2 == i) ? nrow[i] : lim;
+        float* dst = scores + (int64_t)(r0 + 4 * wave + g2) * ld + p0 + c;
+        if (p0 + c + 8 <= lim) {
+            __builtin_nontemporal_store(floatx4{v0.x, v0.y, v0.z, v0.w}, reinterpret_cast<floatx4*>(dst));
+            __builtin_nontemporal_store(floatx4{v1.x, v1.y, v1.z, v1.w}, reinterpret_cast<floatx4*>(dst + 4));
+        } else {
+            const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                if (p0 + c + e < lim) __builtin_nontemporal_store(vv[e], dst + e);
         }
     }
 }
