@@ -8,11 +8,18 @@ one query row each (batched decode), seeded synthetic bf16 N(0,1) inputs.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-Roofline: the dominant kernel is the indexer (it streams 256 bytes of index
-key per visible position).  Its average launch duration is measured here with
-HIP events around back-to-back launches of the same call on the same stream;
-achieved = algorithmic bytes per launch / that duration, against the 8 TB/s
-HBM3E peak.  Algorithmic bytes per row = 256 n (keys) + 8192 (q) + 128 (w).
+Roofline: for decode batches (one query row per sequence) the dominant kernel
+is the indexer (it streams 256 bytes of index key per visible position).  Its
+average launch duration is measured here with HIP events around back-to-back
+launches of the same call on the same stream; achieved = algorithmic bytes per
+launch / that duration, against the 8 TB/s HBM3E peak.  Algorithmic bytes per
+row = 256 n (keys) + 8192 (q) + 128 (w).
+
+Workloads whose rows share a sequence (a prefill chunk) read each key once per
+32-row block and are matrix-core work: there the indexer (8,192 FLOP per row
+and visible position) and the attention (139,264 FLOP per row and selected
+position) are priced in FLOPs against the 2.5 PFLOP/s bf16 peak, and the
+roofline object names the attention kernel, timed alone in the same way.
 """
 import argparse
 import hashlib
@@ -204,7 +211,10 @@ def main():
     n = x["visible_len"].astype(np.int64)
     alg_bytes = int(np.sum(256 * n + 8192 + 128))
     achieved = alg_bytes / (ms_idx * 1e-3) / 1e9
-    log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+    if distinct:
+        log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+    else:
+        log(f"[bench] indexer: {ms_idx * 1e3:.1f} us/launch")
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -216,6 +226,28 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
+
+    # Prefill-type workloads: both big kernels in FLOPs (see the module notes).
+    prefill = None
+    if not distinct:
+        ws_at = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, K_TOP), dev)
+        ms_attn = timed(lambda: dsa.dsa_sparse_mla_attn(rows, q_abs, kv, idx, K_TOP, wl.SOFTMAX_SCALE, out, lse,
+                                                        ws_at, stream=stream))
+        idx_flops = int(8192 * np.sum(n))
+        attn_flops = int(139264 * np.sum(np.minimum(n, K_TOP)))
+
+        def mfma_entry(ms, flops):
+            tfs = flops / (ms * 1e-3) / 1e12
+            return {"us": round(ms * 1e3, 2), "alg_flops": flops, "tflops": round(tfs, 2),
+                    "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+
+        prefill = {"indexer": mfma_entry(ms_idx, idx_flops), "attention": mfma_entry(ms_attn, attn_flops),
+                   "step_alg_flops": idx_flops + attn_flops,
+                   "step_mfma_frac": round((idx_flops + attn_flops) / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                                           4)}
+        log(f"[bench] prefill: indexer {prefill['indexer']['tflops']:.0f} TFLOP/s, attention "
+            f"{prefill['attention']['tflops']:.0f} TFLOP/s ({ms_attn * 1e3:.1f} us)")
+        del ws_at
 
     # IndexShare: a 4-layer group in which one "full" layer runs the whole path
     # and three "shared" layers reuse its top-2048 list for their attention
@@ -361,17 +393,22 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_label(w), "rows": R, "max_visible": maxv, "topk": K_TOP,
                    "index_heads": 32, "index_dim": 128, "heads": 64, "latent_row": 576},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "indexer_rows_kernel<false>", "kernel_us": round(ms_idx * 1e3, 2),
-                     "alg_bytes_per_launch": alg_bytes},
+        "roofline": ({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                      "kernel": "indexer_rows_kernel<false>", "kernel_us": round(ms_idx * 1e3, 2),
+                      "alg_bytes_per_launch": alg_bytes} if prefill is None else
+                     {"bound": "mfma", "achieved": prefill["attention"]["tflops"], "peak": MFMA_BF16_PEAK_TFS,
+                      "unit": "TFLOP/s", "frac": prefill["attention"]["mfma_frac"], "traffic": None,
+                      "kernel": "sparse_mla_kernel", "kernel_us": prefill["attention"]["us"],
+                      "alg_flops_per_launch": prefill["attention"]["alg_flops"]}),
         "cpu_baseline": cpu,
         "projections": projections,
         "index_share": share,
         "cache_write": cache_write,
         "paged": paged,
-        "step_alg_bytes": step_bytes,
-        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "prefill": prefill,
+        "step_alg_bytes": step_bytes if prefill is None else None,
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if prefill is None else None,
     }
     print(json.dumps(res), flush=True)
 
