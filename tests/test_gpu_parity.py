@@ -503,16 +503,20 @@ def test_decode_step_rows_beside_shared_blocks(dsa, oracle_mod):
     assert recall_check(idx_a[rows], idx_ref, s64, y["visible_len"]) >= 0.999
 
 
-def test_decode_step_rows_past_grid_y_limit(dsa, oracle_mod):
+@pytest.mark.parametrize("distinct, span", [(False, 4096), (True, 9000)])
+def test_decode_step_rows_past_grid_y_limit(dsa, oracle_mod, distinct, span):
     """70,000 decode rows, more than a launch grid's y dimension holds: every
     per-row kernel spills its rows into z.  Each row's per-row inputs are one
     of 509 drawn templates (row r uses r % 509), with its own length and cache
     base, so a row computed as another or not at all shows.  Every row is
     checked for whole selection counts and finite outputs; rows on both
-    sides of the y limit are checked against the oracle."""
-    R, NT, CACHE = 70000, 509, 6144
+    sides of the y limit are checked against the oracle.  Lengths up to 4,096
+    without the distinct-sequence hint: listed row indexer, 256-thread top-k.
+    Up to 9,000 with it: direct row-indexer grid, 1024-thread top-k."""
+    R, NT = 70000, 509
+    CACHE = 2048 + span
     r = np.arange(R, dtype=np.int64)
-    vis = (1 + (r * 7919) % 4096).astype(np.int32)
+    vis = (1 + (r * 7919) % span).astype(np.int32)
     base = ((r * 97) % 2048).astype(np.int64)
     w = wl.Workload(name="manyrows", seed=31, visible_len=vis[:NT], row_cache_base=base[:NT],
                     seq_len=np.array([CACHE], np.int64), seq_base=np.zeros(1, np.int64), row_seq=np.zeros(NT, np.int64))
@@ -522,7 +526,7 @@ def test_decode_step_rows_past_grid_y_limit(dsa, oracle_mod):
     wts = dev(x["w"]).index_select(0, tmpl)
     q_abs = dev_bf16(x["q_abs"]).index_select(0, tmpl)
     k = 2048
-    rows = make_rows(dsa, vis, base)
+    rows = make_rows(dsa, vis, base, flags=dsa.ROWS_DISTINCT_SEQUENCES if distinct else 0)
     idx = torch.full((R, k), -7, dtype=torch.int32, device=DEV)
     out = torch.full((R, 64, 512), float("nan"), dtype=torch.float32, device=DEV)
     lse = torch.full((R, 64), float("nan"), dtype=torch.float32, device=DEV)
