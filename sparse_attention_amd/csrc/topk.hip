@@ -960,7 +960,7 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
     __shared__ uint32_t eqbits[TS_WORDS];
     __shared__ uint32_t sh[TS_THREADS / 64];
     __shared__ uint32_t wlo[TS_THREADS / 64], whi[TS_THREADS / 64];
-    __shared__ uint32_t s_bin, s_above, s_cnt;
+    __shared__ uint32_t s_bin, s_above;
 
     // ---- the row's keys, into registers ------------------------------------
     // Element (u, q) of thread t is position 4 (t + TS_THREADS u) + q.  A
@@ -1017,7 +1017,6 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
     // and narrows [lo, hi] to the bin holding the need-th largest (k < n, so
     // it exists).  A histogram is cleared for the round after next.
     uint32_t need = (uint32_t)k;
-    uint32_t eq_total = 0;
     for (int round = 0;; round++) {
         uint32_t* h = hist[round & 1];
         const int shift = max(0, bitlen(hi - lo) - 11);
@@ -1031,22 +1030,17 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
             }
         }
         __syncthreads();
-        find_threshold_bin<TS_THREADS, TS_BINS>(h, need, &s_bin, &s_above, sh, &s_cnt);
+        find_threshold_bin<TS_THREADS, TS_BINS>(h, need, &s_bin, &s_above, sh);
         const uint32_t bin = s_bin;
         need -= s_above;
-        const uint32_t cnt = s_cnt;
         for (int i = tid; i < TS_BINS / 4; i += TS_THREADS)
             reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);
         const uint32_t nlo = lo + (bin << shift);
         hi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
         lo = nlo;
-        if (shift == 0) {
-            eq_total = cnt;
-            break;
-        }
+        if (shift == 0) break;
     }
     const uint32_t theta = lo, need_eq = need;
-    (void)eq_total;
 
     // ---- bitmaps, then the ordered output (thread t owns word t) --------
 #pragma unroll
