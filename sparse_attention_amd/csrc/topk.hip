@@ -566,6 +566,36 @@ constexpr int TR_CAP = 8192;                                       // candidate 
 constexpr int TR_CPT = TR_CAP / TR_THREADS;                        // candidate slots per thread
 constexpr int TR_GROUPS = TR_ROW_PATH_MAXN / (4 * TR_THREADS);     // 16 float4 groups per thread
 constexpr int TR_WORDS = TR_ROW_PATH_MAXN / 32;
+constexpr int TR_FEW = 64;  // keys one wave ranks directly to end the radix rounds
+
+// Ends a radix select once at most 64 keys remain in play: called by one
+// whole wave with the m <= 64 remaining keys in few[] (16-byte aligned), it
+// finds theta, the key with fewer than `need` larger keys among them and at
+// least `need` larger-or-equal ones (a single value, and lanes holding it
+// agree on every count), the number need_eq of theta-valued keys to keep and
+// their total.
+__device__ __forceinline__ void rank_few(const uint32_t* few, uint32_t m, uint32_t need, uint32_t* s_theta,
+                                         uint32_t* s_needeq, uint32_t* s_eqtot)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t mine = lane < (int)m ? few[lane] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = 0; i < m; i += 4) {
+        const uint4 o4 = *reinterpret_cast<const uint4*>(&few[i]);
+        const uint32_t o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const bool live = i + e < m;
+            gt += (live && o[e] > mine) ? 1u : 0u;
+            eq += (live && o[e] == mine) ? 1u : 0u;
+        }
+    }
+    if (lane < (int)m && gt < need && need <= gt + eq) {
+        *s_theta = mine;
+        *s_needeq = need - gt;
+        *s_eqtot = eq;
+    }
+}
 
 // The order-preserving key of a score, branch-free (see score_key).
 __device__ __forceinline__ uint32_t key_of(float f)
@@ -629,6 +659,8 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
     __shared__ float wmax[TR_WAVES];
     __shared__ uint32_t sh[TR_THREADS / 64];
     __shared__ uint32_t s_bin, s_above, s_cnt;
+    __shared__ __attribute__((aligned(16))) uint32_t few[TR_FEW];  // the last keys in play (early finish)
+    __shared__ uint32_t s_nfew, s_theta, s_needeq, s_eqtot;
     if (n > max_n) {
         // The multi-workgroup kernels own this row; its first step, the
         // sampled lower bound, runs here (the candidate list is free LDS).
@@ -665,6 +697,7 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
         gtbits[i] = 0u;
         eqbits[i] = 0u;
     }
+    if (tid == 0) s_nfew = 0u;
     // Only the last group can run past the row.
 #pragma unroll
     for (int u = 0; u < TR_GROUPS; u++) {
@@ -863,6 +896,22 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
             eq_total = s_cnt;
             break;
         }
+        // Few keys left in [lo, hi] (the usual case after the first round):
+        // instead of more histogram rounds, one wave ranks them directly.
+        if (!from_regs && s_cnt <= (uint32_t)TR_FEW) {
+#pragma unroll
+            for (int j = 0; j < TR_CPT; j++) {
+                const uint32_t kk = ck[j];
+                if ((uint32_t)(tid + TR_THREADS * j) < ncand && kk >= lo && kk <= hi) few[atomicAdd(&s_nfew, 1u)] = kk;
+            }
+            __syncthreads();
+            if (wave == 0) rank_few(few, s_cnt, need, &s_theta, &s_needeq, &s_eqtot);
+            __syncthreads();
+            lo = s_theta;
+            need = s_needeq;
+            eq_total = s_eqtot;
+            break;
+        }
     }
     const uint32_t theta = lo;
     const uint32_t need_eq = need;
@@ -960,7 +1009,9 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
     __shared__ uint32_t eqbits[TS_WORDS];
     __shared__ uint32_t sh[TS_THREADS / 64];
     __shared__ uint32_t wlo[TS_THREADS / 64], whi[TS_THREADS / 64];
-    __shared__ uint32_t s_bin, s_above;
+    __shared__ uint32_t s_bin, s_above, s_cnt;
+    __shared__ __attribute__((aligned(16))) uint32_t few[TR_FEW];  // the last keys in play (early finish)
+    __shared__ uint32_t s_nfew, s_theta, s_needeq, s_eqtot;
 
     // ---- the row's keys, into registers ------------------------------------
     // Element (u, q) of thread t is position 4 (t + TS_THREADS u) + q.  A
@@ -994,6 +1045,7 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
         reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
     gtbits[tid] = 0u;
     eqbits[tid] = 0u;
+    if (tid == 0) s_nfew = 0u;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
@@ -1030,7 +1082,7 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
             }
         }
         __syncthreads();
-        find_threshold_bin<TS_THREADS, TS_BINS>(h, need, &s_bin, &s_above, sh);
+        find_threshold_bin<TS_THREADS, TS_BINS>(h, need, &s_bin, &s_above, sh, &s_cnt);
         const uint32_t bin = s_bin;
         need -= s_above;
         for (int i = tid; i < TS_BINS / 4; i += TS_THREADS)
@@ -1039,6 +1091,24 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
         hi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
         lo = nlo;
         if (shift == 0) break;
+        // Few keys left in [lo, hi]: one wave ranks them (see rank_few).
+        if (s_cnt <= (uint32_t)TR_FEW) {
+#pragma unroll
+            for (int u = 0; u < TS_GROUPS; u++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const uint32_t kk = key[u][q];
+                    if (u < nu && 4 * TS_THREADS * u + q < lim && kk >= lo && kk <= hi)
+                        few[atomicAdd(&s_nfew, 1u)] = kk;
+                }
+            }
+            __syncthreads();
+            if (tid < 64) rank_few(few, s_cnt, need, &s_theta, &s_needeq, &s_eqtot);
+            __syncthreads();
+            lo = s_theta;
+            need = s_needeq;
+            break;
+        }
     }
     const uint32_t theta = lo, need_eq = need;
 
