@@ -126,6 +126,37 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* h, uint32_t n
     __syncthreads();
 }
 
+constexpr int TR_FEW = 64;  // keys one wave ranks directly to end the radix rounds
+
+// Ends a radix select once at most 64 keys remain in play: called by one
+// whole wave with the m <= 64 remaining keys in few[] (16-byte aligned), it
+// finds theta, the key with fewer than `need` larger keys among them and at
+// least `need` larger-or-equal ones (a single value, and lanes holding it
+// agree on every count), the number need_eq of theta-valued keys to keep and
+// their total.
+__device__ __forceinline__ void rank_few(const uint32_t* few, uint32_t m, uint32_t need, uint32_t* s_theta,
+                                         uint32_t* s_needeq, uint32_t* s_eqtot)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t mine = lane < (int)m ? few[lane] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t i = 0; i < m; i += 4) {
+        const uint4 o4 = *reinterpret_cast<const uint4*>(&few[i]);
+        const uint32_t o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const bool live = i + e < m;
+            gt += (live && o[e] > mine) ? 1u : 0u;
+            eq += (live && o[e] == mine) ? 1u : 0u;
+        }
+    }
+    if (lane < (int)m && gt < need && need <= gt + eq) {
+        *s_theta = mine;
+        *s_needeq = need - gt;
+        *s_eqtot = eq;
+    }
+}
+
 // Sampled lower bound of one long row (n > TR_ROW_PATH_MAXN, so n is well
 // above TS_SAMPLES): TS_BLOCKS blocks of TS_BLOCK consecutive positions spread
 // evenly over the row; theta_lo = the key of the rho-th largest sample, with
@@ -321,13 +352,16 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
     __shared__ uint32_t cgt[TK_MAX_CHUNKS / 2];  // per-chunk counts, in windows of chunks
     __shared__ uint32_t ceq[TK_MAX_CHUNKS / 2];
     __shared__ uint32_t sh[RS_THREADS / 64];
-    __shared__ uint32_t s_bin, s_above;
+    __shared__ uint32_t s_bin, s_above, s_cnt;
+    __shared__ __attribute__((aligned(16))) uint32_t few[TR_FEW];  // the last keys in play (early finish)
+    __shared__ uint32_t s_nfew, s_theta, s_needeq, s_eqtot;
     const uint32_t nl = topk_items(longrows, nlong, num_rows);
     for (uint32_t li = blockIdx.x; li < nl; li += gridDim.x) {
     const int r = topk_item_row(longrows, li);
     const int n = vis[r];
     if (n <= min_n) continue;
     __syncthreads();  // the previous item is done with the shared state
+    if (threadIdx.x == 0) s_nfew = 0u;
 
     uint32_t* rs = rowst + (int64_t)r * TK_ROWST;
     const uint32_t m = rs[RS_CAND];
@@ -363,11 +397,24 @@ __global__ __launch_bounds__(RS_THREADS) void topk_resolve_kernel(const int32_t*
                 if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> shift], 1u);
             }
             __syncthreads();
-            find_threshold_bin<RS_THREADS, TK_BINS>(h, nd, &s_bin, &s_above, sh);
+            find_threshold_bin<RS_THREADS, TK_BINS>(h, nd, &s_bin, &s_above, sh, &s_cnt);
             nd -= s_above;
             lo += s_bin << shift;
             hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << shift) - 1));
             if (shift == 0) break;  // wave-uniform: every thread holds the same lo, hi
+            // Few candidates left in [lo, hi]: one wave ranks them (see rank_few).
+            if (s_cnt <= (uint32_t)TR_FEW) {
+                for (uint32_t i = threadIdx.x; i < m; i += RS_THREADS) {
+                    const uint32_t key = (uint32_t)(cl[i] >> 32);
+                    if (key >= lo && key <= hi) few[atomicAdd(&s_nfew, 1u)] = key;
+                }
+                __syncthreads();
+                if (threadIdx.x < 64) rank_few(few, s_cnt, nd, &s_theta, &s_needeq, &s_eqtot);
+                __syncthreads();
+                lo = s_theta;
+                nd = s_needeq;
+                break;
+            }
         }
         theta = lo;
         need_eq = nd;
@@ -566,36 +613,6 @@ constexpr int TR_CAP = 8192;                                       // candidate 
 constexpr int TR_CPT = TR_CAP / TR_THREADS;                        // candidate slots per thread
 constexpr int TR_GROUPS = TR_ROW_PATH_MAXN / (4 * TR_THREADS);     // 16 float4 groups per thread
 constexpr int TR_WORDS = TR_ROW_PATH_MAXN / 32;
-constexpr int TR_FEW = 64;  // keys one wave ranks directly to end the radix rounds
-
-// Ends a radix select once at most 64 keys remain in play: called by one
-// whole wave with the m <= 64 remaining keys in few[] (16-byte aligned), it
-// finds theta, the key with fewer than `need` larger keys among them and at
-// least `need` larger-or-equal ones (a single value, and lanes holding it
-// agree on every count), the number need_eq of theta-valued keys to keep and
-// their total.
-__device__ __forceinline__ void rank_few(const uint32_t* few, uint32_t m, uint32_t need, uint32_t* s_theta,
-                                         uint32_t* s_needeq, uint32_t* s_eqtot)
-{
-    const int lane = threadIdx.x & 63;
-    const uint32_t mine = lane < (int)m ? few[lane] : 0u;
-    uint32_t gt = 0, eq = 0;
-    for (uint32_t i = 0; i < m; i += 4) {
-        const uint4 o4 = *reinterpret_cast<const uint4*>(&few[i]);
-        const uint32_t o[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const bool live = i + e < m;
-            gt += (live && o[e] > mine) ? 1u : 0u;
-            eq += (live && o[e] == mine) ? 1u : 0u;
-        }
-    }
-    if (lane < (int)m && gt < need && need <= gt + eq) {
-        *s_theta = mine;
-        *s_needeq = need - gt;
-        *s_eqtot = eq;
-    }
-}
 
 // The order-preserving key of a score, branch-free (see score_key).
 __device__ __forceinline__ uint32_t key_of(float f)
