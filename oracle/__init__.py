@@ -28,6 +28,7 @@ def _lib():
         lib = ctypes.CDLL(ORACLE_LIB)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_set_threads.argtypes = [i32]
         lib.oracle_indexer_scores.argtypes = [i32, P, P, P, P, P, f64, P, i64]
         lib.oracle_round_to_f32.argtypes = [i64, P, P]
         lib.oracle_topk.argtypes = [i32, P, P, i64, i32, P]
@@ -49,8 +50,10 @@ def _c(a, dtype):
 
 
 def set_threads(n):
-    """Bound the OpenMP thread count of later calls (OMP_NUM_THREADS semantics)."""
+    """Thread count of later calls: sets OMP_NUM_THREADS (read when the OpenMP
+    runtime starts) and the running library's own count."""
     os.environ["OMP_NUM_THREADS"] = str(int(n))
+    _lib().oracle_set_threads(int(n))
 
 
 def indexer_scores(visible_len, row_cache_base, q_idx, w, k_idx, index_scale=1.0, ld=None):

@@ -26,6 +26,7 @@
  * inside a row is a single ordered loop nest.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -60,6 +61,10 @@ const char* oracle_version(void) { return "dsa-oracle fp64 1"; }
  * q: [R,32,128] bf16 bits; w: [R,32] fp32; k: packed key cache [*,128] bf16
  * bits; out: [R, ld] fp64, only columns [0, n_r) are written.
  */
+/* Thread count of later parallel regions (the OpenMP runtime reads
+ * OMP_NUM_THREADS only once, at its first parallel region).  No arithmetic. */
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n < 1 ? 1 : n); }
+
 void oracle_indexer_scores(int32_t R, const int32_t* n, const int64_t* base, const uint16_t* q,
                            const float* w, const uint16_t* k, double scale, double* out, int64_t ld)
 {
