@@ -266,6 +266,32 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
+    # Decode batches: the other two kernels of the step, each timed alone on
+    # the step's own data (the indexer's scores, the step's index lists), in
+    # algorithmic bytes against the HBM peak.  Top-k: 4 B per visible score
+    # read + the index lists written.  Attention (with its split combine):
+    # 1152 B per selected latent row + q_abs, out_latent, lse and the index
+    # lists per row.
+    decode_kernels = None
+    if distinct:
+        ws_tk = dsa.workspace(dsa.dsa_topk_workspace_size(R, maxv, K_TOP), dev)
+        idx_tk = torch.empty_like(idx)
+        ms_tk = timed(lambda: dsa.dsa_topk_select(rows, scores, K_TOP, idx_tk, ws_tk, stream=stream))
+        ws_at = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, K_TOP), dev)
+        ms_at = timed(lambda: dsa.dsa_sparse_mla_attn(rows, q_abs, kv, idx, K_TOP, wl.SOFTMAX_SCALE, out, lse, ws_at,
+                                                      stream=stream))
+        tk_bytes = int(4 * np.sum(n) + 4 * R * K_TOP)
+        at_bytes = int(1152 * np.sum(np.minimum(n, K_TOP)) + R * (73728 + 131072 + 256 + 4 * K_TOP))
+
+        def hbm_entry(ms, nbytes):
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "gbs": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+        decode_kernels = {"topk": hbm_entry(ms_tk, tk_bytes), "attention_with_combine": hbm_entry(ms_at, at_bytes)}
+        log(f"[bench] top-k: {ms_tk * 1e3:.1f} us, attention + combine: {ms_at * 1e3:.1f} us")
+        del ws_tk, idx_tk, ws_at
+
     # Prefill-type workloads: both big kernels in FLOPs (see the module notes).
     prefill = None
     if not distinct:
@@ -456,6 +482,7 @@ def main():
         "index_share": share,
         "cache_write": cache_write,
         "paged": paged,
+        "decode_kernels": decode_kernels,
         "prefill": prefill,
         "cold": cold,
         "step_alg_bytes": step_bytes if prefill is None else None,
