@@ -470,6 +470,61 @@ def test_decode_step_attention_matches_standalone_call(dsa, R):
         assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref_lse.view(np.uint32)), rep
 
 
+@pytest.mark.parametrize("k, iscale", [(1, 0.25), (300, 3.0), (1000, 1.0)])
+def test_decode_step_other_k_and_index_scale(dsa, oracle_mod, k, iscale):
+    """The fused step at k below 2048 and index scales other than 1, over rows
+    shorter than, equal to and longer than k: equal to the separate calls bit
+    for bit; rows with n <= k select 0..n-1 and pad with -1; longer rows agree
+    with the oracle's selection (recall, near-threshold swaps only); attention
+    agrees with the oracle on the lists used."""
+    lens = [5000, 700, 300, 1, 4096, 2049, k, k + 1]
+    w = wl._decode("kvar", 13, lens, "k variants")
+    x = w.generate()
+    d = device_inputs(x)
+    vis, base = x["visible_len"], x["row_cache_base"]
+    R = len(vis)
+    rows = make_rows(dsa, vis, base)
+    idx = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, int(vis.max()), k), DEV)
+    dsa.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], iscale, d["q_abs"], d["kv_latent"], wl.SOFTMAX_SCALE,
+                        k, idx, out, lse, ws)
+    torch.cuda.synchronize()
+    idx_h, out_h, lse_h = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    # separate calls
+    ld = ld_for(int(vis.max()))
+    scores = torch.empty((R, ld), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_scores(rows, d["q_idx"], d["w"], d["k_idx"], iscale, scores)
+    idx_b = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    dsa.dsa_topk_select(rows, scores, k, idx_b, dsa.workspace(dsa.dsa_topk_workspace_size(R, int(vis.max()), k), DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_h, idx_b.cpu().numpy())
+    out_b, lse_b = run_attn(dsa, x, idx_h, k, d=d)
+    assert np.array_equal(out_h.view(np.uint32), out_b.view(np.uint32))
+    assert np.array_equal(lse_h.view(np.uint32), lse_b.view(np.uint32))
+    for r in range(R):
+        n = int(vis[r])
+        if n <= k:
+            assert np.array_equal(idx_h[r], np.where(np.arange(k) < n, np.arange(k), -1)), r
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(vis, base, x["q_idx"], x["w"], x["k_idx"], x["q_abs"],
+                                                   x["kv_latent"], k, iscale, wl.SOFTMAX_SCALE)
+    for r in range(R):
+        n, kr = int(vis[r]), min(k, int(vis[r]))
+        a = set(idx_h[r][idx_h[r] >= 0].tolist())
+        b = set(idx_ref[r][idx_ref[r] >= 0].tolist())
+        assert len(a) == kr, r
+        if a != b:
+            row = s64[r, :n]
+            theta = np.sort(row)[::-1][kr - 1]
+            band = 5e-3 * max(abs(theta), 1e-3 * np.max(np.abs(row)))
+            assert len(a & b) >= 0.99 * kr, r
+            for j in b - a:
+                assert abs(row[j] - theta) <= band, (r, j)
+    ref_out, ref_lse = oracle_mod.sparse_mla(base, x["q_abs"], x["kv_latent"], idx_h, wl.SOFTMAX_SCALE)
+    check_attention(out_h, lse_h, ref_out, ref_lse, f"k={k}")
+
+
 def test_decode_step_rows_beside_shared_blocks(dsa, oracle_mod):
     """A batch mixing a prefill chunk (two full 32-row blocks on one sequence,
     which the shared-block kernel scores) with decode rows of very different
