@@ -33,6 +33,73 @@ def f(bits):
     return wl.bf16_bits_to_f32(bits).astype(np.float64)
 
 
+
+# --------------------------------------------------------------------------- fp64 -> fp32 rounding
+
+def _rne_f32_exact(x):
+    """IEEE binary32 round-to-nearest-even of the double x, worked out in exact
+    rational arithmetic from the format's definition (24-bit significand,
+    exponents down to -126, subnormal quantum 2^-149, overflow to infinity at
+    or past the midpoint between the largest finite value and 2^128).  Shares
+    nothing with the C cast the oracle uses."""
+    from fractions import Fraction
+    if x != x:
+        return float("nan")
+    if x == 0.0 or math.isinf(x):
+        return x
+    sign = -1.0 if math.copysign(1.0, x) < 0 else 1.0
+    a = Fraction(abs(x))
+    e = math.frexp(abs(x))[1] - 1  # 2^e <= |x| < 2^(e+1)
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = fl * quantum
+    if val >= Fraction(2) ** 128:
+        return sign * math.inf
+    return sign * float(val)
+
+
+def test_round_to_f32_is_round_to_nearest_even(oracle_mod):
+    """oracle.round_to_f32 (the fp64 -> fp32 step in front of the oracle's
+    top-k; "GLM-5.1 架构深度拆解" §3.6 step 5 computes the scores as an fp32
+    einsum) against an exact rational evaluation of IEEE round-to-nearest-even:
+    exact ties between neighbouring floats (which must go to the even
+    significand, so truncation and round-half-up both fail), one double ulp to
+    either side of each tie, the overflow threshold, subnormals, signed zeros,
+    infinities and ordinary values over many binades."""
+    g = np.random.default_rng(3)
+    vals = []
+    # neighbouring fp32 pairs (normal and subnormal) and their exact midpoints
+    lo = np.concatenate([
+        (g.standard_normal(400) * np.exp2(g.integers(-60, 60, 400))).astype(np.float32),
+        (g.integers(1, 1 << 23, 200) * np.float64(2.0 ** -149)).astype(np.float32),  # subnormals
+        np.array([1.0, 3.0, 2.0 ** -126, 2.0 ** -149, np.finfo(np.float32).max], np.float32)])
+    lo = lo[np.isfinite(lo)]
+    with np.errstate(over="ignore"):
+        hi = np.nextafter(lo, np.float32(np.inf), dtype=np.float32)
+    for a, b in zip(lo.astype(np.float64), hi.astype(np.float64)):
+        if not math.isfinite(b):
+            b = 2.0 ** 128  # the rounding boundary above the largest finite value
+        mid = (a + b) / 2  # exact in fp64: 25 significant bits at most
+        vals += [mid, np.nextafter(mid, -np.inf), np.nextafter(mid, np.inf), -mid]
+    vals += [0.0, -0.0, math.inf, -math.inf, 2.0 ** -150, 3 * 2.0 ** -150, 2.0 ** -151,
+             np.nextafter(2.0 ** -150, 1.0), 1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, 1e300, -1e300, 1e-300]
+    vals += list(g.standard_normal(2000) * np.exp2(g.integers(-140, 127, 2000)))
+    x = np.array(vals, np.float64)
+    got = oracle_mod.round_to_f32(x).astype(np.float64)
+    want = np.array([_rne_f32_exact(float(v)) for v in x])
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), x[~same][:5]
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[want == 0]), np.signbit(want[want == 0]))
+    # ties really occur in the sample and land on even significands
+    ties = (1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, 3 * 2.0 ** -150)
+    assert list(oracle_mod.round_to_f32(np.array(ties))) == [1.0, 1.0 + 2.0 ** -22, 2.0 ** -148]
+
+
 # --------------------------------------------------------------------------- inputs
 
 def test_bf16_rounding_matches_torch():
