@@ -144,6 +144,42 @@ def _ptr(t, name, dtypes=None):
     return t.data_ptr()
 
 
+def _need(t, count, name):
+    """Raises DsaError (invalid argument) unless tensor t holds at least
+    `count` elements.  The C ABI sees only pointers, so the binding checks
+    every buffer against the call's dimensions before any kernel could read
+    or write past it."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() < count:
+        raise DsaError(1, f"{name} holds {t.numel()} elements, the call needs at least {count}")
+
+
+def _scores_ld(rows, scores, ld):
+    """Row stride of a scores buffer: its last dimension unless given; the
+    buffer must hold num_rows rows of that stride, each >= max_visible."""
+    if scores is None:
+        return 0 if ld is None else int(ld)
+    ld = int(scores.shape[-1]) if ld is None else int(ld)
+    if ld < rows.max_visible:
+        raise DsaError(1, f"scores row stride {ld} < max_visible {rows.max_visible}")
+    _need(scores, rows.num_rows * ld, "scores")
+    return ld
+
+
+def _need_rows(rows, q_idx=None, w=None, q_abs=None, indices=None, k=None, out_latent=None, out_lse=None):
+    R = rows.num_rows
+    _need(q_idx, R * INDEX_HEADS * INDEX_DIM, "q_idx")
+    _need(w, R * INDEX_HEADS, "w")
+    _need(q_abs, R * HEADS * ROW_DIM, "q_abs")
+    if indices is not None and k is not None:
+        _need(indices, R * int(k), "indices")
+    _need(out_latent, R * HEADS * LATENT_DIM, "out_latent")
+    _need(out_lse, R * HEADS, "out_lse")
+
+
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
@@ -215,7 +251,8 @@ def workspace(nbytes, device):
 
 def dsa_indexer_scores(rows, q_idx, w, k_idx, index_scale, scores, ld=None, stream=None):
     lib = load_library()
-    ld = scores.shape[-1] if ld is None else ld
+    _need_rows(rows, q_idx=q_idx, w=w)
+    ld = _scores_ld(rows, scores, ld)
     _check(lib.dsa_indexer_scores(rows.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
                                   _ptr(k_idx, "k_idx", _BF16), float(index_scale),
                                   _ptr(scores, "scores", (torch.float32,)), int(ld), _stream(stream, scores)))
@@ -227,7 +264,8 @@ def dsa_topk_workspace_size(num_rows, max_visible, k):
 
 def dsa_topk_select(rows, scores, k, indices, ws, ld=None, stream=None):
     lib = load_library()
-    ld = scores.shape[-1] if ld is None else ld
+    _need_rows(rows, indices=indices, k=k)
+    ld = _scores_ld(rows, scores, ld)
     _check(lib.dsa_topk_select(rows.c, _ptr(scores, "scores", (torch.float32,)), int(ld), int(k),
                                _ptr(indices, "indices", (torch.int32,)), _ptr(ws, "ws"),
                                ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream, scores)))
@@ -240,6 +278,7 @@ def dsa_sparse_mla_workspace_size(num_rows, k):
 def dsa_sparse_mla_attn(rows, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse=None, ws=None,
                         stream=None):
     lib = load_library()
+    _need_rows(rows, q_abs=q_abs, indices=indices, k=k, out_latent=out_latent, out_lse=out_lse)
     _check(lib.dsa_sparse_mla_attn(rows.c, _ptr(q_abs, "q_abs", _BF16), _ptr(kv_latent, "kv_latent", _BF16),
                                    _ptr(indices, "indices", (torch.int32,)), int(k), float(softmax_scale),
                                    _ptr(out_latent, "out_latent", (torch.float32,)),
@@ -255,6 +294,7 @@ def dsa_decode_step_workspace_size(num_rows, max_visible, k):
 def dsa_decode_step(rows, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices, out_latent,
                     out_lse=None, ws=None, stream=None):
     lib = load_library()
+    _need_rows(rows, q_idx=q_idx, w=w, q_abs=q_abs, indices=indices, k=k, out_latent=out_latent, out_lse=out_lse)
     _check(lib.dsa_decode_step(rows.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
                                _ptr(k_idx, "k_idx", _BF16), float(index_scale), _ptr(q_abs, "q_abs", _BF16),
                                _ptr(kv_latent, "kv_latent", _BF16), float(softmax_scale), int(k),
@@ -269,6 +309,10 @@ def dsa_absorb_queries(q_nope, q_pe, kv_b_weight, q_abs, stream=None):
     """q_abs [R,64,576] bf16 = [W_UK^T q_nope || q_pe] per head."""
     lib = load_library()
     R = int(q_nope.shape[0])
+    _need(q_nope, R * HEADS * 192, "q_nope")
+    _need(q_pe, R * HEADS * ROPE_DIM, "q_pe")
+    _need(kv_b_weight, HEADS * 448 * LATENT_DIM, "kv_b_weight")
+    _need(q_abs, R * HEADS * ROW_DIM, "q_abs")
     _check(lib.dsa_absorb_queries(R, _ptr(q_nope, "q_nope", _BF16), _ptr(q_pe, "q_pe", _BF16),
                                   _ptr(kv_b_weight, "kv_b_weight", _BF16), _ptr(q_abs, "q_abs", _BF16),
                                   _stream(stream, q_abs)))
@@ -278,6 +322,9 @@ def dsa_v_up_proj(o_latent, kv_b_weight, out, stream=None):
     """out [R,64,256] fp32 = W_UV bf16(o_latent) per head."""
     lib = load_library()
     R = int(o_latent.shape[0])
+    _need(o_latent, R * HEADS * LATENT_DIM, "o_latent")
+    _need(kv_b_weight, HEADS * 448 * LATENT_DIM, "kv_b_weight")
+    _need(out, R * HEADS * 256, "out")
     _check(lib.dsa_v_up_proj(R, _ptr(o_latent, "o_latent", (torch.float32,)),
                              _ptr(kv_b_weight, "kv_b_weight", _BF16), _ptr(out, "out", (torch.float32,)),
                              _stream(stream, out)))
@@ -302,6 +349,14 @@ def dsa_cache_write(hidden, wk_weight, k_norm_weight, k_norm_bias, k_norm_eps, k
     rows `slots` of the two caches (negative slot: token skipped)."""
     lib = load_library()
     N = int(hidden.shape[0])
+    _need(hidden, N * HIDDEN, "hidden")
+    _need(wk_weight, INDEX_DIM * HIDDEN, "wk_weight")
+    _need(k_norm_weight, INDEX_DIM, "k_norm_weight")
+    _need(k_norm_bias, INDEX_DIM, "k_norm_bias")
+    _need(kv_a_weight, ROW_DIM * HIDDEN, "kv_a_weight")
+    _need(kv_norm_weight, LATENT_DIM, "kv_norm_weight")
+    _need(positions, N, "positions")
+    _need(slots, N, "slots")
     _check(lib.dsa_cache_write(N, _ptr(hidden, "hidden", _BF16), _ptr(wk_weight, "wk_weight", _BF16),
                                _ptr(k_norm_weight, "k_norm_weight", (torch.float32,)),
                                _ptr(k_norm_bias, "k_norm_bias", (torch.float32,)), float(k_norm_eps),
@@ -316,7 +371,8 @@ def dsa_cache_write(hidden, wk_weight, k_norm_weight, k_norm_bias, k_norm_eps, k
 
 def dsa_indexer_scores_paged(rows, paged, q_idx, w, k_pool, index_scale, scores, ld=None, stream=None):
     lib = load_library()
-    ld = scores.shape[-1] if ld is None else ld
+    _need_rows(rows, q_idx=q_idx, w=w)
+    ld = _scores_ld(rows, scores, ld)
     _check(lib.dsa_indexer_scores_paged(rows.c, paged.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
                                         _ptr(k_pool, "k_pool", _BF16), float(index_scale),
                                         _ptr(scores, "scores", (torch.float32,)), int(ld), _stream(stream, scores)))
@@ -329,6 +385,7 @@ def dsa_sparse_mla_paged_workspace_size(num_rows, k):
 def dsa_sparse_mla_attn_paged(rows, paged, q_abs, kv_pool, indices, k, softmax_scale, out_latent, out_lse=None,
                               ws=None, stream=None):
     lib = load_library()
+    _need_rows(rows, q_abs=q_abs, indices=indices, k=k, out_latent=out_latent, out_lse=out_lse)
     _check(lib.dsa_sparse_mla_attn_paged(rows.c, paged.c, _ptr(q_abs, "q_abs", _BF16), _ptr(kv_pool, "kv_pool", _BF16),
                                          _ptr(indices, "indices", (torch.int32,)), int(k), float(softmax_scale),
                                          _ptr(out_latent, "out_latent", (torch.float32,)),
@@ -344,6 +401,7 @@ def dsa_decode_step_paged_workspace_size(num_rows, max_visible, k):
 def dsa_decode_step_paged(rows, paged, q_idx, w, k_pool, index_scale, q_abs, kv_pool, softmax_scale, k, indices,
                           out_latent, out_lse=None, ws=None, stream=None):
     lib = load_library()
+    _need_rows(rows, q_idx=q_idx, w=w, q_abs=q_abs, indices=indices, k=k, out_latent=out_latent, out_lse=out_lse)
     _check(lib.dsa_decode_step_paged(rows.c, paged.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
                                      _ptr(k_pool, "k_pool", _BF16), float(index_scale), _ptr(q_abs, "q_abs", _BF16),
                                      _ptr(kv_pool, "kv_pool", _BF16), float(softmax_scale), int(k),

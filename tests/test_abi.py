@@ -253,3 +253,102 @@ def test_cache_write_workspace_and_validation(lib):
     assert f(ws=0x10010) == MISALIGNED
     if not HAS_GPU:
         assert f() == NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# The binding checks every buffer's size against the call's dimensions before
+# calling the library (the C ABI sees pointers only, so an undersized output
+# would otherwise be written past its end).  CPU tensors suffice: the size
+# checks run before any device or pointer check.
+
+def _fake_rows(R=4, maxv=100):
+    import types
+    return types.SimpleNamespace(num_rows=R, max_visible=maxv, c=None)
+
+
+def _t(n, dtype=torch.float32):
+    return torch.zeros(int(n), dtype=dtype)
+
+
+def _expect_size_error(fn, name):
+    with pytest.raises(m.DsaError) as e:
+        fn()
+    assert e.value.status == INVALID and name in e.value.detail, e.value.detail
+
+
+def test_binding_rejects_undersized_buffers(lib):
+    R, maxv, k = 4, 100, 2048
+    rows = _fake_rows(R, maxv)
+    bf = torch.bfloat16
+    good = dict(q_idx=_t(R * 32 * 128, bf), w=_t(R * 32), k_idx=_t(200 * 128, bf), q_abs=_t(R * 64 * 576, bf),
+                kv=_t(200 * 576, bf), idx=_t(R * k, torch.int32), out=_t(R * 64 * 512), lse=_t(R * 64))
+
+    def with_(**kw):
+        d = dict(good)
+        d.update(kw)
+        return d
+
+    def step(d):
+        return lambda: m.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], 1.0, d["q_abs"], d["kv"], 0.0625, k,
+                                         d["idx"], d["out"], d["lse"], None)
+
+    _expect_size_error(step(with_(idx=_t(R * k - 1, torch.int32))), "indices")
+    _expect_size_error(step(with_(out=_t(R * 64 * 512 - 4))), "out_latent")
+    _expect_size_error(step(with_(lse=_t(R * 64 - 1))), "out_lse")
+    _expect_size_error(step(with_(q_idx=_t(R * 32 * 128 - 8, bf))), "q_idx")
+    _expect_size_error(step(with_(q_abs=_t((R - 1) * 64 * 576, bf))), "q_abs")
+    _expect_size_error(step(with_(w=_t(R * 32 - 1))), "w")
+    # the attention call and its paged form
+    _expect_size_error(lambda: m.dsa_sparse_mla_attn(rows, good["q_abs"], good["kv"], _t(R * k - 1, torch.int32), k,
+                                                     0.0625, good["out"], good["lse"]), "indices")
+    _expect_size_error(lambda: m.dsa_sparse_mla_attn(rows, good["q_abs"], good["kv"], good["idx"], k, 0.0625,
+                                                     _t(100), good["lse"]), "out_latent")
+    _expect_size_error(lambda: m.dsa_sparse_mla_attn_paged(rows, None, good["q_abs"], good["kv"], good["idx"], k,
+                                                           0.0625, good["out"], _t(3)), "out_lse")
+    # scores: too few rows, a flat buffer, a stride below max_visible
+    _expect_size_error(lambda: m.dsa_indexer_scores(rows, good["q_idx"], good["w"], good["k_idx"], 1.0,
+                                                    _t((R - 1) * 100).view(R - 1, 100)), "scores")
+    _expect_size_error(lambda: m.dsa_indexer_scores(rows, good["q_idx"], good["w"], good["k_idx"], 1.0,
+                                                    _t(R * 100)), "scores")
+    _expect_size_error(lambda: m.dsa_indexer_scores(rows, good["q_idx"], good["w"], good["k_idx"], 1.0,
+                                                    _t(R * 96).view(R, 96)), "max_visible")
+    _expect_size_error(lambda: m.dsa_topk_select(rows, _t(R * 100).view(R, 100), k, _t(R * k - 2, torch.int32),
+                                                 None), "indices")
+    _expect_size_error(lambda: m.dsa_indexer_scores_paged(rows, None, _t(8, bf), good["w"], good["k_idx"], 1.0,
+                                                          _t(R * 100).view(R, 100)), "q_idx")
+    _expect_size_error(lambda: m.dsa_decode_step_paged(rows, None, good["q_idx"], good["w"], good["k_idx"], 1.0,
+                                                       good["q_abs"], good["kv"], 0.0625, k, good["idx"], _t(5),
+                                                       None), "out_latent")
+    # projections and the cache writer
+    kvb = _t(64 * 448 * 512, bf)
+    _expect_size_error(lambda: m.dsa_absorb_queries(_t(3 * 64 * 192, bf).view(3, 64, 192), _t(3 * 64 * 64, bf),
+                                                    kvb, _t(2 * 64 * 576, bf)), "q_abs")
+    _expect_size_error(lambda: m.dsa_absorb_queries(_t(3 * 64 * 192, bf).view(3, 64, 192), _t(3 * 64 * 64, bf),
+                                                    _t(100, bf), _t(3 * 64 * 576, bf)), "kv_b_weight")
+    _expect_size_error(lambda: m.dsa_v_up_proj(_t(2 * 64 * 512).view(2, 64, 512), kvb, _t(2 * 64 * 255)), "out")
+    N = 3
+    cw = dict(hidden=_t(N * 6144, bf).view(N, 6144), wk=_t(128 * 6144, bf), kg=_t(128), kb=_t(128),
+              kva=_t(576 * 6144, bf), kvg=_t(512), pos=_t(N, torch.int32), slots=_t(N, torch.int64))
+
+    def cwcall(**kw):
+        d = dict(cw)
+        d.update(kw)
+        return lambda: m.dsa_cache_write(d["hidden"], d["wk"], d["kg"], d["kb"], 1e-6, d["kva"], d["kvg"], 1e-5,
+                                         d["pos"], d["slots"], 1e6, _t(128, bf), _t(576, bf), None)
+
+    _expect_size_error(cwcall(slots=_t(N - 1, torch.int64)), "slots")
+    _expect_size_error(cwcall(kva=_t(575 * 6144, bf)), "kv_a_weight")
+    _expect_size_error(cwcall(kvg=_t(511)), "kv_norm_weight")
+
+
+def test_binding_passes_correctly_sized_buffers_on_to_the_device_checks(lib):
+    """Buffers of exactly the needed size pass the size checks; the call then
+    stops at the device-placement check (CPU tensors here)."""
+    R, k = 4, 2048
+    rows = _fake_rows(R, 100)
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="device tensor"):
+        m.dsa_sparse_mla_attn(rows, _t(R * 64 * 576, bf), _t(576, bf), _t(R * k, torch.int32), k, 0.0625,
+                              _t(R * 64 * 512).view(R, 64, 512), _t(R * 64))
+    with pytest.raises(ValueError, match="device tensor"):
+        m.dsa_indexer_scores(rows, _t(R * 32 * 128, bf), _t(R * 32), _t(128, bf), 1.0, _t(R * 100).view(R, 100))
