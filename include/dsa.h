@@ -171,14 +171,26 @@ DSA_API dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_a
                                  float* out_latent, float* out_lse, void* ws, size_t ws_bytes,
                                  void* hip_stream);
 
-/* Workspace bytes dsa_decode_step needs for these sizes (host arithmetic only). */
+/* Budget, in bytes, of the fp32 score rows dsa_decode_step holds at a time. */
+#define DSA_STEP_SCORES_BUDGET (1u << 30)
+
+/* Workspace bytes dsa_decode_step needs for these sizes (host arithmetic only):
+ *   align256(C * ld * 4) + align256(4 C) + 256 + align256(dsa_topk_workspace_size(C, max_visible, k))
+ *   + align256(dsa_sparse_mla_workspace_size(R, k))
+ * with ld = max_visible rounded up to a multiple of 4 and C the rows scored at
+ * a time: C = R when R * ld * 4 <= DSA_STEP_SCORES_BUDGET, otherwise the
+ * largest multiple of 32 with C * ld * 4 <= DSA_STEP_SCORES_BUDGET, at least
+ * 32.  The score rows of a call thus take at most max(1 GiB, 32 * ld * 4). */
 DSA_API size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k);
 
 /*
  * The whole path in one call: dsa_indexer_scores into workspace, then
  * dsa_topk_select into `indices`, then dsa_sparse_mla_attn.  Arguments mean
  * what they mean above; `indices` [R, k] int32 receives the selection.
- * ws_bytes >= dsa_decode_step_workspace_size(R, max_visible, k).
+ * ws_bytes >= dsa_decode_step_workspace_size(R, max_visible, k).  Rows are
+ * scored and selected C at a time (C as above; chunks start at multiples of
+ * 32 rows), then attended in one pass; results are those of the separate
+ * calls over all rows at once, bit for bit.
  */
 DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, const float* w,
                              const void* k_idx, float index_scale, const void* q_abs,

@@ -126,6 +126,32 @@ dsa_status_t after_launch(hipStream_t stream, const char* what)
 
 size_t scores_ld(int32_t max_visible) { return dsa::align_up((size_t)max_visible, 4); }
 
+// Rows the fused step scores and selects at a time (see dsa_decode_step in
+// dsa.h): all of them while their fp32 score rows fit the budget, else the
+// largest multiple of 32 rows that fits (at least 32).  Chunks start on
+// multiples of 32 rows, so the indexer's 32-row blocks are those of the whole
+// call and the results do not depend on the chunking.
+int32_t step_chunk_rows(int32_t num_rows, int32_t max_visible)
+{
+    const size_t row_bytes = scores_ld(max_visible) * 4;
+    if ((size_t)num_rows * row_bytes <= (size_t)DSA_STEP_SCORES_BUDGET) return num_rows;
+    size_t c = (size_t)DSA_STEP_SCORES_BUDGET / row_bytes / 32 * 32;
+    if (c < 32) c = 32;
+    return c < (size_t)num_rows ? (int32_t)c : num_rows;
+}
+
+// Workspace of the fused step when it scores C rows at a time: the chunk's
+// score rows, the indexer's row list and the top-k state for C rows, and the
+// attention's split partials for all rows.
+size_t step_ws_bytes(int32_t num_rows, int32_t max_visible, int32_t k, int32_t C)
+{
+    size_t b = dsa::align_up((size_t)C * scores_ld(max_visible) * 4, 256);
+    b += dsa::align_up(dsa::indexer_list_bytes(C), 256);
+    b += dsa::align_up(dsa::topk_workspace_bytes(C, max_visible), 256);
+    b += dsa::align_up(dsa::attn_workspace_bytes(num_rows, k), 256);
+    return b;
+}
+
 constexpr dsa::PagedCache kPacked{nullptr, 0, 0};
 
 // Validates a block-table description against the rows and converts it.
@@ -354,11 +380,7 @@ dsa_status_t dsa_sparse_mla_attn_paged(const dsa_rows_t* rows, const dsa_paged_t
 size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
 {
     if (num_rows < 1 || max_visible < 1 || k < 1 || k > DSA_TOPK_MAX) return 0;
-    size_t b = dsa::align_up((size_t)num_rows * scores_ld(max_visible) * 4, 256);
-    b += dsa::align_up(dsa::indexer_list_bytes(num_rows), 256);
-    b += dsa::align_up(dsa_topk_workspace_size(num_rows, max_visible, k), 256);
-    b += dsa::align_up(dsa_sparse_mla_workspace_size(num_rows, k), 256);
-    return b;
+    return step_ws_bytes(num_rows, max_visible, k, step_chunk_rows(num_rows, max_visible));
 }
 
 size_t dsa_decode_step_paged_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k)
@@ -371,10 +393,11 @@ size_t dsa_decode_step_paged_workspace_size(int32_t num_rows, int32_t max_visibl
 
 namespace {
 
-dsa_status_t decode_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_idx, const float* w,
-                         const void* k_idx, float index_scale, const void* q_abs, const void* kv_latent,
-                         float softmax_scale, int32_t k, int32_t* indices, float* out_latent, float* out_lse,
-                         void* ws, size_t ws_bytes, void* hip_stream)
+// The fused step with C rows scored at a time (0: the default chunking of
+// dsa_decode_step_workspace_size).
+dsa_status_t check_step_args(const void* q_idx, const float* w, const void* k_idx, float index_scale,
+                             const void* q_abs, const void* kv_latent, float softmax_scale, int32_t k,
+                             const int32_t* indices, const float* out_latent, const float* out_lse)
 {
     DSA_TRY(check_ptr16(q_idx, "q_idx"));
     DSA_TRY(check_ptr16(w, "w"));
@@ -388,34 +411,102 @@ dsa_status_t decode_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, cons
     if (out_lse && !aligned(out_lse, 4)) return fail(DSA_ERR_MISALIGNED, "out_lse not 4-byte aligned");
     if (!good_scale(index_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "index_scale must be finite and > 0");
     if (!good_scale(softmax_scale)) return fail(DSA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-    DSA_TRY(check_ws(ws, ws_bytes,
-                     pc.block_table ? dsa_decode_step_paged_workspace_size(rows->num_rows, rows->max_visible, k)
-                                    : dsa_decode_step_workspace_size(rows->num_rows, rows->max_visible, k)));
-    DSA_TRY(check_device());
+    return DSA_OK;
+}
 
+// Enqueues the fused step with C rows scored at a time (arguments already
+// validated, workspace large enough for C).
+dsa_status_t decode_run(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_idx, const float* w,
+                        const void* k_idx, float index_scale, const void* q_abs, const void* kv_latent,
+                        float softmax_scale, int32_t k, int32_t* indices, float* out_latent, float* out_lse,
+                        void* ws, void* hip_stream, int32_t C)
+{
     hipStream_t st = (hipStream_t)hip_stream;
     const int32_t R = rows->num_rows;
-    const int64_t ld = (int64_t)scores_ld(rows->max_visible);
+    const int32_t maxv = rows->max_visible;
+    const int64_t ld = (int64_t)scores_ld(maxv);
     char* p = (char*)ws;
     float* scores = (float*)p;
-    p += dsa::align_up((size_t)R * ld * 4, 256);
+    p += dsa::align_up((size_t)C * ld * 4, 256);
     void* lws = p;  // the indexer's row list (used when rows may share blocks)
-    p += dsa::align_up(dsa::indexer_list_bytes(R), 256);
+    p += dsa::align_up(dsa::indexer_list_bytes(C), 256);
     void* tws = p;
-    p += dsa::align_up(dsa_topk_workspace_size(R, rows->max_visible, k), 256);
+    p += dsa::align_up(dsa_topk_workspace_size(C, maxv, k), 256);
     void* aws = p;
 
-    dsa::launch_indexer_scores(R, rows->max_visible, rows->visible_len, rows->row_cache_base, (const uint16_t*)q_idx,
-                               w, (const uint16_t*)k_idx, index_scale, scores, ld,
-                               (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0, pc, st, lws);
-    DSA_TRY(after_launch(st, "decode_step/indexer"));
-    dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, R, rows->max_visible);
-    dsa::launch_topk(R, rows->max_visible, rows->visible_len, scores, ld, k, indices, tw, st);
-    DSA_TRY(after_launch(st, "decode_step/topk"));
+    // Scores and selection chunk by chunk (the index lists land in
+    // `indices`), then one attention launch over every row.
+    const bool distinct = (rows->flags & DSA_ROWS_DISTINCT_SEQUENCES) != 0;
+    for (int32_t c0 = 0; c0 < R; c0 += C) {
+        const int32_t nc = R - c0 < C ? R - c0 : C;
+        const int32_t* vis = rows->visible_len + c0;
+        const int64_t* base = rows->row_cache_base + c0;
+        dsa::launch_indexer_scores(nc, maxv, vis, base, (const uint16_t*)q_idx + (int64_t)c0 * DSA_INDEX_HEADS * DSA_INDEX_DIM,
+                                   w + (int64_t)c0 * DSA_INDEX_HEADS, (const uint16_t*)k_idx, index_scale, scores, ld,
+                                   distinct, pc, st, lws);
+        DSA_TRY(after_launch(st, "decode_step/indexer"));
+        dsa::TopkWorkspace tw = dsa::topk_workspace_carve(tws, nc, maxv);
+        dsa::launch_topk(nc, maxv, vis, scores, ld, k, indices + (int64_t)c0 * k, tw, st);
+        DSA_TRY(after_launch(st, "decode_step/topk"));
+    }
     return attn_impl(rows, pc, q_abs, kv_latent, indices, k, softmax_scale, out_latent, out_lse, aws, st);
 }
 
+dsa_status_t decode_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const void* q_idx, const float* w,
+                         const void* k_idx, float index_scale, const void* q_abs, const void* kv_latent,
+                         float softmax_scale, int32_t k, int32_t* indices, float* out_latent, float* out_lse,
+                         void* ws, size_t ws_bytes, void* hip_stream)
+{
+    DSA_TRY(check_step_args(q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices, out_latent,
+                            out_lse));
+    const int32_t R = rows->num_rows;
+    const int32_t C = step_chunk_rows(R, rows->max_visible);
+    DSA_TRY(check_ws(ws, ws_bytes,
+                     step_ws_bytes(R, rows->max_visible, k, C) + (pc.block_table ? paged_attn_extra(R, k) : 0)));
+    DSA_TRY(check_device());
+    return decode_run(rows, pc, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices,
+                      out_latent, out_lse, ws, hip_stream, C);
+}
+
 }  // namespace
+
+namespace dsa {
+
+dsa_status_t decode_step_in_scratch(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                                    float index_scale, const void* q_abs, const void* kv_latent, float softmax_scale,
+                                    int32_t k, int32_t* indices, float* out_latent, float* out_lse,
+                                    size_t scratch_bytes, void* (*scratch_ptr)(), void* hip_stream)
+{
+    g_detail[0] = '\0';
+    DSA_TRY(check_rows(rows));
+    DSA_TRY(check_step_args(q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices, out_latent,
+                            out_lse));
+    // As many rows at a time as the scratch holds: the default chunk if it
+    // fits, else the largest multiple of 32 rows (all rows when fewer than 32).
+    const int32_t R = rows->num_rows, maxv = rows->max_visible;
+    int32_t C = step_chunk_rows(R, maxv);
+    if (step_ws_bytes(R, maxv, k, C) > scratch_bytes) {
+        int32_t lo = 0, hi = C / 32;  // largest m in [1, hi] with 32 m rows fitting, 0 if none
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) / 2;
+            if (step_ws_bytes(R, maxv, k, 32 * mid) <= scratch_bytes) lo = mid;
+            else hi = mid - 1;
+        }
+        if (lo == 0)
+            return fail(DSA_ERR_INVALID_ARGUMENT,
+                        "rows=%d, max_visible=%d, k=%d need %zu bytes of scratch even 32 rows at a time; the scratch "
+                        "holds %zu",
+                        R, maxv, k, step_ws_bytes(R, maxv, k, R < 32 ? R : 32), scratch_bytes);
+        C = 32 * lo;
+    }
+    DSA_TRY(check_device());
+    void* scratch = scratch_ptr();
+    if (!scratch) return fail(DSA_ERR_HIP, "the scratch array's device address is unavailable");
+    return decode_run(rows, kPacked, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices,
+                      out_latent, out_lse, scratch, hip_stream, C);
+}
+
+}  // namespace dsa
 
 extern "C" {
 

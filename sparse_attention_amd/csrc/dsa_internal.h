@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dsa.h"
+
 namespace dsa {
 
 // A paged cache: position p of the sequence whose block-table row is s sits at
@@ -81,6 +83,16 @@ void launch_cache_write(int32_t num_tokens, const uint16_t* hidden, const uint16
                         const float* k_norm_bias, float k_norm_eps, const uint16_t* kv_a, const float* kv_norm_weight,
                         float kv_norm_eps, const int32_t* positions, const int64_t* slots, double rope_theta,
                         uint16_t* k_idx_cache, uint16_t* kv_latent_cache, void* ws, hipStream_t stream);
+
+// ---- fused step over a fixed scratch region ------------------------------
+// Validates the call in full, picks the rows scored at a time so that the
+// step's workspace fits scratch_bytes (an error if 32 rows do not fit), checks
+// the device, then asks scratch_ptr() for the region's device address and
+// enqueues the step there.  scratch_ptr returns nullptr on failure.
+dsa_status_t decode_step_in_scratch(const dsa_rows_t* rows, const void* q_idx, const float* w, const void* k_idx,
+                                    float index_scale, const void* q_abs, const void* kv_latent, float softmax_scale,
+                                    int32_t k, int32_t* indices, float* out_latent, float* out_lse,
+                                    size_t scratch_bytes, void* (*scratch_ptr)(), void* hip_stream);
 
 // Debug aid: when DSA_SYNC_DEBUG=1, synchronize after every launch.
 bool sync_debug();

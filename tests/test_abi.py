@@ -352,3 +352,33 @@ def test_binding_passes_correctly_sized_buffers_on_to_the_device_checks(lib):
                               _t(R * 64 * 512).view(R, 64, 512), _t(R * 64))
     with pytest.raises(ValueError, match="device tensor"):
         m.dsa_indexer_scores(rows, _t(R * 32 * 128, bf), _t(R * 32), _t(128, bf), 1.0, _t(R * 100).view(R, 100))
+
+
+def test_decode_step_workspace_follows_the_chunk_formula(lib):
+    """dsa_decode_step_workspace_size as include/dsa.h spells it out: all rows'
+    fp32 score rows while they fit the 1 GiB budget, else chunks of the
+    largest multiple of 32 rows that fit (at least 32)."""
+    budget = 1 << 30
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    def formula(R, maxv, k):
+        ld = (maxv + 3) // 4 * 4
+        if R * ld * 4 <= budget:
+            C = R
+        else:
+            C = max(32, budget // (ld * 4) // 32 * 32)
+            C = min(C, R)
+        return (a256(C * ld * 4) + a256(4 * C) + 256 + a256(m.dsa_topk_workspace_size(C, maxv, k))
+                + a256(m.dsa_sparse_mla_workspace_size(R, k)))
+
+    for R, maxv in [(64, 32768), (16, 202752), (16512, 131072), (8192, 8192), (1, 4096), (3, 1 << 24),
+                    (40, 1 << 24), (70000, 9000), (2049, 131072)]:
+        assert m.dsa_decode_step_workspace_size(R, maxv, 2048) == formula(R, maxv, 2048), (R, maxv)
+    # the ragged batch (16,512 rows up to 131,072 positions) holds 2,048 rows of scores at a time
+    assert m.dsa_decode_step_workspace_size(16512, 131072, 2048) < 1.2 * budget
+    # the paged step adds the translated index lists and zero row bases
+    R, k = 100, 2048
+    assert (m.dsa_decode_step_paged_workspace_size(R, 32768, k)
+            == m.dsa_decode_step_workspace_size(R, 32768, k) + a256(R * k * 4) + a256(R * 8))
