@@ -13,7 +13,13 @@ is the indexer (it streams 256 bytes of index key per visible position).  Its
 average launch duration is measured here with HIP events around back-to-back
 launches of the same call on the same stream; achieved = algorithmic bytes per
 launch / that duration, against the 8 TB/s HBM3E peak.  Algorithmic bytes per
-row = 256 n (keys) + 8192 (q) + 128 (w).
+row = 256 n (keys) + 8192 (q) + 128 (w).  The roofline object's `step` entry
+prices the whole step the same way: algorithmic bytes of the path per step
+(256 n + 1152 min(n, 2048) + 221,312 per row) over the measured step time.
+
+The default run (the batched-decode workload) also measures the 8,192-token
+causal prefill (`prefill_c2`): the step, the indexer and the attention, each
+timed alone with HIP events, in FLOPs against the bf16 matrix-core peak.
 
 Workloads whose rows share a sequence (a prefill chunk) read each key once per
 32-row block and are matrix-core work: there the indexer (8,192 FLOP per row
@@ -48,7 +54,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", default="c3", help="workload: c1 | c3 | c4 | c5")
+    p.add_argument("--config", default="c3", help="workload: c1 | c2 | c3 | c4 | c5")
+    p.add_argument("--no-prefill", dest="prefill", action="store_false",
+                   help="skip the 8,192-token prefill measurement that accompanies a decode workload")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (oracle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-paged", dest="paged", action="store_false",
@@ -133,6 +141,67 @@ def cpu_baseline(w, x, budget_s):
     oracle.set_threads(cores)
     res["single_thread"] = {"value": m1 / dt1, "unit": "tokens/s", "cores": 1,
                             "sample": f"{m1} of the rows above, once, {dt1:.1f} s"}
+    return res
+
+
+def measure_prefill(dsa, wl, torch, dev, stream, steps, warmup, name="c2"):
+    """Step, indexer and attention of a prefill workload, each timed alone
+    over `steps` back-to-back launches (HIP events on the launch stream), in
+    FLOPs against the bf16 peak."""
+    w = wl.config(name)
+    log(f"[bench] generating {w.name}: {w.num_rows} rows")
+    x = w.generate()
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R, maxv = w.num_rows, w.max_visible
+    q_idx, wts, k_idx = bf(x["q_idx"]), torch.from_numpy(x["w"]).to(dev), bf(x["k_idx"])
+    q_abs, kv = bf(x["q_abs"]), bf(x["kv_latent"])
+    rows = dsa.Rows(torch.from_numpy(x["visible_len"]).to(dev), torch.from_numpy(x["row_cache_base"]).to(dev), maxv)
+    idx = torch.empty((R, K_TOP), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=dev)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, maxv, K_TOP), dev)
+    ld = (maxv + 3) // 4 * 4
+    scores = torch.empty((R, ld), dtype=torch.float32, device=dev)
+    ws_at = dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, K_TOP), dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_step = timed(lambda: dsa.dsa_decode_step(rows, q_idx, wts, k_idx, wl.INDEX_SCALE, q_abs, kv, wl.SOFTMAX_SCALE,
+                                                 K_TOP, idx, out, lse, ws, stream=stream))
+    ms_idx = timed(lambda: dsa.dsa_indexer_scores(rows, q_idx, wts, k_idx, wl.INDEX_SCALE, scores, stream=stream))
+    ms_attn = timed(lambda: dsa.dsa_sparse_mla_attn(rows, q_abs, kv, idx, K_TOP, wl.SOFTMAX_SCALE, out, lse, ws_at,
+                                                    stream=stream))
+    n = x["visible_len"].astype(np.int64)
+    idx_flops = int(8192 * np.sum(n))
+    attn_flops = int(139264 * np.sum(np.minimum(n, K_TOP)))
+
+    def mfma_entry(ms, flops):
+        tfs = flops / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 2), "alg_flops": flops, "tflops": round(tfs, 2),
+                "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+
+    res = {"workload": workload_label(w), "rows": R, "us_per_step": round(ms_step * 1e3, 2),
+           "rows_per_s": round(R / (ms_step * 1e-3), 1),
+           "indexer": mfma_entry(ms_idx, idx_flops), "attention": mfma_entry(ms_attn, attn_flops),
+           "step_alg_flops": idx_flops + attn_flops,
+           "step_mfma_frac": round((idx_flops + attn_flops) / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
+    log(f"[bench] {w.name} prefill: step {ms_step * 1e3:.1f} us, indexer {ms_idx * 1e3:.1f} us "
+        f"({res['indexer']['mfma_frac']:.3f} of bf16 peak), attention {ms_attn * 1e3:.1f} us "
+        f"({res['attention']['mfma_frac']:.3f})")
+    del q_idx, wts, k_idx, q_abs, kv, idx, out, lse, ws, scores, ws_at
     return res
 
 
@@ -432,17 +501,15 @@ def main():
     cache_write = dict(tokens=Nw, **proj_entry(ms_cw, cw_bytes, cw_flops))
     log(f"[bench] cache_write: {ms_cw * 1e3:.1f} us ({Nw} tokens)")
 
-    # A plain 1 GiB device copy: the HBM rate this machine reaches, for context
-    # beside the 8 TB/s specification.
-    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cdst = torch.empty_like(csrc)
-    ms_copy = timed(lambda: cdst.copy_(csrc))
-    copy_gbs = 2 * csrc.numel() * 4 / (ms_copy * 1e-3) / 1e9
-    del csrc, cdst
-    log(f"[bench] 1 GiB device copy: {copy_gbs:.0f} GB/s (read + write)")
-
-    # Step-level algorithmic bytes (whole path) for context.
+    # Step-level algorithmic bytes (whole path).
     step_bytes = int(np.sum(256 * n + 1152 * np.minimum(n, K_TOP) + 82048 + 139264))
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # The 8,192-token causal prefill beside a decode workload (matrix-core
+    # bound; timed alone, its inputs freed afterwards).
+    prefill_c2 = None
+    if args.prefill and prefill is None:
+        prefill_c2 = measure_prefill(dsa, wl, torch, dev, stream, args.steps, args.warmup)
     traffic = traffic_from_profiles("indexer", w.name, src_hash(["indexer.hip", "dsa_device.h"]))
 
     cpu = None
@@ -471,8 +538,10 @@ def main():
         "roofline": ({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                       "kernel": "indexer_rows_kernel<false>", "kernel_us": round(ms_idx * 1e3, 2),
-                      "alg_bytes_per_launch": alg_bytes, "copy_gbs": round(copy_gbs, 1),
-                      "frac_of_copy": round(achieved / copy_gbs, 4)} if prefill is None else
+                      "alg_bytes_per_launch": alg_bytes,
+                      "step": {"alg_bytes": step_bytes, "us": round(ms_step * 1e3, 2),
+                               "achieved": round(step_gbs, 1), "frac": round(step_gbs / HBM_PEAK_GBS, 4)}}
+                     if prefill is None else
                      {"bound": "mfma", "achieved": prefill["attention"]["tflops"], "peak": MFMA_BF16_PEAK_TFS,
                       "unit": "TFLOP/s", "frac": prefill["attention"]["mfma_frac"], "traffic": None,
                       "kernel": "sparse_mla_kernel", "kernel_us": prefill["attention"]["us"],
@@ -484,6 +553,7 @@ def main():
         "paged": paged,
         "decode_kernels": decode_kernels,
         "prefill": prefill,
+        "prefill_c2": prefill_c2,
         "cold": cold,
         "step_alg_bytes": step_bytes if prefill is None else None,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if prefill is None else None,
