@@ -198,6 +198,32 @@ DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, 
                              int32_t* indices, float* out_latent, float* out_lse, void* ws,
                              size_t ws_bytes, void* hip_stream);
 
+/* ---- The fused step without a workspace argument -----------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as dsa_decode_step, with the workspace taken from a scratch array of
+ * DSA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on, from the first call there until the process ends.  The call itself
+ * allocates nothing.  Rows are scored and selected as many at a time as the
+ * scratch holds (the dsa_decode_step_workspace_size formula with the largest
+ * fitting C, a multiple of 32 rows, or all rows when fewer than 32); results
+ * equal dsa_decode_step's bit for bit.  Every call on one device uses that
+ * device's single array: calls that overlap on one device (other streams,
+ * other host threads) race and must be serialized by the caller.
+ * Errors: as for dsa_decode_step, plus DSA_ERR_INVALID_ARGUMENT when even 32
+ * rows at a time (with the attention's split partials for every row) exceed
+ * the scratch (from max_visible of about 500,000 positions up, depending on
+ * the row count); DSA_ERR_HIP if
+ * the scratch array's device address cannot be obtained. */
+#define DSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+DSA_API dsa_status_t dsa_decode_step_noalloc(const dsa_rows_t* rows, const void* q_idx, const float* w,
+                                             const void* k_idx, float index_scale, const void* q_abs,
+                                             const void* kv_latent, float softmax_scale, int32_t k,
+                                             int32_t* indices, float* out_latent, float* out_lse,
+                                             void* hip_stream);
+
 /* ---- Paged caches -------------------------------------------------------
  *
  * The same calls over caches kept in fixed-size blocks of a shared pool, with

@@ -23,7 +23,7 @@ __all__ = [
     "dsa_indexer_scores_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_sparse_mla_attn_paged",
     "dsa_decode_step_paged_workspace_size", "dsa_decode_step_paged", "HIDDEN",
     "INDEX_HEADS", "INDEX_DIM", "HEADS", "LATENT_DIM", "ROPE_DIM", "ROW_DIM", "TOPK_MAX",
-    "ROWS_DISTINCT_SEQUENCES",
+    "ROWS_DISTINCT_SEQUENCES", "dsa_decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 INDEX_HEADS = 32
@@ -34,6 +34,7 @@ ROPE_DIM = 64
 ROW_DIM = 576
 TOPK_MAX = 2048
 HIDDEN = 6144
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -99,6 +100,7 @@ def load_library():
         "dsa_decode_step_paged_workspace_size": ([i32, i32, i32], sz),
         "dsa_decode_step_paged": ([rows_p, paged_p, P, P, P, f32, P, P, f32, i32, P, P, P, P, sz, P], ctypes.c_int),
         "dsa_cache_write": ([i32, P, P, P, P, f32, P, P, f32, P, P, ctypes.c_double, P, P, P, sz, P], ctypes.c_int),
+        "dsa_decode_step_noalloc": ([rows_p, P, P, P, f32, P, P, f32, i32, P, P, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sigs.items():
         fn = getattr(lib, name)
@@ -116,7 +118,7 @@ def exported_symbols():
         "dsa_sparse_mla_attn", "dsa_decode_step_workspace_size", "dsa_decode_step", "dsa_absorb_queries",
         "dsa_v_up_proj", "dsa_index_share_source", "dsa_cache_write_workspace_size", "dsa_cache_write",
         "dsa_indexer_scores_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_sparse_mla_attn_paged",
-        "dsa_decode_step_paged_workspace_size", "dsa_decode_step_paged",
+        "dsa_decode_step_paged_workspace_size", "dsa_decode_step_paged", "dsa_decode_step_noalloc",
     ]
 
 
@@ -410,3 +412,18 @@ def dsa_decode_step_paged(rows, paged, q_idx, w, k_pool, index_scale, q_abs, kv_
                                      _ptr(out_lse, "out_lse", (torch.float32,)), _ptr(ws, "ws"),
                                      ws.numel() * ws.element_size() if ws is not None else 0,
                                      _stream(stream, out_latent)))
+
+
+def dsa_decode_step_noalloc(rows, q_idx, w, k_idx, index_scale, q_abs, kv_latent, softmax_scale, k, indices,
+                            out_latent, out_lse=None, stream=None):
+    """dsa_decode_step without a workspace argument: the library's per-device
+    scratch array serves as the workspace (nothing is allocated; calls that
+    overlap on one device race)."""
+    lib = load_library()
+    _need_rows(rows, q_idx=q_idx, w=w, q_abs=q_abs, indices=indices, k=k, out_latent=out_latent, out_lse=out_lse)
+    _check(lib.dsa_decode_step_noalloc(rows.c, _ptr(q_idx, "q_idx", _BF16), _ptr(w, "w", (torch.float32,)),
+                                       _ptr(k_idx, "k_idx", _BF16), float(index_scale), _ptr(q_abs, "q_abs", _BF16),
+                                       _ptr(kv_latent, "kv_latent", _BF16), float(softmax_scale), int(k),
+                                       _ptr(indices, "indices", (torch.int32,)),
+                                       _ptr(out_latent, "out_latent", (torch.float32,)),
+                                       _ptr(out_lse, "out_lse", (torch.float32,)), _stream(stream, out_latent)))
