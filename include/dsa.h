@@ -178,9 +178,11 @@ DSA_API dsa_status_t dsa_sparse_mla_attn(const dsa_rows_t* rows, const void* q_a
  *   align256(C * ld * 4) + align256(4 C) + 256 + align256(dsa_topk_workspace_size(C, max_visible, k))
  *   + align256(dsa_sparse_mla_workspace_size(R, k))
  * with ld = max_visible rounded up to a multiple of 4 and C the rows scored at
- * a time: C = R when R * ld * 4 <= DSA_STEP_SCORES_BUDGET, otherwise the
- * largest multiple of 32 with C * ld * 4 <= DSA_STEP_SCORES_BUDGET, at least
- * 32.  The score rows of a call thus take at most max(1 GiB, 32 * ld * 4). */
+ * a time: C = R when R * ld * 4 <= DSA_STEP_SCORES_BUDGET; otherwise, with
+ * F = floor(DSA_STEP_SCORES_BUDGET / (ld * 4)) rows fitting the budget, C is
+ * F rounded down to a multiple of 256 when F >= 256, else to a multiple of
+ * 32, and at least 32 (at most R).  The score rows of a call thus take at
+ * most max(1 GiB, 32 * ld * 4). */
 DSA_API size_t dsa_decode_step_workspace_size(int32_t num_rows, int32_t max_visible, int32_t k);
 
 /*
@@ -206,9 +208,9 @@ DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, 
  * DSA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
  * runs on, from the first call there until the process ends.  The call itself
  * allocates nothing.  Rows are scored and selected as many at a time as the
- * scratch holds (the dsa_decode_step_workspace_size formula with the largest
- * fitting C, a multiple of 32 rows, or all rows when fewer than 32); results
- * equal dsa_decode_step's bit for bit.  Every call on one device uses that
+ * scratch holds (the dsa_decode_step_workspace_size formula with C the
+ * largest multiple of 32 rows that fits, or all rows when fewer than 32);
+ * results equal dsa_decode_step's bit for bit.  Every call on one device uses that
  * device's single array: calls that overlap on one device (other streams,
  * other host threads) race and must be serialized by the caller.
  * Errors: as for dsa_decode_step, plus DSA_ERR_INVALID_ARGUMENT when even 32

@@ -128,14 +128,16 @@ size_t scores_ld(int32_t max_visible) { return dsa::align_up((size_t)max_visible
 
 // Rows the fused step scores and selects at a time (see dsa_decode_step in
 // dsa.h): all of them while their fp32 score rows fit the budget, else the
-// largest multiple of 32 rows that fits (at least 32).  Chunks start on
-// multiples of 32 rows, so the indexer's 32-row blocks are those of the whole
-// call and the results do not depend on the chunking.
+// largest multiple of 256 rows that fits (a whole number of rows per CU for
+// the per-row kernels), or of 32 rows below that (at least 32).  Chunks start
+// on multiples of 32 rows, so the indexer's 32-row blocks are those of the
+// whole call and the results do not depend on the chunking.
 int32_t step_chunk_rows(int32_t num_rows, int32_t max_visible)
 {
     const size_t row_bytes = scores_ld(max_visible) * 4;
     if ((size_t)num_rows * row_bytes <= (size_t)DSA_STEP_SCORES_BUDGET) return num_rows;
-    size_t c = (size_t)DSA_STEP_SCORES_BUDGET / row_bytes / 32 * 32;
+    const size_t fit = (size_t)DSA_STEP_SCORES_BUDGET / row_bytes;
+    size_t c = fit >= 256 ? fit / 256 * 256 : fit / 32 * 32;
     if (c < 32) c = 32;
     return c < (size_t)num_rows ? (int32_t)c : num_rows;
 }

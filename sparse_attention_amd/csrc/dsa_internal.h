@@ -49,6 +49,8 @@ struct TopkWorkspace {
     int32_t* longrows;         // [R]: rows the multi-workgroup kernels own, in row order
     uint32_t* nlong;           // their count
     int32_t chunks;            // CH
+    uint32_t* crec;            // chunked path for few rows: [R][CH] (count, largest key, theta_lo, -)
+    unsigned long long* mcand; //   [R][CH][slots] (key, position) in position order
 };
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible);
 TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visible);

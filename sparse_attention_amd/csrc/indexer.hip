@@ -436,11 +436,12 @@ void launch_indexer_scores(int32_t num_rows, int32_t max_visible, const int32_t*
     const bool pg = paged.block_table != nullptr;
     const int nblk = distinct_sequences ? 0 : num_rows / IDX_TILE_ROWS;
     if (nblk > 0) {
-        // Workgroups per shared block: enough for ~2 per CU overall, never
-        // more than the block's key tiles.
+        // Workgroups per shared block: enough for ~2 per CU overall (up to
+        // 32 per block, for calls with few blocks), never more than the
+        // block's key tiles.
         const int tiles = (max_visible + IDX_TILE_POS - 1) / IDX_TILE_POS;
         int cx = (512 + nblk - 1) / nblk;
-        if (cx > 8) cx = 8;
+        if (cx > 32) cx = 32;
         if (cx > tiles) cx = tiles;
         if (cx < 1) cx = 1;
         if (pg)

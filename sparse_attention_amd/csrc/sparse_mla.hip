@@ -114,18 +114,28 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
                                                            const uint16_t* __restrict__ kv,
                                                            const int32_t* __restrict__ idx, int k,
                                                            int num_rows, float scale_log2, int split_len,
-                                                           int pad_rows,
+                                                           int nsplit, int pad_rows,
                                                            float* __restrict__ out, float* __restrict__ lse,
                                                            float* __restrict__ part_o,
                                                            float2* __restrict__ part_ml)
 {
-    // Rows in reverse: in a causal prefill chunk the last rows select the
-    // most positions, and starting them first shortens the tail (the results
-    // do not depend on the order).
-    if (grid_item() >= num_rows) return;
-    const int r = num_rows - 1 - grid_item();
-    const int sp = blockIdx.x;
-    const int nsplit = gridDim.x;
+    // One split per row: rows in reverse (in a causal prefill chunk the last
+    // rows select the most positions, and starting them first shortens the
+    // tail).  Several splits: a one-dimensional grid numbered so that the
+    // splits of a row share an XCD (workgroups go to the eight XCDs in turn),
+    // and the later splits find the row's queries in that XCD's L2.  Results
+    // do not depend on the order.
+    int r, sp;
+    if (nsplit == 1) {
+        if (grid_item() >= num_rows) return;
+        r = num_rows - 1 - grid_item();
+        sp = 0;
+    } else {
+        const int id = blockIdx.x, blk = id / (8 * nsplit), j = id - blk * 8 * nsplit;
+        r = blk * 8 + (j & 7);
+        sp = j >> 3;
+        if (r >= num_rows) return;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const bool scorer = wave < 4;  // wave-uniform role
@@ -537,8 +547,8 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
 int attn_pick_splits(int32_t num_rows, int32_t k)
 {
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
-    // One 256-thread workgroup per CU (the kernel uses the whole register
-    // file of its SIMDs): aim for 256 workgroups.
+    // One 768-thread workgroup per CU (its LDS ring and registers fill the
+    // CU): aim for 256 workgroups.
     int s = (int)((256 + num_rows - 1) / num_rows);
     if (s > 16) s = 16;
     if (s > tiles) s = tiles;
@@ -569,8 +579,11 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
         part_o = (float*)ws;
         part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
     }
-    hipLaunchKernelGGL(sparse_mla_kernel, item_grid(s, num_rows), dim3(AT_THREADS), 0, stream, base, qa, kv, idx,
-                       k, (int)num_rows, softmax_scale * LOG2E, split_len, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
+    // Several splits only occur below 256 rows (attn_pick_splits), so their
+    // one-dimensional grid stays small.
+    const dim3 grid = s == 1 ? item_grid(1, num_rows) : dim3((unsigned)(((num_rows + 7) / 8) * 8 * s));
+    hipLaunchKernelGGL(sparse_mla_kernel, grid, dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k, (int)num_rows,
+                       softmax_scale * LOG2E, split_len, s, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
     if (s > 1)
         hipLaunchKernelGGL(sparse_mla_combine_kernel, item_grid(64, num_rows), dim3(128), 0, stream, part_o, part_ml,
                            s, (int)num_rows, out, lse);

@@ -9,9 +9,13 @@
 //
 // Design: a radix select on the order-preserving 32-bit key of each score.
 // Calls whose rows all have at most 8,192 positions take one 256-thread
-// workgroup per row, several rows to a CU (topk_short_kernel).  Otherwise
-// rows of at most 65,536 positions take one 1024-thread workgroup each (one
-// streaming pass over the row, the rest in LDS; see topk_rows_kernel).
+// workgroup per row, several rows to a CU (topk_short_kernel).  Calls with
+// few rows (at most 256) whose longest row has 65,537 to 262,144 positions
+// split each row over 4,096-position chunks (topk_sfilter_kernel: a sampled
+// bound, then the chunk's candidates in position order) and finish each row
+// in one workgroup (topk_sresolve_kernel).  Otherwise rows of at most 65,536
+// positions take one 1024-thread workgroup each (one streaming pass over the
+// row, the rest in LDS; see topk_rows_kernel).
 // Longer rows are split over workgroups, because a single CU streams too
 // slowly for them; only integer counts are combined across workgroups, so the
 // result does not depend on scheduling:
@@ -992,6 +996,322 @@ __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __
     }
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (a decode batch) longer than one workgroup streams quickly (the
+// longest above 65,536 positions, up to TM_MAXN).  Each row is split over
+// 4,096-position chunks:
+//   topk_sfilter_kernel   rows x chunks, 256 threads.  Every workgroup of a
+//       row draws the same sample of 2,048 scores (32 blocks of 64 consecutive
+//       positions spread evenly over the row) and finds the same bound
+//       theta_lo: the lower edge of the 12-bit key bin that holds the sample's
+//       rho-th largest key, rho = 1.3 x the rank the k-th largest element has
+//       in the sample, plus 8.  Rows of at most TM_MINSAMPLE_N positions use
+//       theta_lo = 0, i.e. every element.  The chunk's elements with key >=
+//       theta_lo go to the chunk's own slots, in position order (thread t
+//       holds positions 16 t .. 16 t + 15), with their count, their largest
+//       key and theta_lo; nothing crosses workgroups, so nothing needs
+//       clearing first.
+//   topk_sresolve_kernel  one 1024-thread workgroup per row.  If the
+//       candidates number at least k and fit in LDS, they hold the k-th largest key theta and every key above it, and
+//       the radix rounds of topk_resolve_kernel (over [theta_lo, largest
+//       candidate], early finish) give theta and need_eq.  The concatenated lists
+//       are in position order, so two block scans over them give the
+//       ascending output (theta-valued elements kept up to need_eq in
+//       position order).  Otherwise (a misleading sample, huge tie groups, NaN)
+//       three radix rounds and the ordered output run over the row itself,
+//       read from memory: slower, equally exact.
+// The sample only decides how fast a row goes, never what it selects.
+constexpr int TM_MAXN = 262144;
+constexpr int TM_MAXROWS = 256;
+constexpr int TM_THREADS = 256;
+constexpr int TM_SBLOCKS = 32;
+constexpr int TM_SBLOCK = 64;
+constexpr int TM_SAMPLES = TM_SBLOCKS * TM_SBLOCK;  // 8 per thread
+constexpr int TM_CCAP = TK_CHUNK;                   // candidate slots per chunk (never overflow)
+constexpr int TM_LCAP = 8192;                       // candidates the resolve holds in LDS
+constexpr int TM_MINSAMPLE_N = 8192;
+constexpr int TM_MAXCH = TM_MAXN / TK_CHUNK;        // 64 chunks
+static_assert(TM_SAMPLES == 8 * TM_THREADS, "two sample float4 per thread");
+static_assert(TK_CHUNK == TK_PER_THREAD * TM_THREADS, "one chunk per workgroup");
+static_assert(TM_MAXCH == 64, "the resolve scans chunk counts with one wave");
+constexpr int TM_RTHREADS = 1024;  // topk_sresolve_kernel
+
+// Per-chunk record written by topk_sfilter_kernel: candidate count, largest
+// candidate key, theta_lo.
+constexpr int TM_CREC = 4;
+
+__global__ __launch_bounds__(TM_THREADS) void topk_sfilter_kernel(const int32_t* __restrict__ vis,
+                                                                  const float* __restrict__ scores, int64_t ld, int k,
+                                                                  uint32_t* __restrict__ crec,
+                                                                  unsigned long long* __restrict__ mcand, int chunks,
+                                                                  int num_rows)
+{
+    const int r = grid_item();
+    if (r >= num_rows) return;
+    const int c = blockIdx.x;
+    const int n = vis[r];
+    const int start = c * TK_CHUNK;
+    if (n <= k || start >= n) return;  // the resolve reads counts of chunks below n only, and only when n > k
+    const int end = min(n, start + TK_CHUNK);
+    const float* row = scores + (int64_t)r * ld;
+    const int t = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
+    __shared__ uint32_t sh[TM_THREADS / 64];
+    __shared__ uint32_t s_bin, s_above;
+
+    // The chunk's keys and the sample go out together.
+    uint32_t key[TK_PER_THREAD], present;
+    load_chunk_keys(row, start, end, key, present);
+    uint32_t thlo = 0u;
+    if (n > TM_MINSAMPLE_N) {
+        uint32_t sk[8];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            // 4-aligned block start with the block inside the row: s0 + 63 < n.
+            const int blk = (t >> 4) + 16 * j;
+            const int s0 = (int)(((int64_t)(n - TM_SBLOCK) * blk / (TM_SBLOCKS - 1)) & ~3LL);
+            const float4 v = *reinterpret_cast<const float4*>(row + s0 + 4 * (t & 15));
+            sk[4 * j + 0] = score_key(v.x);
+            sk[4 * j + 1] = score_key(v.y);
+            sk[4 * j + 2] = score_key(v.z);
+            sk[4 * j + 3] = score_key(v.w);
+        }
+        const uint32_t rho = (uint32_t)min((int64_t)TM_SAMPLES,
+                                           (13LL * k * TM_SAMPLES + 10LL * n - 1) / (10LL * n) + 8);
+        for (int i = t; i < TK_BINS; i += TM_THREADS) h[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; e++) atomicAdd(&h[sk[e] >> 20], 1u);
+        __syncthreads();
+        find_threshold_bin<TM_THREADS, TK_BINS>(h, rho, &s_bin, &s_above, sh);
+        thlo = s_bin << 20;
+    }
+    uint32_t sel = 0u, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < TK_PER_THREAD; i++)
+        if (((present >> i) & 1u) && key[i] >= thlo) {
+            sel |= 1u << i;
+            kmax = max(kmax, key[i]);
+        }
+    // Exclusive scan of the counts and maximum of the keys, one barrier pair.
+    const int lane = t & 63, wave = t >> 6;
+    const uint32_t cnt = __popc(sel);
+    const uint32_t incl = wave_inclusive_scan(cnt);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    __shared__ uint32_t smax[TM_THREADS / 64];
+    if (lane == 63) sh[wave] = incl;
+    if (lane == 0) smax[wave] = kmax;
+    __syncthreads();
+    uint32_t before = 0, total = 0, cmax = 0;
+#pragma unroll
+    for (int w = 0; w < TM_THREADS / 64; w++) {
+        before += w < wave ? sh[w] : 0u;
+        total += sh[w];
+        cmax = max(cmax, smax[w]);
+    }
+    uint32_t slot = before + incl - cnt;
+    unsigned long long* cc = mcand + ((int64_t)r * chunks + c) * TM_CCAP;
+    const int t0 = start + TK_PER_THREAD * t;
+#pragma unroll
+    for (int i = 0; i < TK_PER_THREAD; i++)
+        if ((sel >> i) & 1u) {
+            if (slot < (uint32_t)TM_CCAP) cc[slot] = ((unsigned long long)key[i] << 32) | (uint32_t)(t0 + i);
+            slot++;
+        }
+    if (t == 0) {
+        uint32_t* rec = crec + ((int64_t)r * chunks + c) * TM_CREC;
+        rec[0] = total;
+        rec[1] = cmax;
+        rec[2] = thlo;
+    }
+}
+
+__global__ __launch_bounds__(TM_RTHREADS) void topk_sresolve_kernel(const int32_t* __restrict__ vis,
+                                                                   const float* __restrict__ scores, int64_t ld,
+                                                                   int k, int32_t* __restrict__ indices,
+                                                                   const uint32_t* __restrict__ crec,
+                                                                   const unsigned long long* __restrict__ mcand,
+                                                                   int chunks, int num_rows)
+{
+    const int r = grid_item();
+    if (r >= num_rows) return;
+    const int n = vis[r];
+    int32_t* out = indices + (int64_t)r * k;
+    const int t = threadIdx.x;
+    if (n <= k) {
+        for (int i = t; i < k; i += TM_RTHREADS) out[i] = i < n ? i : -1;
+        return;
+    }
+    __shared__ unsigned long long cl[TM_LCAP];
+    __shared__ __attribute__((aligned(16))) uint32_t h[TK_BINS];
+    __shared__ uint32_t coff[TM_MAXCH + 1];
+    __shared__ uint32_t sh[TM_RTHREADS / 64];
+    __shared__ uint32_t s_bin, s_above, s_cnt, s_total, s_over, s_max, s_thlo;
+    __shared__ __attribute__((aligned(16))) uint32_t few[TR_FEW];
+    __shared__ uint32_t s_nfew, s_theta, s_needeq, s_eqtot;
+    const int nch = (n + TK_CHUNK - 1) / TK_CHUNK;  // <= TM_MAXCH
+
+    // Chunk records -> offsets of each chunk's list in the concatenation,
+    // the largest candidate key, theta_lo.
+    if (t < 64) {
+        uint4 rec = make_uint4(0u, 0u, 0u, 0u);
+        if (t < nch) rec = *reinterpret_cast<const uint4*>(crec + ((int64_t)r * chunks + t) * TM_CREC);
+        const uint32_t cnt = rec.x;
+        const uint32_t incl = wave_inclusive_scan(cnt);
+        coff[t] = incl - cnt;
+        const bool over = __ballot(cnt > (uint32_t)TM_CCAP) != 0ull;
+        uint32_t mx = rec.y;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+        if (t == 0) s_thlo = rec.z;
+        if (t == 63) {
+            coff[64] = incl;
+            s_total = incl;
+            s_over = over ? 1u : 0u;
+            s_max = mx;
+        }
+    }
+    if (t == 0) s_nfew = 0u;
+    __syncthreads();
+    const uint32_t m = s_total;
+    const bool fast = !s_over && m >= (uint32_t)k && m <= (uint32_t)TM_LCAP;
+
+    uint32_t theta, need_eq, eq_total = 0;
+    bool keep_all_ties = false;
+    if (fast) {
+        // Each wave copies whole chunk lists (64 lanes per pass).
+        for (int ch = t >> 6; ch < nch; ch += TM_RTHREADS / 64) {
+            const uint32_t o = coff[ch], cnt = coff[ch + 1] - o;
+            const unsigned long long* src = mcand + ((int64_t)r * chunks + ch) * TM_CCAP;
+            for (uint32_t j = t & 63; j < cnt; j += 64) cl[o + j] = src[j];
+        }
+        __syncthreads();
+        // Radix rounds over [theta_lo, largest candidate]: every candidate's
+        // key lies there (and m >= k >= 1 makes the maximum a real key).
+        uint32_t lo = s_thlo, hi = s_max, nd = (uint32_t)k;
+        for (;;) {
+            const uint32_t span = hi - lo;
+            const int shift = span < (uint32_t)TK_BINS ? 0 : (32 - __clz(span)) - 12;
+            for (int i = t; i < TK_BINS; i += TM_RTHREADS) h[i] = 0u;
+            __syncthreads();
+            for (uint32_t i = t; i < m; i += TM_RTHREADS) {
+                const uint32_t key = (uint32_t)(cl[i] >> 32);
+                if (key >= lo && key <= hi) atomicAdd(&h[(key - lo) >> shift], 1u);
+            }
+            __syncthreads();
+            find_threshold_bin<TM_RTHREADS, TK_BINS>(h, nd, &s_bin, &s_above, sh, &s_cnt);
+            nd -= s_above;
+            lo += s_bin << shift;
+            hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << shift) - 1));
+            if (shift == 0) {  // wave-uniform: every thread holds the same lo, hi
+                eq_total = s_cnt;
+                break;
+            }
+            if (s_cnt <= (uint32_t)TR_FEW) {
+                for (uint32_t i = t; i < m; i += TM_RTHREADS) {
+                    const uint32_t key = (uint32_t)(cl[i] >> 32);
+                    if (key >= lo && key <= hi) few[atomicAdd(&s_nfew, 1u)] = key;
+                }
+                __syncthreads();
+                if (t < 64) rank_few(few, s_cnt, nd, &s_theta, &s_needeq, &s_eqtot);
+                __syncthreads();
+                lo = s_theta;
+                nd = s_needeq;
+                eq_total = s_eqtot;
+                break;
+            }
+        }
+        theta = lo;
+        need_eq = nd;
+        keep_all_ties = need_eq == eq_total;
+
+        // Ordered output: thread t owns candidates [t per, (t + 1) per) of the
+        // position-ordered list.
+        const uint32_t per = (m + TM_RTHREADS - 1) / TM_RTHREADS;
+        const uint32_t i0 = min(m, t * per), i1 = min(m, i0 + per);
+        uint32_t tot, eq_rank = 0;
+        if (!keep_all_ties) {
+            uint32_t neq = 0;
+            for (uint32_t i = i0; i < i1; i++) neq += (uint32_t)(cl[i] >> 32) == theta;
+            eq_rank = block_exclusive_scan<TM_RTHREADS>(neq, &tot, sh);
+        }
+        uint32_t nk = 0, er = eq_rank;
+        for (uint32_t i = i0; i < i1; i++) {
+            const uint32_t key = (uint32_t)(cl[i] >> 32);
+            if (key > theta) nk++;
+            else if (key == theta) nk += (keep_all_ties || er++ < need_eq) ? 1u : 0u;
+        }
+        uint32_t pos = block_exclusive_scan<TM_RTHREADS>(nk, &tot, sh);
+        er = eq_rank;
+        for (uint32_t i = i0; i < i1; i++) {
+            const uint32_t key = (uint32_t)(cl[i] >> 32);
+            bool keep = key > theta;
+            if (key == theta) keep = keep_all_ties || er++ < need_eq;
+            if (keep) {
+                if (pos < (uint32_t)k) out[pos] = (int32_t)(uint32_t)cl[i];
+                pos++;
+            }
+        }
+        return;
+    }
+
+    // Exact path over the row itself (a misleading sample, ties or NaN
+    // filling the chunk slots).  Three radix rounds on absolute key bits.
+    const float* row = scores + (int64_t)r * ld;
+    for (int i = t; i < TK_BINS; i += TM_RTHREADS) h[i] = 0u;
+    __syncthreads();
+    for (int p = t; p < n; p += TM_RTHREADS) atomicAdd(&h[score_key(row[p]) >> 20], 1u);
+    __syncthreads();
+    find_threshold_bin<TM_RTHREADS, TK_BINS>(h, (uint32_t)k, &s_bin, &s_above, sh);
+    const uint32_t b0 = s_bin;
+    const uint32_t need = (uint32_t)k - s_above;
+    for (int i = t; i < TK_BINS; i += TM_RTHREADS) h[i] = 0u;
+    __syncthreads();
+    for (int p = t; p < n; p += TM_RTHREADS) {
+        const uint32_t key = score_key(row[p]);
+        if ((key >> 20) == b0) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<TM_RTHREADS, TK_BINS>(h, need, &s_bin, &s_above, sh);
+    const uint32_t pre20 = (b0 << 12) | s_bin;
+    const uint32_t need2 = need - s_above;
+    for (int i = t; i < 1024; i += TM_RTHREADS) h[i] = 0u;
+    __syncthreads();
+    for (int p = t; p < n; p += TM_RTHREADS) {
+        const uint32_t key = score_key(row[p]);
+        if ((key >> 8) == pre20) atomicAdd(&h[key & 0xffu], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<TM_RTHREADS, 1024>(h, need2, &s_bin, &s_above, sh);
+    theta = (pre20 << 8) | s_bin;
+    need_eq = need2 - s_above;
+    // Thread t owns positions [t per, (t + 1) per): ties ranked in position
+    // order, then the kept positions written in order.
+    const int per = (n + TM_RTHREADS - 1) / TM_RTHREADS;
+    const int p0 = min(n, t * per), p1 = min(n, p0 + per);
+    uint32_t tot, neq = 0;
+    for (int p = p0; p < p1; p++) neq += score_key(row[p]) == theta;
+    const uint32_t eq_rank = block_exclusive_scan<TM_RTHREADS>(neq, &tot, sh);
+    uint32_t nk = 0, er = eq_rank;
+    for (int p = p0; p < p1; p++) {
+        const uint32_t key = score_key(row[p]);
+        if (key > theta) nk++;
+        else if (key == theta) nk += er++ < need_eq ? 1u : 0u;
+    }
+    uint32_t pos = block_exclusive_scan<TM_RTHREADS>(nk, &tot, sh);
+    er = eq_rank;
+    for (int p = p0; p < p1; p++) {
+        const uint32_t key = score_key(row[p]);
+        bool keep = key > theta;
+        if (key == theta) keep = er++ < need_eq;
+        if (keep) {
+            if (pos < (uint32_t)k) out[pos] = p;
+            pos++;
+        }
+    }
+}
+
 // Calls whose rows all have at most TS_MAXN positions (a prefill chunk of up
 // to 8,192 tokens, short decode rows): 256 threads per row and the row's keys
 // held in registers, 32 per thread.  The radix rounds histogram those
@@ -1168,8 +1488,20 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
 
 }  // namespace
 
+// Calls that take the chunked path for few rows (topk_sfilter_kernel).
+static bool topk_chunked_path(int32_t num_rows, int32_t max_visible)
+{
+    return num_rows <= TM_MAXROWS && max_visible > TR_ROW_PATH_MAXN && max_visible <= TM_MAXN;
+}
+
 size_t topk_workspace_bytes(int32_t num_rows, int32_t max_visible)
 {
+    if (topk_chunked_path(num_rows, max_visible)) {
+        // per-chunk candidate counts and slots
+        const size_t R = (size_t)num_rows;
+        const size_t CH = (size_t)((max_visible + TK_CHUNK - 1) / TK_CHUNK);
+        return align_up(R * CH * TM_CREC * 4, 256) + align_up(R * CH * TM_CCAP * 8, 256);
+    }
     if (max_visible <= TR_ROW_PATH_MAXN) return 0;  // the one-workgroup-per-row path needs none
     const size_t R = (size_t)num_rows;
     const size_t CH = (size_t)((max_visible + TK_CHUNK - 1) / TK_CHUNK);
@@ -1187,7 +1519,14 @@ TopkWorkspace topk_workspace_carve(void* ws, int32_t num_rows, int32_t max_visib
     const size_t R = (size_t)num_rows;
     const int32_t CH = (max_visible + TK_CHUNK - 1) / TK_CHUNK;
     char* p = (char*)ws;
-    TopkWorkspace tw;
+    TopkWorkspace tw{};
+    if (topk_chunked_path(num_rows, max_visible)) {
+        tw.crec = (uint32_t*)p;
+        p += align_up(R * CH * TM_CREC * 4, 256);
+        tw.mcand = (unsigned long long*)p;
+        tw.chunks = CH;
+        return tw;
+    }
     tw.rowst = (uint32_t*)p;
     p += align_up(R * TK_ROWST * 4, 256);
     tw.chunkst = (uint32_t*)p;
@@ -1212,6 +1551,13 @@ void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, cons
     if (max_visible <= TS_MAXN) {
         hipLaunchKernelGGL(topk_short_kernel, item_grid(1, num_rows), dim3(TS_THREADS), 0, stream, vis, scores, ld, k,
                            indices, (int)num_rows);
+        return;
+    }
+    if (topk_chunked_path(num_rows, max_visible)) {
+        hipLaunchKernelGGL(topk_sfilter_kernel, item_grid(tw.chunks, num_rows), dim3(TM_THREADS), 0, stream, vis,
+                           scores, ld, k, tw.crec, tw.mcand, tw.chunks, (int)num_rows);
+        hipLaunchKernelGGL(topk_sresolve_kernel, item_grid(1, num_rows), dim3(TM_RTHREADS), 0, stream, vis, scores, ld,
+                           k, indices, tw.crec, tw.mcand, tw.chunks, (int)num_rows);
         return;
     }
     const bool has_long = max_visible > TR_ROW_PATH_MAXN;

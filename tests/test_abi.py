@@ -53,9 +53,12 @@ def test_workspace_sizes(lib):
     assert m.dsa_topk_workspace_size(0, 10, 2048) == 0
     assert m.dsa_sparse_mla_workspace_size(1, 0) == 0
     assert m.dsa_decode_step_workspace_size(1, 1, 2049) == 0
-    # rows up to 65,536 positions need no top-k workspace; longer rows do
+    # rows of up to 65,536 positions (one workgroup per row) need no top-k
+    # workspace; few rows of up to 262,144 positions hold a 16-byte record and
+    # 4,096 candidate slots per 4,096-position chunk
+    assert m.dsa_topk_workspace_size(300, 32768, 2048) == 0
     assert m.dsa_topk_workspace_size(64, 32768, 2048) == 0
-    assert m.dsa_topk_workspace_size(16, 202752, 2048) > 0
+    assert m.dsa_topk_workspace_size(16, 202752, 2048) == 16 * 50 * 16 + 16 * 50 * 4096 * 8
     a = m.dsa_topk_workspace_size(16, 300000, 2048)
     b = m.dsa_topk_workspace_size(32, 300000, 2048)
     assert 0 < a < b and a % 256 == 0
@@ -368,15 +371,15 @@ def test_decode_step_workspace_follows_the_chunk_formula(lib):
         if R * ld * 4 <= budget:
             C = R
         else:
-            C = max(32, budget // (ld * 4) // 32 * 32)
-            C = min(C, R)
+            fit = budget // (ld * 4)
+            C = min(R, max(32, fit // 256 * 256 if fit >= 256 else fit // 32 * 32))
         return (a256(C * ld * 4) + a256(4 * C) + 256 + a256(m.dsa_topk_workspace_size(C, maxv, k))
                 + a256(m.dsa_sparse_mla_workspace_size(R, k)))
 
     for R, maxv in [(64, 32768), (16, 202752), (16512, 131072), (8192, 8192), (1, 4096), (3, 1 << 24),
                     (40, 1 << 24), (70000, 9000), (2049, 131072)]:
         assert m.dsa_decode_step_workspace_size(R, maxv, 2048) == formula(R, maxv, 2048), (R, maxv)
-    # the ragged batch (16,512 rows up to 131,072 positions) holds 2,048 rows of scores at a time
+    # the ragged batch (16,512 rows up to 131,072 positions) scores 2,048 rows at a time
     assert m.dsa_decode_step_workspace_size(16512, 131072, 2048) < 1.2 * budget
     # the paged step adds the translated index lists and zero row bases
     R, k = 100, 2048

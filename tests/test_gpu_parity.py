@@ -293,15 +293,15 @@ def test_topk_bitexact_rows_beyond_one_workgroup(dsa, oracle_mod, kind):
 
 
 def test_topk_bitexact_many_rows_few_long(dsa, oracle_mod):
-    """More than 64 rows, a few of them longer than 65,536 positions: the
+    """More than 256 rows, a few of them longer than 65,536 positions: the
     long rows are listed on the device and walked by fixed grids (the short
     ones stay with the one-workgroup-per-row kernel).  Long rows sit at the
     start, middle and end of the batch, and include ties and all-equal rows."""
     g = np.random.default_rng(77)
-    R = 150
+    R = 300
     lens = g.integers(1, 65537, size=R).astype(np.int32)
     lens[:4] = [2048, 1, 2049, 65536]
-    long_at = [0, 5, 6, 71, 72, 100, 149]
+    long_at = [0, 5, 6, 71, 72, 100, 299]
     lens[long_at] = [65537, 150000, 99999, 70000, 131072, 66000, 120001]
     kinds = {5: "ties", 72: "zeros", 100: "coarse"}
     n = int(lens.max())
@@ -310,6 +310,29 @@ def test_topk_bitexact_many_rows_few_long(dsa, oracle_mod):
         s[r] = wl.random_scores(40 + r, 1, n, kind=kd)[0]
     got = run_topk(dsa, lens, s, 2048)
     ref = oracle_mod.topk(lens, s, 2048)
+    bad = [r for r in range(R) if not np.array_equal(got[r], ref[r])]
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("k", [2048, 1, 300])
+def test_topk_bitexact_chunked_path_for_few_rows(dsa, oracle_mod, k):
+    """Calls with at most 256 rows whose longest row has 65,537..262,144
+    positions split each row over 4,096-position chunks: a sampled bound per
+    row, candidates per chunk in position order, one workgroup finishing each
+    row.  Rows at and around the chunk and length limits; a row whose top sits
+    in one chunk; 8-valued ties and all-equal rows (more candidates than the
+    finishing workgroup holds: exact whole-row path); a row mostly NaN;
+    normal rows."""
+    lens = np.array([262144, 8193, 12288, 12289, 40000, 65536, 100000, 262143, 30000, 30000, 2048, 9000],
+                    np.int32)
+    R, n = len(lens), int(lens.max())
+    kinds = ["normal", "normal", "ties", "normal", "zeros", "coarse", "normal", "tiny", "normal", "normal",
+             "normal", "signed_zeros"]
+    s = np.concatenate([wl.random_scores(90 + i, 1, n, kind=kd) for i, kd in enumerate(kinds)])
+    s[8, 8192:12288] += 20.0  # the top of this row lies in one chunk
+    s[9, 100:29000] = np.nan
+    got = run_topk(dsa, lens, s, k)
+    ref = oracle_mod.topk(lens, s, k)
     bad = [r for r in range(R) if not np.array_equal(got[r], ref[r])]
     assert not bad, bad
 
