@@ -841,8 +841,12 @@ def test_cache_write_feeds_the_path(dsa, oracle_mod):
     lb = wl.f32_to_bf16_bits(lat.astype(np.float32))
     s64, _, idx_ref, _, _ = oracle_mod.decode_step(x["visible_len"], x["row_cache_base"], x["q_idx"], x["w"], kb,
                                                    x["q_abs"], lb, 2048, 1.0, wl.SOFTMAX_SCALE)
-    assert recall_check(idx, idx_ref, s64, x["visible_len"]) >= 0.99
-    ref_out, ref_lse = oracle_mod.sparse_mla(x["row_cache_base"], x["q_abs"], lc, idx, wl.SOFTMAX_SCALE)
+    # The caches differ from bf16(oracle rows) in at most 0.5% of elements, by
+    # one bf16 unit (test_cache_write_against_oracle); the scores move far
+    # less than the gap band, so the usual recall rule applies, and the
+    # oracle's attention runs on its own rows.
+    assert recall_check(idx, idx_ref, s64, x["visible_len"]) >= 0.999
+    ref_out, ref_lse = oracle_mod.sparse_mla(x["row_cache_base"], x["q_abs"], lb, idx, wl.SOFTMAX_SCALE)
     check_attention(out, lse, ref_out, ref_lse, "written caches")
 
 
@@ -960,7 +964,8 @@ def test_cache_writer_fills_paged_pools_for_the_paged_step(dsa, oracle_mod):
     new tokens into block-scattered pools (slots = pool rows from the block
     table), then dsa_decode_step_paged runs over those pools.  It must equal,
     bit for bit, the packed step over packed caches written by the same
-    writer, and agree with the oracle on the depaged pools."""
+    writer, and agree with the oracle's attention over the oracle's own cache
+    rows."""
     B = 64
     lens = np.array([3000, 2048, 777], np.int64)
     S = len(lens)
@@ -1005,11 +1010,13 @@ def test_cache_writer_fills_paged_pools_for_the_paged_step(dsa, oracle_mod):
     assert np.array_equal(idx_a, idx_b.cpu().numpy())
     assert np.array_equal(out_a.view(np.uint32), out_b.cpu().numpy().view(np.uint32))
     assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
-    for i in range(S):
-        L = int(lens[i])
-        assert np.array_equal(oracle_mod.depage(lpool, bt[i], L, B), lc_packed[seq_base[i]:seq_base[i] + L])
-        assert np.array_equal(oracle_mod.depage(kpool, bt[i], L, B), kc_packed[seq_base[i]:seq_base[i] + L])
-    ref_out, ref_lse = oracle_mod.sparse_mla(seq_base, q["q_abs"], lc_packed, idx_a, wl.SOFTMAX_SCALE)
+    # every token's rows sit at its block-table slot of the pools
+    assert np.array_equal(lpool[pool_rows], lc_packed) and np.array_equal(kpool[pool_rows], kc_packed)
+    # the oracle attends over its own cache rows (bf16-rounded) on the GPU's lists
+    _, lat = oracle_mod.cache_rows(c["hidden"], c["wk"], c["k_norm_weight"], c["k_norm_bias"], 1e-6, c["kv_a"],
+                                   c["kv_norm_weight"], 1e-5, pos.astype(np.int64), 1e6)
+    lb = wl.f32_to_bf16_bits(lat.astype(np.float32))
+    ref_out, ref_lse = oracle_mod.sparse_mla(seq_base, q["q_abs"], lb, idx_a, wl.SOFTMAX_SCALE)
     check_attention(out_b.cpu().numpy(), lse_b.cpu().numpy(), ref_out, ref_lse, "written paged pools")
 
 
