@@ -581,7 +581,7 @@ def test_prefill_rows_up_to_k_equal_dense(dsa, oracle_mod):
 @pytest.mark.parametrize("R", [64, 100, 128, 16])
 def test_decode_step_attention_matches_standalone_call(dsa, R):
     """The attention inside dsa_decode_step equals dsa_sparse_mla_attn on the
-    same index lists bit for bit, for 4, 3, 2 and 16 splits per row, also when
+    same index lists bit for bit, for 4, 3, 2 and 8 splits per row, also when
     the workspace starts out full of garbage and is reused by a second call
     (the split partials and their merge leave nothing behind)."""
     w, x = inputs("c3")
