@@ -1045,6 +1045,76 @@ def test_paged_decode_step_full_size_equals_packed(dsa):
     assert np.array_equal(lse_a.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
 
 
+def test_decode_step_chunk_boundaries_packed_and_paged(dsa, oracle_mod):
+    """A host bound max_visible far above the rows' lengths (1,000,000) makes
+    each fp32 score row 4 MB, so the fused step takes 256 rows at a time: 300
+    rows split into chunks of 256 and 44.  Rows 0..255 are a prefill chunk on
+    one sequence (shared 32-row blocks), rows 256..299 decode rows on their own
+    sequences.  The packed and the paged step equal, bit for bit, the separate
+    calls over all rows at once, and sampled rows on both sides of the chunk
+    boundary agree with the oracle."""
+    T0 = 4000
+    dec = [2500, 1, 2049, 4097, 3333, 100, 2048, 5000] * 5 + [777, 3000, 4100, 1500]
+    vis = np.concatenate([np.arange(T0 - 255, T0 + 1), dec]).astype(np.int32)
+    seq_len = np.array([T0] + dec, np.int64)
+    seq_base = np.concatenate([[0], np.cumsum(seq_len)[:-1]]).astype(np.int64)
+    base = np.concatenate([np.zeros(256), seq_base[1:]]).astype(np.int64)
+    row_seq = np.concatenate([np.zeros(256), np.arange(1, len(dec) + 1)]).astype(np.int64)
+    w = wl.Workload(name="chunks", seed=29, visible_len=vis, row_cache_base=base, seq_len=seq_len,
+                    seq_base=seq_base, row_seq=row_seq)
+    x = w.generate()
+    d = device_inputs(x)
+    R, k, maxv = len(vis), 2048, 1_000_000
+    rows = dsa.Rows(dev(vis), dev(base), maxv)
+    ws_bytes = dsa.dsa_decode_step_workspace_size(R, maxv, k)
+    assert 256 * 4 * maxv <= ws_bytes < 300 * 4 * maxv  # 256 score rows at a time
+    idx = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+    ws = dsa.workspace(ws_bytes, DEV)
+    ws.fill_(255)
+    dsa.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], wl.INDEX_SCALE, d["q_abs"], d["kv_latent"],
+                        wl.SOFTMAX_SCALE, k, idx, out, lse, ws)
+    # separate calls, all rows at once
+    scores = torch.empty((R, maxv), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_scores(rows, d["q_idx"], d["w"], d["k_idx"], wl.INDEX_SCALE, scores)
+    idx_b = torch.empty_like(idx)
+    dsa.dsa_topk_select(rows, scores, k, idx_b, dsa.workspace(dsa.dsa_topk_workspace_size(R, maxv, k), DEV))
+    out_b, lse_b = torch.empty_like(out), torch.empty_like(lse)
+    dsa.dsa_sparse_mla_attn(rows, d["q_abs"], d["kv_latent"], idx_b, k, wl.SOFTMAX_SCALE, out_b, lse_b,
+                            dsa.workspace(dsa.dsa_sparse_mla_workspace_size(R, k), DEV))
+    torch.cuda.synchronize()
+    del scores
+    assert torch.equal(idx, idx_b)
+    assert torch.equal(out.view(torch.int32), out_b.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse_b.view(torch.int32))
+    # the paged step over 64-position blocks
+    B = 64
+    kpool, lpool, bt, seq_of_row = page_caches(x, seq_base, seq_len, B, seed=29)
+    bt_wide = np.zeros((bt.shape[0], (maxv + B - 1) // B), np.int32)
+    bt_wide[:, :bt.shape[1]] = bt
+    prow = dsa.Rows(dev(vis), dev(seq_of_row), maxv)
+    idx_p = torch.empty_like(idx)
+    out_p, lse_p = torch.empty_like(out), torch.empty_like(lse)
+    dsa.dsa_decode_step_paged(prow, dsa.Paged(dev(bt_wide), B), d["q_idx"], d["w"], dev_bf16(kpool), wl.INDEX_SCALE,
+                              d["q_abs"], dev_bf16(lpool), wl.SOFTMAX_SCALE, k, idx_p, out_p, lse_p,
+                              dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, maxv, k), DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_p)
+    assert torch.equal(out.view(torch.int32), out_p.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse_p.view(torch.int32))
+    # oracle on rows around the boundary
+    pick = [0, 254, 255, 256, 257, 259, 299]
+    y = sub(x, pick)
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(y["visible_len"], y["row_cache_base"], y["q_idx"], y["w"],
+                                                   y["k_idx"], y["q_abs"], y["kv_latent"], k, 1.0, wl.SOFTMAX_SCALE)
+    idx_h = idx.cpu().numpy()
+    assert recall_check(idx_h[pick], idx_ref, s64, y["visible_len"]) >= 0.999
+    ref_out, ref_lse = oracle_mod.sparse_mla(y["row_cache_base"], y["q_abs"], y["kv_latent"], idx_h[pick],
+                                             wl.SOFTMAX_SCALE)
+    check_attention(out[pick].cpu().numpy(), lse[pick].cpu().numpy(), ref_out, ref_lse, "chunk boundary")
+
+
 # ----------------------------------------------------------------------------- IndexShare
 
 def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):
