@@ -19,7 +19,9 @@ prices the whole step the same way: algorithmic bytes of the path per step
 
 The default run (the batched-decode workload) also measures the 8,192-token
 causal prefill (`prefill_c2`): the step, the indexer and the attention, each
-timed alone with HIP events, in FLOPs against the bf16 matrix-core peak.
+timed alone with HIP events, in FLOPs against the bf16 matrix-core peak; and
+the long-context decode step, 16 sequences x 202,752 positions
+(`long_decode_c4`), in algorithmic bytes against the HBM peak.
 
 Workloads whose rows share a sequence (a prefill chunk) read each key once per
 32-row block and are matrix-core work: there the indexer (8,192 FLOP per row
@@ -57,6 +59,8 @@ def parse():
     p.add_argument("--config", default="c3", help="workload: c1 | c2 | c3 | c4 | c5")
     p.add_argument("--no-prefill", dest="prefill", action="store_false",
                    help="skip the 8,192-token prefill measurement that accompanies a decode workload")
+    p.add_argument("--no-long", dest="long", action="store_false",
+                   help="skip the long-context decode step (16 x 202,752) that accompanies the default workload")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU baseline budget (oracle)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-paged", dest="paged", action="store_false",
@@ -202,6 +206,53 @@ def measure_prefill(dsa, wl, torch, dev, stream, steps, warmup, name="c2"):
         f"({res['indexer']['mfma_frac']:.3f} of bf16 peak), attention {ms_attn * 1e3:.1f} us "
         f"({res['attention']['mfma_frac']:.3f})")
     del q_idx, wts, k_idx, q_abs, kv, idx, out, lse, ws, scores, ws_at
+    return res
+
+
+def measure_long_decode(dsa, wl, torch, dev, stream, steps, warmup, name="c4"):
+    """The whole decode step of the long-context workload, timed over `steps`
+    back-to-back launches (HIP events on the launch stream), in algorithmic
+    bytes against the HBM peak."""
+    w = wl.config(name)
+    log(f"[bench] generating {w.name}: {w.num_rows} rows, {w.cache_rows} cache rows")
+    x = w.generate()
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R, maxv = w.num_rows, w.max_visible
+    q_idx, wts, k_idx = bf(x["q_idx"]), torch.from_numpy(x["w"]).to(dev), bf(x["k_idx"])
+    q_abs, kv = bf(x["q_abs"]), bf(x["kv_latent"])
+    del x
+    rows = dsa.Rows(torch.from_numpy(w.visible_len).to(dev), torch.from_numpy(w.row_cache_base).to(dev), maxv,
+                    flags=dsa.ROWS_DISTINCT_SEQUENCES)
+    idx = torch.empty((R, K_TOP), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=dev)
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, maxv, K_TOP), dev)
+
+    def step():
+        dsa.dsa_decode_step(rows, q_idx, wts, k_idx, wl.INDEX_SCALE, q_abs, kv, wl.SOFTMAX_SCALE, K_TOP, idx, out, lse,
+                            ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n = w.visible_len.astype(np.int64)
+    nbytes = int(np.sum(256 * n + 1152 * np.minimum(n, K_TOP) + 82048 + 139264))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": workload_label(w), "rows": R, "us_per_step": round(ms * 1e3, 2),
+           "tokens_per_s": round(R / (ms * 1e-3), 1), "step_alg_bytes": nbytes, "achieved_gbs": round(gbs, 1),
+           "step_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"[bench] {w.name} decode: {ms * 1e3:.1f} us/step, {res['step_hbm_frac']:.3f} of HBM peak")
+    del q_idx, wts, k_idx, q_abs, kv, idx, out, lse, ws
     return res
 
 
@@ -510,6 +561,11 @@ def main():
     prefill_c2 = None
     if args.prefill and prefill is None:
         prefill_c2 = measure_prefill(dsa, wl, torch, dev, stream, args.steps, args.warmup)
+    # The long-context decode batch beside the default workload (HBM bound;
+    # timed alone, its inputs freed afterwards).
+    long_c4 = None
+    if args.long and w.name == "c3":
+        long_c4 = measure_long_decode(dsa, wl, torch, dev, stream, args.steps, args.warmup)
     traffic = traffic_from_profiles("indexer", w.name, src_hash(["indexer.hip", "dsa_device.h"]))
 
     cpu = None
@@ -554,6 +610,7 @@ def main():
         "decode_kernels": decode_kernels,
         "prefill": prefill,
         "prefill_c2": prefill_c2,
+        "long_decode_c4": long_c4,
         "cold": cold,
         "step_alg_bytes": step_bytes if prefill is None else None,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if prefill is None else None,
