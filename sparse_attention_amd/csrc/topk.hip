@@ -13,9 +13,11 @@
 // few rows (at most 256) whose longest row has 65,537 to 262,144 positions
 // split each row over 4,096-position chunks (topk_sfilter_kernel: a sampled
 // bound, then the chunk's candidates in position order) and finish each row
-// in one workgroup (topk_sresolve_kernel).  Otherwise rows of at most 65,536
-// positions take one 1024-thread workgroup each (one streaming pass over the
-// row, the rest in LDS; see topk_rows_kernel).
+// in one workgroup (topk_sresolve_kernel).  Calls of at least 1,024 rows give
+// their rows of at most 65,536 positions one 256-thread workgroup each, four
+// to a CU (topk_stream_kernel).  Otherwise rows of at most 65,536 positions
+// take one 1024-thread workgroup each (one streaming pass over the row, the
+// rest in LDS; see topk_rows_kernel).
 // Longer rows are split over workgroups, because a single CU streams too
 // slowly for them; only integer counts are combined across workgroups, so the
 // result does not depend on scheduling:
@@ -658,12 +660,14 @@ __device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz(x) : 0
 __global__ __launch_bounds__(TR_THREADS) void topk_rows_kernel(const int32_t* __restrict__ vis,
                                                                const float* __restrict__ scores, int64_t ld,
                                                                int k, int32_t* __restrict__ indices, int max_n,
-                                                               uint32_t* __restrict__ long_rowst, int num_rows)
+                                                               uint32_t* __restrict__ long_rowst, int num_rows,
+                                                               int sample_only)
 {
     static_assert(TR_THREADS == TP_THREADS, "the sampling step runs on this workgroup");
     const int r = grid_item();
     if (r >= num_rows) return;
     const int n = vis[r];
+    if (sample_only && n <= max_n) return;  // topk_stream_kernel owns this row
     int32_t* out = indices + (int64_t)r * k;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1486,6 +1490,397 @@ __global__ __launch_bounds__(TS_THREADS) void topk_short_kernel(const int32_t* _
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Many rows of up to 65,536 positions (the rows of a prefill chunk): one
+// 256-thread workgroup per row with ~40 KB of LDS, so four rows share a CU
+// and the barrier-bound selection of one row overlaps the others' streaming
+// (the 1024-thread kernel holds a CU for each row in turn).  The row is read
+// from memory once, as it streams past a bound:
+//   1. Bound: 4,096 sampled scores (64 blocks of 64 consecutive positions
+//      spread evenly over the row).  Two 11-bit radix rounds over their keys
+//      give the 22-bit prefix of the rho-th largest sample key, rho = E +
+//      4 sqrt(E) + 16 with E = k 4096 / n the rank the k-th largest element
+//      has in the sample on average; its lower edge is the bound theta_lo.
+//      Rows of at most TQ_ALL positions take every element instead.
+//   2. Stream: wave w owns the w-th quarter of the row (a multiple of 256
+//      positions) and appends the elements whose key is >= theta_lo (a float
+//      compare against the bound's float, as in topk_rows_kernel) to its own
+//      ordered list: one wave prefix sum per 256 positions, slots in 64-slot
+//      chunks of a pool the four waves share (a wave takes chunks as it
+//      needs them, so rows whose large scores cluster in one quarter fit as
+//      well as any other).  Key and 16-bit position per slot.
+//   3. Select: if the lists hold at least k elements and the pool did not run
+//      out, they hold the k-th largest key theta and every larger key, and
+//      radix rounds over [theta_lo, largest candidate] (10 bits a round,
+//      early finish with rank_few) give theta and need_eq.
+//   4. Output: the four lists in wave order are in position order.  Each
+//      thread takes a contiguous run of entries; one packed block scan gives
+//      its output offset and the count of theta-valued entries before it, and
+//      the first need_eq of those are kept.
+// When the sampled bound fails (fewer than k candidates, or more than the
+// pool holds), a histogram of the whole row's top 10 key bits gives the bin
+// of the k-th largest; if that bin and everything above it fit the pool, the
+// row streams once more past that exact bound and steps 3-4 run as above.
+// Otherwise (huge tie groups, all-equal rows) four radix rounds and an
+// ordered pass run over the row itself.  Exact for any input.
+constexpr int TQ_THREADS = 256;
+constexpr int TQ_WAVES = TQ_THREADS / 64;
+constexpr int TQ_CHUNKS = 83;               // pool: 83 chunks of 64 slots
+constexpr int TQ_CAP = TQ_CHUNKS * 64;      // 5,312 slots: 4 B key + 2 B position each
+constexpr int TQ_FIT = TQ_CAP - TQ_WAVES * 63;  // candidates that always fit (each wave's last chunk partly empty)
+constexpr int TQ_BINS = 1024;               // 10-bit digit
+constexpr int TQ_SBLOCKS = 64;
+constexpr int TQ_SBLOCK = 64;
+constexpr int TQ_SAMPLES = TQ_SBLOCKS * TQ_SBLOCK;  // 16 per thread
+constexpr int TQ_MAXN = 65536;              // positions fit the 16-bit slots
+constexpr int TQ_ALL = 4096;                // rows of at most this take every element
+constexpr int TQ_MIN_ROWS = 1024;           // calls with at least this many rows take the kernel
+constexpr int TQ_PF = 4;                    // stream steps in flight per wave
+static_assert(TQ_SAMPLES == 16 * TQ_THREADS, "four sample float4 per thread");
+static_assert(TQ_ALL <= TQ_FIT, "a short row fits the pool whole");
+
+__global__ __launch_bounds__(TQ_THREADS) void topk_stream_kernel(const int32_t* __restrict__ vis,
+                                                                 const float* __restrict__ scores, int64_t ld,
+                                                                 int k, int32_t* __restrict__ indices,
+                                                                 int num_rows)
+{
+    const int r = grid_item();
+    if (r >= num_rows) return;
+    const int n = vis[r];
+    if (n > TQ_MAXN) return;  // the multi-workgroup path owns this row
+    int32_t* out = indices + (int64_t)r * k;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (n <= k) {
+        for (int t = tid; t < k; t += TQ_THREADS) out[t] = t < n ? t : -1;
+        return;
+    }
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2][TQ_BINS];  // radix rounds, alternating
+    __shared__ uint32_t pkey[TQ_CAP];
+    __shared__ uint16_t ppos[TQ_CAP];
+    __shared__ uint8_t wch[TQ_WAVES][TQ_CHUNKS];  // each wave's chunks, in order
+    __shared__ uint32_t sh[TQ_WAVES];
+    __shared__ uint32_t wcnt[TQ_WAVES], wmax[TQ_WAVES];
+    __shared__ uint32_t s_bin, s_above, s_cnt, s_next;
+    __shared__ __attribute__((aligned(16))) uint32_t few[TR_FEW];
+    __shared__ uint32_t s_nfew, s_theta, s_needeq, s_eqtot;
+    const float* row = scores + (int64_t)r * ld;
+
+    auto clear_hist = [&]() {
+        for (int i = tid; i < 2 * TQ_BINS / 4; i += TQ_THREADS)
+            reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    };
+    clear_hist();
+    if (tid == 0) s_nfew = 0u;
+
+    // ---- 1. sampled bound -------------------------------------------------
+    uint32_t lo0 = 0x007fffffu;  // key(-inf): every element but NaN
+    if (n > TQ_ALL) {
+        uint32_t sk[16];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            // 4-aligned block start with the block inside the row: s0 + 63 < n.
+            const int blk = (tid >> 4) + 16 * j;
+            const int s0 = (int)(((int64_t)(n - TQ_SBLOCK) * blk / (TQ_SBLOCKS - 1)) & ~3LL);
+            const float4 v = *reinterpret_cast<const float4*>(row + s0 + 4 * (tid & 15));
+            sk[4 * j + 0] = key_of(v.x);
+            sk[4 * j + 1] = key_of(v.y);
+            sk[4 * j + 2] = key_of(v.z);
+            sk[4 * j + 3] = key_of(v.w);
+        }
+        const float E = (float)k * (float)TQ_SAMPLES / (float)n;
+        const uint32_t rho = (uint32_t)min((float)TQ_SAMPLES, E + 4.f * sqrtf(E) + 16.f);
+        __syncthreads();  // histograms cleared
+        // Top 11 key bits (the two 10-bit histograms side by side hold 2,048 bins).
+        uint32_t* h11 = &hist[0][0];
+#pragma unroll
+        for (int e = 0; e < 16; e++) atomicAdd(&h11[sk[e] >> 21], 1u);
+        __syncthreads();
+        find_threshold_bin<TQ_THREADS, 2 * TQ_BINS>(h11, rho, &s_bin, &s_above, sh);
+        const uint32_t b1 = s_bin, rho2 = rho - s_above;
+        clear_hist();
+        __syncthreads();
+        // Next 11 bits of the samples inside that bin.
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+            if ((sk[e] >> 21) == b1) atomicAdd(&h11[(sk[e] >> 10) & 0x7ffu], 1u);
+        __syncthreads();
+        find_threshold_bin<TQ_THREADS, 2 * TQ_BINS>(h11, rho2, &s_bin, &s_above, sh);
+        lo0 = max((b1 << 21) | (s_bin << 10), 0x007fffffu);
+        clear_hist();
+    }
+
+    // ---- 2. stream the row past a bound -------------------------------------
+    // Wave w: positions [w Q, min(n, (w + 1) Q)), 256 per step, lane l taking
+    // the 4-aligned group at 4 l (inside the row allocation: ld is a multiple
+    // of 4 and n <= ld), TQ_PF steps of loads in flight.  Returns false if the
+    // pool ran out.  Counts and largest keys go to wcnt / wmax.
+    const int Q = ((n + 4 * TQ_WAVES - 1) / (4 * TQ_WAVES) + 63) / 64 * 256;
+    // Loads are never conditional (a branch around them would make the
+    // compiler wait for every load at once): addresses past the row are
+    // clamped onto its last 4-aligned group, and their elements masked.
+    const int pmax = (n - 1) & ~3;
+    const int wbeg = wave * Q, wend = min(n, wbeg + Q);
+    const int nsteps = wend > wbeg ? (wend - wbeg + 255) / 256 : 0;
+    auto stream_pass = [&](uint32_t lo) {
+        const float flo = float_of_key(lo);
+        if (tid == 0) s_next = 0u;
+        __syncthreads();  // pool counter reset; previous readers of the lists done
+        // cnt, nch and full are wave-uniform; readfirstlane keeps them scalar.
+        uint32_t cnt = 0, kmax = 0, nch = 0, full = 0;
+        auto load = [&](int st) {
+            return *reinterpret_cast<const float4*>(row + min(wbeg + 256 * st + 4 * lane, pmax));
+        };
+        auto step = [&](int st, const float4& v) {
+            const int p = wbeg + 256 * st + 4 * lane;
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            uint32_t f = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) f |= (p + q < wend && x[q] >= flo) ? (1u << q) : 0u;
+            const uint32_t c = (uint32_t)__popc(f);
+            const uint32_t incl = wave_inclusive_scan(c);
+            const uint32_t step_total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            // Chunks for slots [cnt, cnt + step_total) of this wave's list.
+            const uint32_t need = (uint32_t)__builtin_amdgcn_readfirstlane((int)((cnt + step_total + 63u) >> 6));
+            if (!full && need > nch) {
+                uint32_t first = 0;
+                if (lane == 0) first = atomicAdd(&s_next, need - nch);
+                first = (uint32_t)__builtin_amdgcn_readfirstlane((int)first);
+                if (first + (need - nch) > (uint32_t)TQ_CHUNKS) full = 1u;
+                else if ((uint32_t)lane < need - nch) wch[wave][nch + lane] = (uint8_t)(first + lane);
+                nch = need;
+            }
+            uint32_t slot = cnt + incl - c;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if ((f >> q) & 1u) {
+                    const uint32_t kk = key_of(x[q]);
+                    kmax = max(kmax, kk);
+                    if (!full) {
+                        const uint32_t i = (uint32_t)wch[wave][slot >> 6] * 64u + (slot & 63u);
+                        pkey[i] = kk;
+                        ppos[i] = (uint16_t)(p + q);
+                    }
+                    slot++;
+                }
+            }
+            cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)(cnt + step_total));
+        };
+        // Groups of TQ_PF steps: the loads of group g + 1 go out before group g
+        // is processed (two register sets, loop unrolled by two groups).
+        float4 va[TQ_PF], vb[TQ_PF];
+#pragma unroll
+        for (int i = 0; i < TQ_PF; i++) va[i] = load(i);
+        for (int g0 = 0; g0 < nsteps; g0 += 2 * TQ_PF) {
+#pragma unroll
+            for (int i = 0; i < TQ_PF; i++) vb[i] = load(g0 + TQ_PF + i);
+#pragma unroll
+            for (int i = 0; i < TQ_PF; i++)
+                if (g0 + i < nsteps) step(g0 + i, va[i]);
+#pragma unroll
+            for (int i = 0; i < TQ_PF; i++) va[i] = load(g0 + 2 * TQ_PF + i);
+#pragma unroll
+            for (int i = 0; i < TQ_PF; i++)
+                if (g0 + TQ_PF + i < nsteps) step(g0 + TQ_PF + i, vb[i]);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+        if (lane == 0) {
+            wcnt[wave] = full ? 0xffffffffu : cnt;
+            wmax[wave] = kmax;
+        }
+        __syncthreads();  // lists, counts and cleared histograms visible
+    };
+    uint32_t cw[TQ_WAVES], total = 0, hi = 0;
+    auto gather_counts = [&]() {
+        bool full = false;
+        total = 0;
+        hi = 0;
+#pragma unroll
+        for (int w = 0; w < TQ_WAVES; w++) {
+            cw[w] = wcnt[w];
+            full |= cw[w] == 0xffffffffu;
+            total += full ? 0u : cw[w];
+            hi = max(hi, wmax[w]);
+        }
+        return !full && total >= (uint32_t)k;
+    };
+    stream_pass(lo0);
+    bool fast = gather_counts();
+
+    uint32_t need = (uint32_t)k;
+    uint32_t lo = lo0;
+    auto row_keys = [&](auto&& fn) {  // every element of the row, 4 float4 per thread in flight
+        for (int p0 = 4 * tid; p0 < n; p0 += 16 * TQ_THREADS) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const float4*>(row + min(p0 + 4 * TQ_THREADS * u, pmax));
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int p = p0 + 4 * TQ_THREADS * u;
+                const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    if (p + q < n) fn(key_of(x[q]));
+            }
+        }
+    };
+    bool rows_path = false;  // selection over the row itself (no lists)
+    if (!fast) {
+        // Exact bin of the k-th largest: top 10 key bits of the whole row
+        // (NaN, key 0, included).  hist[0] is clear (stream_pass ran after the
+        // last clear and uses no histogram).
+        uint32_t* h = hist[0];
+        row_keys([&](uint32_t kk) { atomicAdd(&h[kk >> 22], 1u); });
+        __syncthreads();
+        find_threshold_bin<TQ_THREADS, TQ_BINS>(h, (uint32_t)k, &s_bin, &s_above, sh, &s_cnt);
+        const uint32_t b0 = s_bin;
+        const uint32_t upto = s_above + s_cnt;  // elements with key >= b0 << 22
+        for (int i = tid; i < TQ_BINS / 4; i += TQ_THREADS) reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();  // cleared before the radix rounds or the next pass use it
+        if (upto <= (uint32_t)TQ_FIT && b0 != 0u) {
+            // The lists can hold them: stream again past the exact bound (keys
+            // below key(-inf) belong to NaN only, and NaN keys are 0).
+            lo = max(b0 << 22, 0x007fffffu);
+            stream_pass(lo);
+            fast = gather_counts();  // total == upto >= k, and it fits
+        }
+        if (!fast) {
+            rows_path = true;
+            lo = 0u;
+            hi = 0xffffffffu;
+        }
+    }
+
+    // ---- 3. radix rounds --------------------------------------------------------
+    // Each round histograms (key - lo) >> shift over the keys in [lo, hi],
+    // from the lists or (rows_path) the row, and narrows [lo, hi] to the bin
+    // holding the need-th largest.
+    auto list_slot = [&](int w, uint32_t g) { return (uint32_t)wch[w][g >> 6] * 64u + (g & 63u); };
+    auto each_key = [&](auto&& fn) {
+        if (!rows_path) {
+#pragma unroll
+            for (int w = 0; w < TQ_WAVES; w++)
+                for (uint32_t g = tid; g < cw[w]; g += TQ_THREADS) fn(pkey[list_slot(w, g)]);
+        } else {
+            row_keys(fn);
+        }
+    };
+    for (int round = 0;; round++) {
+        uint32_t* h = hist[round & 1];
+        const int shift = max(0, bitlen(hi - lo) - 10);
+        const uint32_t lo_r = lo, hi_r = hi;
+        each_key([&](uint32_t kk) {
+            if (kk >= lo_r && kk <= hi_r) atomicAdd(&h[(kk - lo_r) >> shift], 1u);
+        });
+        __syncthreads();
+        find_threshold_bin<TQ_THREADS, TQ_BINS>(h, need, &s_bin, &s_above, sh, &s_cnt);
+        const uint32_t bin = s_bin;
+        need -= s_above;
+        for (int i = tid; i < TQ_BINS / 4; i += TQ_THREADS)
+            reinterpret_cast<uint4*>(h)[i] = make_uint4(0u, 0u, 0u, 0u);  // for round + 2
+        const uint32_t nlo = lo + (bin << shift);
+        hi = shift == 0 ? nlo : min(hi, nlo + ((1u << shift) - 1u));
+        lo = nlo;
+        if (shift == 0) break;
+        // Few keys left in [lo, hi]: one wave ranks them.
+        if (!rows_path && s_cnt <= (uint32_t)TR_FEW) {
+            const uint32_t lo_f = lo, hi_f = hi;
+            each_key([&](uint32_t kk) {
+                if (kk >= lo_f && kk <= hi_f) few[atomicAdd(&s_nfew, 1u)] = kk;
+            });
+            __syncthreads();
+            if (tid < 64) rank_few(few, s_cnt, need, &s_theta, &s_needeq, &s_eqtot);
+            __syncthreads();
+            lo = s_theta;
+            need = s_needeq;
+            break;
+        }
+    }
+    const uint32_t theta = lo, need_eq = need;
+
+    // ---- 4. ordered output ------------------------------------------------------
+    uint32_t tot;
+    if (!rows_path) {
+        // Entry e of the lists in wave order: wave w = the number of lists that
+        // end at or below e, index e - (entries of the waves before w).
+        const uint32_t per = (total + TQ_THREADS - 1) / TQ_THREADS;
+        const uint32_t e0 = min(total, tid * per), e1 = min(total, e0 + per);
+        auto entry = [&](uint32_t e) {
+            int w = 0;
+            uint32_t base = 0;
+#pragma unroll
+            for (int i = 0; i < TQ_WAVES - 1; i++) {
+                if (w == i && e >= base + cw[i]) {
+                    base += cw[i];
+                    w++;
+                }
+            }
+            return list_slot(w, e - base);
+        };
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t e = e0; e < e1; e++) {
+            const uint32_t kk = pkey[entry(e)];
+            gt += kk > theta ? 1u : 0u;
+            eq += kk == theta ? 1u : 0u;
+        }
+        // Both counts in one scan (each total is below TQ_CAP < 2^16).
+        const uint32_t before = block_exclusive_scan<TQ_THREADS>(gt | (eq << 16), &tot, sh);
+        uint32_t eqb = before >> 16;
+        uint32_t pos = (before & 0xffffu) + min(eqb, need_eq);
+        for (uint32_t e = e0; e < e1; e++) {
+            const uint32_t i = entry(e);
+            const uint32_t kk = pkey[i];
+            bool keep = kk > theta;
+            if (kk == theta) {
+                keep = eqb < need_eq;
+                eqb++;
+            }
+            if (keep) {
+                if (pos < (uint32_t)k) out[pos] = (int32_t)ppos[i];  // exactly k are kept
+                pos++;
+            }
+        }
+    } else {
+        // Thread t owns positions [t S, (t + 1) S): count, two block scans
+        // (counts above theta, theta-valued counts), then write in order.
+        const int S = ((n + TQ_THREADS - 1) / TQ_THREADS + 3) & ~3;
+        const int pb = min(n, tid * S), pe = min(n, pb + S);
+        uint32_t gt = 0, eq = 0;
+        for (int p = pb; p < pe; p += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + p);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t kk = key_of(x[q]);
+                gt += (p + q < pe && kk > theta) ? 1u : 0u;
+                eq += (p + q < pe && kk == theta) ? 1u : 0u;
+            }
+        }
+        const uint32_t gt_before = block_exclusive_scan<TQ_THREADS>(gt, &tot, sh);
+        uint32_t eqb = block_exclusive_scan<TQ_THREADS>(eq, &tot, sh);
+        uint32_t pos = gt_before + min(eqb, need_eq);
+        for (int p = pb; p < pe; p += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + p);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if (p + q >= pe) continue;
+                const uint32_t kk = key_of(x[q]);
+                bool keep = kk > theta;
+                if (kk == theta) {
+                    keep = eqb < need_eq;
+                    eqb++;
+                }
+                if (keep) {
+                    if (pos < (uint32_t)k) out[pos] = p + q;
+                    pos++;
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // Calls that take the chunked path for few rows (topk_sfilter_kernel).
@@ -1561,8 +1956,17 @@ void launch_topk(int32_t num_rows, int32_t max_visible, const int32_t* vis, cons
         return;
     }
     const bool has_long = max_visible > TR_ROW_PATH_MAXN;
-    hipLaunchKernelGGL(topk_rows_kernel, item_grid(1, num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld, k,
-                       indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr, (int)num_rows);
+    // Many rows: the rows of up to TQ_MAXN positions take four small
+    // workgroups per CU (topk_stream_kernel); the one-workgroup kernel then
+    // only samples the long rows.
+    const bool streamed = num_rows >= TQ_MIN_ROWS;
+    if (streamed)
+        hipLaunchKernelGGL(topk_stream_kernel, item_grid(1, num_rows), dim3(TQ_THREADS), 0, stream, vis, scores, ld,
+                           k, indices, (int)num_rows);
+    if (!streamed || has_long)
+        hipLaunchKernelGGL(topk_rows_kernel, item_grid(1, num_rows), dim3(TR_THREADS), 0, stream, vis, scores, ld,
+                           k, indices, (int)TR_ROW_PATH_MAXN, has_long ? tw.rowst : nullptr, (int)num_rows,
+                           streamed ? 1 : 0);
     if (!has_long) return;
     const int CH = tw.chunks;
     const int min_n = TR_ROW_PATH_MAXN;

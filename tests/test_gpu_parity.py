@@ -314,6 +314,74 @@ def test_topk_bitexact_many_rows_few_long(dsa, oracle_mod):
     assert not bad, bad
 
 
+def _stream_rows(R, seed, max_n):
+    """R rows for the many-rows top-k kernel: every length class around its
+    thresholds, normal scores in most rows and, in others, 8-valued ties,
+    all-equal rows, coarse values, denormals with signed zeros, NaN runs, -inf
+    blocks, +inf, an ascending row whose candidates all belong to the last
+    wave (they share the pool), ties above every other score, and large
+    scores hidden between the sample blocks (exact-bound pass)."""
+    g = np.random.default_rng(seed)
+    lens = g.integers(1, max_n + 1, size=R).astype(np.int32)
+    edge = [1, 2047, 2048, 2049, 3071, 3072, 3073, 4096, 8192, 8193, 9000, 32768, 65535, 65536]
+    lens[: len(edge)] = [min(e, max_n) for e in edge]
+    n = int(lens.max())
+    s = wl.random_scores(seed, R, n, kind="normal")
+    kinds = ["ties", "zeros", "coarse", "tiny", "signed_zeros"]
+    for i, r in enumerate(range(len(edge), len(edge) + 3 * len(kinds))):
+        s[r] = wl.random_scores(seed + 1 + i, 1, n, kind=kinds[i % len(kinds)])[0]
+        lens[r] = max(int(lens[r]), 9000)
+    r0 = len(edge) + 3 * len(kinds)
+    lens[r0:r0 + 5] = [60000, 60000, 40000, 20000, 65536]
+    s[r0, 100:59000] = np.nan                        # fewer non-NaN scores than k: NaN kept, lowest positions first
+    s[r0 + 1, :30000] = -np.inf
+    s[r0 + 1, 40000] = np.inf
+    s[r0 + 2, :40000] = np.arange(40000, dtype=np.float32)  # ascending: the last quarter holds every candidate
+    s[r0 + 3] = s[r0 + 3] * np.float32(1 / 16)
+    s[r0 + 3, ::20] = np.float32(5.0)                 # 1,000 ties above every other score: theta for k < 1,000
+    # 2,400 large scores placed between the kernel's 64 sample blocks (64
+    # positions at ((n - 64) b / 63) & ~3): the sampled bound misses them and
+    # too many candidates pass it, so the row takes the exact-bound pass.
+    n4 = 65536
+    starts = [((n4 - 64) * b // 63) & ~3 for b in (10, 20, 30)]
+    big = np.concatenate([np.arange(a + 200, a + 1000) for a in starts])
+    s[r0 + 4, big] = np.float32(1e6) + np.arange(len(big), dtype=np.float32)
+    return lens, s
+
+
+@pytest.mark.parametrize("k", [2048, 1, 7, 300])
+def test_topk_bitexact_stream_kernel_many_rows(dsa, oracle_mod, k):
+    """Calls with at least 1,024 rows whose rows have at most 65,536 positions
+    take the four-per-CU streaming kernel: sampled bound, per-wave ordered
+    candidate lists in a shared chunk pool, radix rounds, and the exact-bound
+    re-stream or whole-row fallback when the pool overflows or holds fewer
+    than k (ties at the bound, NaN, all-equal rows)."""
+    lens, s = _stream_rows(1030, 90 + k, 65536)
+    got = run_topk(dsa, lens, s, k)
+    ref = oracle_mod.topk(lens, s, k)
+    bad = [r for r in range(len(lens)) if not np.array_equal(got[r], ref[r])]
+    assert not bad, bad[:10]
+
+
+def test_topk_bitexact_stream_kernel_beside_long_rows(dsa, oracle_mod):
+    """Many rows with a few longer than 65,536 positions: the streaming kernel
+    takes the short rows, the one-workgroup kernel only samples the long ones
+    and the multi-workgroup path finishes them; each row has exactly one owner."""
+    lens, s = _stream_rows(1040, 7, 65536)
+    n_long = 90000
+    s2 = np.zeros((len(lens), n_long), np.float32)
+    s2[:, : s.shape[1]] = s
+    del s
+    long_at = [3, 200, 1039]
+    for i, r in enumerate(long_at):
+        lens[r] = [65537, n_long, 70001][i]
+        s2[r] = wl.random_scores(500 + r, 1, n_long, kind=["normal", "ties", "normal"][i])[0]
+    got = run_topk(dsa, lens, s2, 2048)
+    ref = oracle_mod.topk(lens, s2, 2048)
+    bad = [r for r in range(len(lens)) if not np.array_equal(got[r], ref[r])]
+    assert not bad, bad[:10]
+
+
 @pytest.mark.parametrize("k", [2048, 1, 300])
 def test_topk_bitexact_chunked_path_for_few_rows(dsa, oracle_mod, k):
     """Calls with at most 256 rows whose longest row has 65,537..262,144
