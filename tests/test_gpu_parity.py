@@ -590,11 +590,11 @@ def test_attention_many_rows_single_split(dsa, oracle_mod):
 
 # ----------------------------------------------------------------------------- fused path
 
-def recall_check(idx_gpu, idx_ref, s_ref64, vis):
+def recall_check(idx_gpu, idx_ref, s_ref64, vis, k=2048):
     recalls = []
     for r in range(len(vis)):
         n = int(vis[r])
-        kr = min(2048, n)
+        kr = min(k, n)
         a = set(idx_gpu[r][idx_gpu[r] >= 0].tolist())
         b = set(idx_ref[r][idx_ref[r] >= 0].tolist())
         assert len(a) == kr
@@ -1184,6 +1184,82 @@ def test_decode_step_chunk_boundaries_packed_and_paged(dsa, oracle_mod):
 
 
 # ----------------------------------------------------------------------------- IndexShare
+
+def _random_batch(seed):
+    """A random decode batch: 1-39 decode rows with log-uniform lengths
+    (1..12,000, each seeing its whole sequence) and, in most batches, a causal
+    chunk of 1-89 rows on a 0-4,999-position history, inserted as one
+    contiguous run at a random place (so shared 32-row blocks start at any
+    offset).  Returns the workload and its per-row sequence index."""
+    g = np.random.default_rng(1000 + seed)
+    n_dec = int(g.integers(1, 40))
+    dec = np.floor(np.exp(g.uniform(0.0, np.log(12000.0), size=n_dec))).astype(np.int64)
+    chunk = int(g.integers(0, 90)) if seed % 3 else 0
+    hist = int(g.integers(0, 5000))
+    seq_len = np.array(list(dec) + ([hist + chunk] if chunk else []), np.int64)
+    seq_base = np.concatenate([[0], np.cumsum(seq_len)[:-1]]).astype(np.int64)
+    at = int(g.integers(0, n_dec + 1))
+    vis = list(dec[:at]) + list(range(hist + 1, hist + chunk + 1)) + list(dec[at:])
+    rseq = list(range(at)) + [n_dec] * chunk + list(range(at, n_dec))
+    rseq = np.array(rseq, np.int64)
+    w = wl.Workload(name=f"rand{seed}", seed=40 + seed, visible_len=np.array(vis, np.int32),
+                    row_cache_base=seq_base[rseq], seq_len=seq_len, seq_base=seq_base, row_seq=rseq,
+                    description="random batch")
+    return w, seq_base, seq_len, chunk
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_decode_step_random_batches(dsa, oracle_mod, seed):
+    """Random batches through the fused step, packed and over a paged pool
+    (random block size): the two agree bit for bit; rows with n <= k select
+    0..n-1; sampled rows agree with the oracle (recall with near-threshold
+    swaps only, attention on the GPU's own lists)."""
+    w, seq_base, seq_len, chunk = _random_batch(seed)
+    g = np.random.default_rng(2000 + seed)
+    k = int(g.choice([1, 64, 300, 2048]))
+    iscale = float(g.choice([1.0, 0.5]))
+    B = int(g.choice([16, 64, 256]))
+    x = w.generate()
+    d = device_inputs(x)
+    vis, base = x["visible_len"], x["row_cache_base"]
+    R = len(vis)
+    flags = 0 if chunk else dsa.ROWS_DISTINCT_SEQUENCES
+    rows = make_rows(dsa, vis, base, flags)
+
+    def outs():
+        return (torch.empty((R, k), dtype=torch.int32, device=DEV),
+                torch.empty((R, 64, 512), dtype=torch.float32, device=DEV),
+                torch.empty((R, 64), dtype=torch.float32, device=DEV))
+
+    idx_a, out_a, lse_a = outs()
+    ws = dsa.workspace(dsa.dsa_decode_step_workspace_size(R, int(vis.max()), k), DEV)
+    dsa.dsa_decode_step(rows, d["q_idx"], d["w"], d["k_idx"], iscale, d["q_abs"], d["kv_latent"],
+                        wl.SOFTMAX_SCALE, k, idx_a, out_a, lse_a, ws)
+    kpool, lpool, bt, seq_of_row = page_caches(x, seq_base, seq_len, B, seed=seed)
+    prow = make_rows(dsa, vis, seq_of_row, flags)
+    idx_b, out_b, lse_b = outs()
+    ws = dsa.workspace(dsa.dsa_decode_step_paged_workspace_size(R, int(vis.max()), k), DEV)
+    dsa.dsa_decode_step_paged(prow, dsa.Paged(dev(bt), B), d["q_idx"], d["w"], dev_bf16(kpool), iscale, d["q_abs"],
+                              dev_bf16(lpool), wl.SOFTMAX_SCALE, k, idx_b, out_b, lse_b, ws)
+    torch.cuda.synchronize()
+    idx_h, out_h, lse_h = idx_a.cpu().numpy(), out_a.cpu().numpy(), lse_a.cpu().numpy()
+    assert np.array_equal(idx_h, idx_b.cpu().numpy())
+    assert np.array_equal(out_h.view(np.uint32), out_b.cpu().numpy().view(np.uint32))
+    assert np.array_equal(lse_h.view(np.uint32), lse_b.cpu().numpy().view(np.uint32))
+    for r in range(R):
+        n = int(vis[r])
+        if n <= k:
+            assert np.array_equal(idx_h[r], np.where(np.arange(k) < n, np.arange(k), -1)), r
+    rs = sorted(set(g.choice(R, size=min(R, 10), replace=False).tolist()) | {0, R - 1})
+    y = sub(x, rs)
+    s64, _, idx_ref, _, _ = oracle_mod.decode_step(y["visible_len"], y["row_cache_base"], y["q_idx"], y["w"],
+                                                   y["k_idx"], y["q_abs"], y["kv_latent"], k, iscale,
+                                                   wl.SOFTMAX_SCALE)
+    assert recall_check(idx_h[rs], idx_ref, s64, y["visible_len"], k) >= 0.999
+    ref_out, ref_lse = oracle_mod.sparse_mla(y["row_cache_base"], y["q_abs"], y["kv_latent"], idx_h[rs],
+                                             wl.SOFTMAX_SCALE)
+    check_attention(out_h[rs], lse_h[rs], ref_out, ref_lse, f"random batch {seed}")
+
 
 def test_index_share_cold_start_block_and_first_period(dsa, oracle_mod):
     """Layers 0..9 of the GLM-5.2 pattern (3 full, 3 shared, 1 full, 3 shared;
