@@ -329,21 +329,29 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
         // spread over the PV MFMAs: a wave waiting for the address unit leaves
         // the matrix core to the other output wave of its SIMD.
         const bool five = ob < AT_GQ - 4 * AT_OWAVES;  // wave-uniform
+        // Per gather i: the tile row lane L fetches for (clamped for the
+        // fifth gather of waves that issue only four) and the byte offset of
+        // its swizzled chunk in that latent row.  Both are fixed for the
+        // whole loop.
+        int grow[5], gbyte[5];
+#pragma unroll
+        for (int i = 0; i < 5; i++) {
+            const int p = min((ob + AT_OWAVES * i) * 64 + lane, AT_TILE * AT_CHUNKS - 1);
+            grow[i] = p / AT_CHUNKS;
+            gbyte[i] = 16 * ((p - grow[i] * AT_CHUNKS) ^ (grow[i] & 7));
+        }
         int gid[5];
         auto gather_ids = [&](int t) {
 #pragma unroll
-            for (int i = 0; i < 5; i++)
-                gid[i] = sid[t % AT_SID][min((ob + AT_OWAVES * i) * 64 + lane, AT_TILE * AT_CHUNKS - 1) / AT_CHUNKS];
+            for (int i = 0; i < 5; i++) gid[i] = sid[t % AT_SID][grow[i]];
         };
+        const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kvrow);
         auto gather_one = [&](int t, int i) {
             const int q = ob + AT_OWAVES * i;
             const uint32_t dst =
                 __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ring[t % AT_STAGES] + q * 1024));
-            const int p = q * 64 + lane;
-            const int row = p / AT_CHUNKS;
-            const int part = (p - row * AT_CHUNKS) ^ (row & 7);
             const int64_t gr = gid[i] >= 0 ? (int64_t)gid[i] : (pad_rows ? -1 - (int64_t)gid[i] : 0);
-            gather16_to_lds(kvrow + gr * 576 + part * 8, dst);
+            gather16_to_lds(kvbytes + gr * 1152 + gbyte[i], dst);
         };
         auto issue = [&](int t) {
             gather_ids(t);
