@@ -257,7 +257,7 @@ dsa_status_t attn_impl(const dsa_rows_t* rows, const dsa::PagedCache& pc, const 
         idx = phys;
     }
     dsa::launch_sparse_mla(rows->num_rows, base, (const uint16_t*)q_abs, (const uint16_t*)kv_latent, idx, k,
-                           softmax_scale, out_latent, out_lse, aws, st, pc.block_table != nullptr);
+                           softmax_scale, out_latent, out_lse, aws, st, rows->max_visible, pc.block_table != nullptr);
     return after_launch(st, "sparse_mla");
 }
 

@@ -63,7 +63,8 @@ int attn_pick_splits(int32_t num_rows, int32_t k);
 size_t attn_workspace_bytes(int32_t num_rows, int32_t k);
 void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa,
                        const uint16_t* kv, const int32_t* idx, int32_t k, float softmax_scale,
-                       float* out, float* lse, void* ws, hipStream_t stream, bool pad_rows = false);
+                       float* out, float* lse, void* ws, hipStream_t stream, int32_t max_visible,
+                       bool pad_rows = false);
 
 // Logical selection -> physical pool rows of a paged latent cache; a negative
 // entry becomes -1 - (pool row of the sequence's position 0), the row the

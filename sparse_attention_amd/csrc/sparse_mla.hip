@@ -102,6 +102,14 @@ __device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_ba
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
 
+// The same from a uniform 64-bit base plus a 32-bit per-lane byte offset
+// (the scalar-base form: no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void gather16_to_lds_off(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+
 // The same for 4 bytes per lane (lane L's word lands at lds_base + 4 L).
 __device__ __forceinline__ void load4_to_lds(const void* src, uint32_t lds_base)
 {
@@ -109,6 +117,17 @@ __device__ __forceinline__ void load4_to_lds(const void* src, uint32_t lds_base)
 }
 #pragma clang diagnostic pop
 
+// Byte offset of a shared-memory object inside the workgroup's LDS, as the
+// direct loads take it in M0.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_offset(T* p)
+{
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
+}
+
+// OFF32: every gathered row lies within 2^32 bytes of the row's cache base
+// (no paged pool), so a gather address is the base plus a 32-bit offset.
+template <bool OFF32>
 __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t* __restrict__ base,
                                                            const uint16_t* __restrict__ qa,
                                                            const uint16_t* __restrict__ kv,
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
         auto fetch_ids = [&](int tt) {
             if (lane < AT_TILE) {
                 const int i = min(tt * AT_TILE + lane, nslots - 1);
-                load4_to_lds(irow + i, (uint32_t)(uintptr_t)&sid[tt % AT_SID][0]);
+                load4_to_lds(irow + i, lds_offset(&sid[tt % AT_SID][0]));
             }
         };
         if (wr == 0 && AT_STAGES < ntiles) fetch_ids(AT_STAGES);
@@ -346,12 +365,20 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
             for (int i = 0; i < 5; i++) gid[i] = sid[t % AT_SID][grow[i]];
         };
         const uint8_t* kvbytes = reinterpret_cast<const uint8_t*>(kvrow);
+        const uint32_t ring_lds = lds_offset(&ring[0][0]);
         auto gather_one = [&](int t, int i) {
             const int q = ob + AT_OWAVES * i;
             const uint32_t dst =
-                __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ring[t % AT_STAGES] + q * 1024));
-            const int64_t gr = gid[i] >= 0 ? (int64_t)gid[i] : (pad_rows ? -1 - (int64_t)gid[i] : 0);
-            gather16_to_lds(kvbytes + gr * 1152 + gbyte[i], dst);
+                __builtin_amdgcn_readfirstlane(ring_lds + (uint32_t)((t % AT_STAGES) * AT_TILE_BYTES + q * 1024));
+            if constexpr (OFF32) {
+                // No pool: padding fetches row 0.  Rows stay below 2^24 here
+                // (2^32 / 1152), so the offset is one 24-bit multiply-add.
+                const uint32_t gr = (uint32_t)min(max(gid[i], 0), 0xffffff);
+                gather16_to_lds_off(kvbytes, gr * 1152u + (uint32_t)gbyte[i], dst);
+            } else {
+                const int64_t gr = gid[i] >= 0 ? (int64_t)gid[i] : (pad_rows ? -1 - (int64_t)gid[i] : 0);
+                gather16_to_lds(kvbytes + gr * 1152 + gbyte[i], dst);
+            }
         };
         auto issue = [&](int t) {
             gather_ids(t);
@@ -581,7 +608,7 @@ size_t attn_workspace_bytes(int32_t num_rows, int32_t k)
 
 void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa, const uint16_t* kv,
                        const int32_t* idx, int32_t k, float softmax_scale, float* out, float* lse, void* ws,
-                       hipStream_t stream, bool pad_rows)
+                       hipStream_t stream, int32_t max_visible, bool pad_rows)
 {
     const int s = attn_pick_splits(num_rows, k);
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
@@ -595,8 +622,15 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
     // Several splits only occur below 256 rows (attn_pick_splits), so their
     // one-dimensional grid stays small.
     const dim3 grid = s == 1 ? item_grid(1, num_rows) : dim3((unsigned)(((num_rows + 7) / 8) * 8 * s));
-    hipLaunchKernelGGL(sparse_mla_kernel, grid, dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k, (int)num_rows,
-                       softmax_scale * LOG2E, split_len, s, pad_rows ? 1 : 0, out, lse, part_o, part_ml);
+    // Selected positions lie below max_visible; pool rows (pad_rows) are not bounded.
+    const bool off32 = !pad_rows && (uint64_t)max_visible * 1152 <= 0xffffffffull;
+    if (off32)
+        hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k,
+                           (int)num_rows, softmax_scale * LOG2E, split_len, s, 0, out, lse, part_o, part_ml);
+    else
+        hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, dim3(AT_THREADS), 0, stream, base, qa, kv, idx, k,
+                           (int)num_rows, softmax_scale * LOG2E, split_len, s, pad_rows ? 1 : 0, out, lse, part_o,
+                           part_ml);
     if (s > 1)
         hipLaunchKernelGGL(sparse_mla_combine_kernel, item_grid(64, num_rows), dim3(128), 0, stream, part_o, part_ml,
                            s, (int)num_rows, out, lse);
