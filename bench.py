@@ -600,7 +600,7 @@ def main():
                      if prefill is None else
                      {"bound": "mfma", "achieved": prefill["attention"]["tflops"], "peak": MFMA_BF16_PEAK_TFS,
                       "unit": "TFLOP/s", "frac": prefill["attention"]["mfma_frac"], "traffic": None,
-                      "kernel": "sparse_mla_kernel", "kernel_us": prefill["attention"]["us"],
+                      "kernel": "sparse_mla_kernel<true>", "kernel_us": prefill["attention"]["us"],
                       "alg_flops_per_launch": prefill["attention"]["alg_flops"]}),
         "cpu_baseline": cpu,
         "projections": projections,
