@@ -267,17 +267,21 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
             // Validity of the tile's 32 slots (bit p: slot p holds a position).
             const uint32_t vbits =
                 (uint32_t)__ballot(sid[t % AT_SID][lane & 31] >= 0 && t * AT_TILE + (lane & 31) < nslots);
+            // Raw scores; the scale (> 0, so the maximum commutes with it) is
+            // applied to the tile maximum and inside the exponent's fma.
             float z[8];
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                z[v] = s0[v] * scale_log2;
-                z[4 + v] = s1[v] * scale_log2;
+                z[v] = s0[v];
+                z[4 + v] = s1[v];
             }
+            if (vbits != 0xffffffffu) {  // wave-uniform: only tiles with empty slots
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                z[e] = ((vbits >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u) ? z[e] : -INFINITY;
+                for (int e = 0; e < 8; e++)
+                    z[e] = ((vbits >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u) ? z[e] : -INFINITY;
+            }
             float mt = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-            mt = xrow_max(mt);
+            mt = xrow_max(mt) * scale_log2;
 
             // Lazy reference maximum: m_run moves only when the tile's maximum
             // exceeds it by more than 2^RESCALE_LOG2, so weights stay below
@@ -291,14 +295,14 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
             m_run = m_new;
             const float m_safe = (m_run == -INFINITY) ? 0.f : m_run;  // then every z is -inf
 
-            // P = 2^(z - m_run) (zero for empty slots), rounded to bf16, stored
-            // as this lane's PV A operand: row = head h0 + j, k = positions
-            // {4g..4g+3, 16+4g..16+4g+3}.
+            // P = 2^(scale z - m_run) (zero for empty slots), rounded to bf16,
+            // stored as this lane's PV A operand: row = head h0 + j, k =
+            // positions {4g..4g+3, 16+4g..16+4g+3}.
             u32x4 pk;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float p0 = __builtin_amdgcn_exp2f(z[2 * e] - m_safe);
-                const float p1 = __builtin_amdgcn_exp2f(z[2 * e + 1] - m_safe);
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * e], scale_log2, -m_safe));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z[2 * e + 1], scale_log2, -m_safe));
                 l_run += p0 + p1;
                 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
                 const bf16x2 h = {(__bf16)p0, (__bf16)p1};
