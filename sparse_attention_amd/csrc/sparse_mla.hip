@@ -38,6 +38,8 @@
 //  - Splits write unnormalized partials (O, running max, running sum); a
 //    combine kernel merges them in split order, so results do not depend on
 //    scheduling.  A single split normalizes in place.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -585,21 +587,42 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
 
 int attn_pick_splits(int32_t num_rows, int32_t k)
 {
+    // The split count with the least modelled time.  One 768-thread
+    // workgroup fills a CU (LDS ring and registers), so at most 256 run at
+    // once and the rest start in later rounds.  A workgroup costs ~7 us
+    // besides its tiles (index list and queries in, output or partial out);
+    // a tile takes the longer of ~1.03 us (one CU's gather rate, three tiles
+    // in flight) and the time the busy CUs' tiles take together at ~6.5 TB/s.
+    // Every split adds a 128 KB fp32 partial per row, written and read back
+    // by the merge, which is one more launch.  Fitted to decode batches of
+    // 2,048 selected rows (attention + merge): 64 rows 39.4 us with 3
+    // splits against 40.8 with 4 and 45.5 with 2; 48 rows 34.4 with 4
+    // against 49.2 with 6 (two rounds); 100 rows 55.6 with 2 against 78.5
+    // with 3; 32 rows 29.0 with 6 against 30.6 with 8; 16 rows 22.3 with 8.
+    constexpr double kTileFloor = 1.03e-6, kGatherBw = 6.5e12, kFixed = 7e-6, kMergeLaunch = 2e-6;
+    constexpr double kPartialBytes = 64.0 * 512 * 4 * 2;  // per row and split: written, then read
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
-    // One 768-thread workgroup per CU (its LDS ring and registers fill the
-    // CU): aim for 256 workgroups.  While at least 128 remain, a split keeps
-    // at least 8 tiles, since every split adds a 128 KB partial to write and
-    // merge (16 rows x 2,048: 8 splits, 22.8 us with the merge, against 26.7 us
-    // with 16).
-    int s = (int)((256 + num_rows - 1) / num_rows);
-    if (s > 16) s = 16;
-    const int keep = (int)((128 + num_rows - 1) / num_rows);
-    if (s > tiles / 8 && tiles / 8 >= keep) s = tiles / 8;
-    if (s > tiles) s = tiles;
-    if (s < 1) s = 1;
-    // Equal whole-tile splits.
-    const int per = (tiles + s - 1) / s;
-    return (tiles + per - 1) / per;
+    int best = 1;
+    double best_t = 0.0;
+    for (int s = 1; s <= 16 && s <= tiles; s++) {
+        const int per = (tiles + s - 1) / s;  // equal whole-tile splits
+        if ((tiles + per - 1) / per != s) continue;  // the same splits as a smaller count
+        const double wgs = (double)num_rows * s;
+        double t = 0.0;
+        for (double left = wgs; left > 0.0; left -= 256.0) {
+            const double busy = left < 256.0 ? left : 256.0;
+            const double step = std::max(kTileFloor, busy * AT_TILE_BYTES / kGatherBw);
+            t += kFixed + per * step;
+        }
+        if (s > 1) t += kMergeLaunch + wgs * kPartialBytes / kGatherBw;
+        // A further split has to save at least 2%: the merge's partials are
+        // the model's least certain part.
+        if (s == 1 || t < 0.98 * best_t) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 size_t attn_workspace_bytes(int32_t num_rows, int32_t k)

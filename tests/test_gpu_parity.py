@@ -646,10 +646,10 @@ def test_prefill_rows_up_to_k_equal_dense(dsa, oracle_mod):
     assert recall_check(idx[rows], idx_ref, s64, y["visible_len"]) >= 0.999
 
 
-@pytest.mark.parametrize("R", [64, 100, 128, 16])
+@pytest.mark.parametrize("R", [64, 128, 48, 16, 8])
 def test_decode_step_attention_matches_standalone_call(dsa, R):
     """The attention inside dsa_decode_step equals dsa_sparse_mla_attn on the
-    same index lists bit for bit, for 4, 3, 2 and 8 splits per row, also when
+    same index lists bit for bit, for 3, 2, 4, 8 and 13 splits per row, also when
     the workspace starts out full of garbage and is reused by a second call
     (the split partials and their merge leave nothing behind)."""
     w, x = inputs("c3")
