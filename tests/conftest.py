@@ -9,7 +9,7 @@ if REPO not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs a gfx950 GPU (runs on the MI355X box)")
+    config.addinivalue_line("markers", "gpu: needs a gfx950 GPU (MI355X)")
 
 
 @pytest.fixture(scope="session")
@@ -28,7 +28,7 @@ def gpu_available():
 
 @pytest.fixture(scope="session")
 def dsa():
-    """The HIP binding; fails (not skips) when the library is missing on a GPU machine."""
+    """The HIP binding; fails (not skips) when the library is missing on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
