@@ -39,6 +39,7 @@
 //    combine kernel merges them in split order, so results do not depend on
 //    scheduling.  A single split normalizes in place.
 #include <algorithm>
+#include <cmath>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -608,12 +609,11 @@ int attn_pick_splits(int32_t num_rows, int32_t k)
         const int per = (tiles + s - 1) / s;  // equal whole-tile splits
         if ((tiles + per - 1) / per != s) continue;  // the same splits as a smaller count
         const double wgs = (double)num_rows * s;
-        double t = 0.0;
-        for (double left = wgs; left > 0.0; left -= 256.0) {
-            const double busy = left < 256.0 ? left : 256.0;
-            const double step = std::max(kTileFloor, busy * AT_TILE_BYTES / kGatherBw);
-            t += kFixed + per * step;
-        }
+        auto round_time = [&](double busy) {
+            return kFixed + per * std::max(kTileFloor, busy * AT_TILE_BYTES / kGatherBw);
+        };
+        const double full = std::floor(wgs / 256.0), rest = wgs - 256.0 * full;
+        double t = full * round_time(256.0) + (rest > 0.0 ? round_time(rest) : 0.0);
         if (s > 1) t += kMergeLaunch + wgs * kPartialBytes / kGatherBw;
         // A further split has to save at least 2%: the merge's partials are
         // the model's least certain part.
