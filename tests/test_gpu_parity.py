@@ -576,6 +576,45 @@ def test_attention_random_index_sets_with_padding(dsa, oracle_mod, k):
         assert np.all(out[4] == 0) and np.all(np.isneginf(lse[4]))
 
 
+def _splits_of_call(dsa, R, k):
+    """Splits per row of an attention call, read back from the workspace it asks
+    for: R * s fp32 partials of 64 x 512 plus R * s (max, sum) pairs of 64."""
+    ws = dsa.dsa_sparse_mla_workspace_size(R, k)
+    al = lambda b: (b + 255) // 256 * 256
+    found = [s for s in range(1, 17) if (0 if s == 1 else al(R * s * 64 * 512 * 4) + al(R * s * 64 * 8)) == ws]
+    assert len(found) == 1, (R, k, ws)
+    return found[0]
+
+
+@pytest.mark.parametrize("R, k, splits", [(1, 2048, 16), (8, 2048, 13), (4, 1000, 11), (16, 2048, 8), (32, 2048, 5),
+                                          (48, 2048, 4), (64, 2048, 3), (100, 2048, 2), (160, 2048, 1)])
+def test_attention_each_split_count(dsa, oracle_mod, R, k, splits):
+    """Attention against the oracle for calls whose rows are split 16, 13, 11,
+    8, 5, 4, 3, 2 ways or not at all (splits of equal whole tiles, the last
+    one shorter where the tiles do not divide), with padding slots inside the
+    lists and one row that selects nothing; sampled rows.  R rows read one
+    4,096-position sequence through their own random index sets."""
+    assert _splits_of_call(dsa, R, k) == splits
+    T = 4096
+    w = wl.Workload(name="splits", seed=40 + R, visible_len=np.full(R, T, np.int32),
+                    row_cache_base=np.zeros(R, np.int64), seq_len=np.array([T], np.int64),
+                    seq_base=np.zeros(1, np.int64), row_seq=np.zeros(R, np.int64))
+    x = w.generate()
+    g = np.random.default_rng(1000 * R + k)
+    idx = np.stack([np.sort(g.choice(T, size=k, replace=False)) for _ in range(R)]).astype(np.int32)
+    idx[0, 3:40] = -1                 # padding inside the first row's list
+    if R > 2:
+        idx[R // 2, :] = -1           # a row with nothing selected
+    out, lse = run_attn(dsa, x, idx, k)
+    rows = sorted({0, R // 2, R - 1})
+    y = sub(x, rows)
+    ref_out, ref_lse = oracle_mod.sparse_mla(y["row_cache_base"], y["q_abs"], x["kv_latent"], idx[rows],
+                                             wl.SOFTMAX_SCALE)
+    check_attention(out[rows], lse[rows], ref_out, ref_lse, f"R={R} k={k} splits={splits}")
+    if R > 2:
+        assert np.all(out[R // 2] == 0) and np.all(np.isneginf(lse[R // 2]))
+
+
 def test_attention_many_rows_single_split(dsa, oracle_mod):
     # >= 512 rows: one split per row (no combine pass).
     w = wl.prefill(700, seed=5)
