@@ -1,7 +1,9 @@
 """dsa_decode_step_noalloc (the fused step over the library's own scratch
 array, for callers that cannot allocate) against dsa_decode_step, through the
 C ABI: bit-for-bit equal outputs on two calls in a row, the second smaller,
-then a call whose score rows exceed the scratch and are taken in chunks."""
+then a call whose score rows exceed the scratch and are taken in chunks; and
+the call captured in a HIP graph (it allocates nothing, so it can be), whose
+replays equal the eager call."""
 import numpy as np
 import pytest
 import torch
@@ -71,3 +73,45 @@ def test_noalloc_rejects_rows_the_scratch_cannot_hold(dsa):
                                     1.0, t(R * 64 * 576, torch.bfloat16), t(maxv * 576, torch.bfloat16), 0.0625,
                                     2048, t(R * 2048, torch.int32), t(R * 64 * 512), t(R * 64))
     assert e.value.status == 1 and "scratch" in e.value.detail
+
+
+def test_noalloc_step_replays_from_a_graph(dsa):
+    x = wl.decode(16, 5000, seed=11).generate()
+    vis, base = x["visible_len"], x["row_cache_base"]
+    R, k = len(vis), 2048
+    rows = dsa.Rows(torch.from_numpy(vis).to(DEV), torch.from_numpy(base).to(DEV), int(vis.max()))
+    d = dict(q_idx=_dev_bf16(x["q_idx"]), w=torch.from_numpy(x["w"]).to(DEV), k_idx=_dev_bf16(x["k_idx"]),
+             q_abs=_dev_bf16(x["q_abs"]), kv=_dev_bf16(x["kv_latent"]))
+    idx = torch.empty((R, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((R, 64, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((R, 64), dtype=torch.float32, device=DEV)
+
+    def step():
+        dsa.dsa_decode_step_noalloc(rows, d["q_idx"], d["w"], d["k_idx"], wl.INDEX_SCALE, d["q_abs"], d["kv"],
+                                    wl.SOFTMAX_SCALE, k, idx, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.cpu().numpy(), out.cpu().numpy().view(np.uint32), lse.cpu().numpy().view(np.uint32))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        # eager work between replays: clobber the outputs
+        idx.fill_(-5)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref[0]), rep
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref[1]), rep
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref[2]), rep
