@@ -215,7 +215,7 @@ DSA_API dsa_status_t dsa_decode_step(const dsa_rows_t* rows, const void* q_idx, 
  * other host threads) race and must be serialized by the caller.
  * Errors: as for dsa_decode_step, plus DSA_ERR_INVALID_ARGUMENT when even 32
  * rows at a time (with the attention's split partials for every row) exceed
- * the scratch (from max_visible of about 770,000 positions up, depending on
+ * the scratch (from max_visible of about 900,000 positions up, depending on
  * the row count); DSA_ERR_HIP if
  * the scratch array's device address cannot be obtained. */
 #define DSA_NOALLOC_SCRATCH_BYTES (128u << 20)

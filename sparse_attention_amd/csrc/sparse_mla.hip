@@ -35,9 +35,10 @@
 //  - One barrier per tile: score waves hand over P(t) while output waves
 //    finish PV(t-1); P, the rescale factors and the selected indices live in
 //    small double / octuple buffers.
-//  - Splits write unnormalized partials (O, running max, running sum); a
-//    combine kernel merges them in split order, so results do not depend on
-//    scheduling.  A single split normalizes in place.
+//  - A split writes its own normalized output, rounded to bf16, with its
+//    running maximum and sum; a combine kernel merges the splits in split
+//    order (in fp32), so results do not depend on scheduling.  A single split
+//    writes the fp32 output itself.
 #include <algorithm>
 #include <cmath>
 
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
                                                            int num_rows, float scale_log2, int split_len,
                                                            int nsplit, int pad_rows,
                                                            float* __restrict__ out, float* __restrict__ lse,
-                                                           float* __restrict__ part_o,
+                                                           uint16_t* __restrict__ part_o,
                                                            float2* __restrict__ part_ml)
 {
     // One split per row: rows in reverse (in a causal prefill chunk the last
@@ -503,17 +504,18 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
         if (ntiles > 0) pv_last(ntiles - 1);
         __syncthreads();  // lfin visible
 
-        // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j]; the
+        // Epilogue.  Lane (j, g) holds O[16 mb + 4 g + v][c0 + 16 cb + j],
+        // normalized by the head's sum (a split normalizes by its own).  The
         // block goes through this wave's own region of the (now idle) ring,
         // rows padded to AT_OPAD floats, so that the stores leave as 16-byte
-        // pieces of 256-byte row segments.
+        // pieces of row segments.
         float* ot = reinterpret_cast<float*>(&ring[0][0]) + ob * (64 * AT_OPAD);
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) {
             const floatx4 lv = *reinterpret_cast<const floatx4*>(&lfin[16 * mb + 4 * g]);
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const float scl = nsplit == 1 ? (lv[v] > 0.f ? 1.f / lv[v] : 0.f) : 1.f;
+                const float scl = lv[v] > 0.f ? 1.f / lv[v] : 0.f;
                 float* orow = ot + (16 * mb + 4 * g + v) * AT_OPAD + j;
 #pragma unroll
                 for (int cb = 0; cb < AT_OCB; cb++) orow[16 * cb] = o[mb][cb][v] * scl;
@@ -523,22 +525,43 @@ __global__ __launch_bounds__(AT_THREADS, 1) void sparse_mla_kernel(const int64_t
         // Non-temporal stores: the output (or the split partials, read once
         // by the combine kernel) would otherwise be written back from L2 at
         // the kernel's end.
-        float* dst = nsplit == 1 ? out + (int64_t)r * 64 * 512 + c0
-                                 : part_o + ((int64_t)r * nsplit + sp) * 64 * 512 + c0;
+        if (nsplit == 1) {
+            float* dst = out + (int64_t)r * 64 * 512 + c0;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int h = 4 * i + (lane >> 4), c = 4 * (lane & 15);
-            const floatx4 val = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
-            __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c));
+            for (int i = 0; i < 16; i++) {
+                const int h = 4 * i + (lane >> 4), c = 4 * (lane & 15);
+                const floatx4 val = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
+                __builtin_nontemporal_store(val, reinterpret_cast<floatx4*>(dst + (int64_t)h * 512 + c));
+            }
+        } else {
+            // A split's partial, rounded to bf16 (to nearest even): a convex
+            // combination of V rows, so each element is off by at most
+            // 2^-9 max|V|, the precision of a bf16 output.
+            uint16_t* dst = part_o + ((int64_t)r * nsplit + sp) * 64 * 512 + c0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int h = 8 * i + (lane >> 3), c = 8 * (lane & 7);
+                const floatx4 a = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c);
+                const floatx4 b = *reinterpret_cast<const floatx4*>(ot + h * AT_OPAD + c + 4);
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                u32x4 pk;
+                pk[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[0], (__bf16)a[1]});
+                pk[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a[2], (__bf16)a[3]});
+                pk[2] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)b[0], (__bf16)b[1]});
+                pk[3] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)b[2], (__bf16)b[3]});
+                __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(dst + (int64_t)h * 512 + c));
+            }
         }
     }
 }
 
 // Merges split partials in split order: one workgroup per (head, row), each
-// thread four latent columns.  Every split's loads are issued before any is
-// used (one memory round trip per thread); the arithmetic still runs in
-// split order, so results do not depend on scheduling.
-__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __restrict__ part_o,
+// thread four latent columns.  A split's partial is its own normalized output
+// (bf16) with its running maximum m_s and sum l_s, so the merge weighs split s
+// by l_s 2^(m_s - M).  Every split's loads are issued before any is used (one
+// memory round trip per thread); the arithmetic still runs in split order, so
+// results do not depend on scheduling.
+__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const uint16_t* __restrict__ part_o,
                                                                 const float2* __restrict__ part_ml, int nsplit,
                                                                 int num_rows, float* __restrict__ out,
                                                                 float* __restrict__ lse)
@@ -548,14 +571,14 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
     const int r = grid_item();
     if (r >= num_rows) return;
     const float2* ml = part_ml + (int64_t)r * nsplit * 64 + h;
-    const float* po = part_o + ((int64_t)r * nsplit * 64 + h) * 512 + 4 * threadIdx.x;
+    const uint16_t* po = part_o + ((int64_t)r * nsplit * 64 + h) * 512 + 4 * threadIdx.x;
     float2 e[MAXS];
-    float4 p[MAXS];
+    uint2 p[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; s++) {
         if (s < nsplit) {
             e[s] = ml[(int64_t)s * 64];
-            p[s] = *reinterpret_cast<const float4*>(po + (int64_t)s * 64 * 512);
+            p[s] = *reinterpret_cast<const uint2*>(po + (int64_t)s * 64 * 512);
         }
     }
     float M = -INFINITY;
@@ -568,12 +591,12 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
 #pragma unroll
         for (int s = 0; s < MAXS; s++) {
             if (s < nsplit) {
-                const float f = exp2f(e[s].x - M);
-                L += e[s].y * f;
-                acc.x += p[s].x * f;
-                acc.y += p[s].y * f;
-                acc.z += p[s].z * f;
-                acc.w += p[s].w * f;
+                const float wgt = e[s].y * exp2f(e[s].x - M);
+                L += wgt;
+                acc.x += __uint_as_float(p[s].x << 16) * wgt;
+                acc.y += __uint_as_float(p[s].x & 0xffff0000u) * wgt;
+                acc.z += __uint_as_float(p[s].y << 16) * wgt;
+                acc.w += __uint_as_float(p[s].y & 0xffff0000u) * wgt;
             }
         }
     }
@@ -594,14 +617,16 @@ int attn_pick_splits(int32_t num_rows, int32_t k)
     // besides its tiles (index list and queries in, output or partial out);
     // a tile takes the longer of ~1.03 us (one CU's gather rate, three tiles
     // in flight) and the time the busy CUs' tiles take together at ~6.5 TB/s.
-    // Every split adds a 128 KB fp32 partial per row, written and read back
+    // Every split adds a 64 KB bf16 partial per row, written and read back
     // by the merge, which is one more launch.  Fitted to decode batches of
-    // 2,048 selected rows (attention + merge): 64 rows 39.4 us with 3
-    // splits against 40.8 with 4 and 45.5 with 2; 48 rows 34.4 with 4
-    // against 49.2 with 6 (two rounds); 100 rows 55.6 with 2 against 78.5
-    // with 3; 32 rows 29.0 with 6 against 30.6 with 8; 16 rows 22.3 with 8.
+    // 2,048 selected rows (attention + merge, then re-measured with the bf16
+    // partials): 64 rows 36.6-37.0 us with 3 splits against 36.8-37.0 with 4
+    // (whose step is 2 us slower) and 44.1 with 2; 16 rows 20.0-20.5 us with
+    // 8 to 13 splits against 21.8 with 6 and 21.2 with 16; and, with fp32
+    // partials, 48 rows 34.4 us with 4 against 49.2 with 6 (two rounds), 100
+    // rows 55.6 with 2 against 78.5 with 3.
     constexpr double kTileFloor = 1.03e-6, kGatherBw = 6.5e12, kFixed = 7e-6, kMergeLaunch = 2e-6;
-    constexpr double kPartialBytes = 64.0 * 512 * 4 * 2;  // per row and split: written, then read
+    constexpr double kPartialBytes = 64.0 * 512 * 2 * 2;  // per row and split: written, then read
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
     int best = 1;
     double best_t = 0.0;
@@ -630,7 +655,7 @@ size_t attn_workspace_bytes(int32_t num_rows, int32_t k)
     const int s = attn_pick_splits(num_rows, k);
     if (s == 1) return 0;
     const size_t R = (size_t)num_rows;
-    return align_up(R * s * 64 * 512 * 4, 256) + align_up(R * s * 64 * 8, 256);
+    return align_up(R * s * 64 * 512 * 2, 256) + align_up(R * s * 64 * 8, 256);
 }
 
 void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa, const uint16_t* kv,
@@ -640,11 +665,11 @@ void launch_sparse_mla(int32_t num_rows, const int64_t* base, const uint16_t* qa
     const int s = attn_pick_splits(num_rows, k);
     const int tiles = (k + AT_TILE - 1) / AT_TILE;
     const int split_len = ((tiles + s - 1) / s) * AT_TILE;
-    float* part_o = nullptr;
+    uint16_t* part_o = nullptr;
     float2* part_ml = nullptr;
     if (s > 1) {
-        part_o = (float*)ws;
-        part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 4, 256));
+        part_o = (uint16_t*)ws;
+        part_ml = (float2*)((char*)ws + align_up((size_t)num_rows * s * 64 * 512 * 2, 256));
     }
     // Several splits only occur below 256 rows (attn_pick_splits), so their
     // one-dimensional grid stays small.

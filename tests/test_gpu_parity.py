@@ -578,19 +578,19 @@ def test_attention_random_index_sets_with_padding(dsa, oracle_mod, k):
 
 def _splits_of_call(dsa, R, k):
     """Splits per row of an attention call, read back from the workspace it asks
-    for: R * s fp32 partials of 64 x 512 plus R * s (max, sum) pairs of 64."""
+    for: R * s bf16 partials of 64 x 512 plus R * s (max, sum) pairs of 64."""
     ws = dsa.dsa_sparse_mla_workspace_size(R, k)
     al = lambda b: (b + 255) // 256 * 256
-    found = [s for s in range(1, 17) if (0 if s == 1 else al(R * s * 64 * 512 * 4) + al(R * s * 64 * 8)) == ws]
+    found = [s for s in range(1, 17) if (0 if s == 1 else al(R * s * 64 * 512 * 2) + al(R * s * 64 * 8)) == ws]
     assert len(found) == 1, (R, k, ws)
     return found[0]
 
 
-@pytest.mark.parametrize("R, k, splits", [(1, 2048, 16), (8, 2048, 13), (4, 1000, 11), (16, 2048, 8), (32, 2048, 5),
-                                          (48, 2048, 4), (64, 2048, 3), (100, 2048, 2), (160, 2048, 1)])
+@pytest.mark.parametrize("R, k, splits", [(1, 2048, 16), (12, 2048, 13), (8, 1000, 11), (19, 2048, 8), (26, 2048, 7),
+                                          (33, 2048, 5), (41, 2048, 4), (64, 2048, 3), (100, 2048, 2), (160, 2048, 1)])
 def test_attention_each_split_count(dsa, oracle_mod, R, k, splits):
     """Attention against the oracle for calls whose rows are split 16, 13, 11,
-    8, 5, 4, 3, 2 ways or not at all (splits of equal whole tiles, the last
+    8, 7, 5, 4, 3, 2 ways or not at all (splits of equal whole tiles, the last
     one shorter where the tiles do not divide), with padding slots inside the
     lists and one row that selects nothing; sampled rows.  R rows read one
     4,096-position sequence through their own random index sets."""
@@ -688,7 +688,7 @@ def test_prefill_rows_up_to_k_equal_dense(dsa, oracle_mod):
 @pytest.mark.parametrize("R", [64, 128, 48, 16, 8])
 def test_decode_step_attention_matches_standalone_call(dsa, R):
     """The attention inside dsa_decode_step equals dsa_sparse_mla_attn on the
-    same index lists bit for bit, for 3, 2, 4, 8 and 13 splits per row, also when
+    same index lists bit for bit, for 3, 2, 4, 11 and 16 splits per row, also when
     the workspace starts out full of garbage and is reused by a second call
     (the split partials and their merge leave nothing behind)."""
     w, x = inputs("c3")
